@@ -1,0 +1,190 @@
+/*
+ * muse_attn.h -- C ABI of the MI355X (gfx950) attention core of one Muse
+ * Glimmer text layer.
+ *
+ * What one call computes, for every new token t of sequence s, at position
+ * p = seq_len[s] + t (pages cited by title and section):
+ *   1. Per-head QK-norm: each 128-wide head slice of Q (32 heads) and K
+ *      (2 heads) becomes x / sqrt(mean(x^2) + eps) * gain, with a constant
+ *      gain per tensor.  ["Chapter 9 - The Muse Glimmer architecture" 9.5
+ *      RMSNorm formula; "Chapter 14 - QK-norm and RoPE" 14.3]
+ *   2. RoPE on sliding layers only: adjacent pairs (x[2i], x[2i+1]) rotate by
+ *      the f32 angle p * theta_i, theta_i = base^(-2i/128) held as f32.
+ *      Full layers are NoPE and skip this step.  [Ch 14, 14.1, 14.4.1,
+ *      14.4.2, 14.5; Ch 9, 9.7]
+ *   3. KV append: cache row p of KV head g receives the normed (and rotated)
+ *      K and the raw V.  [Ch 14, 14.7: keys are rotated before they are stored]
+ *   4. Causal GQA attention: query head h reads KV head h / 16; key j is
+ *      visible iff j <= p and, on sliding layers, p - j < window; scores are
+ *      (q . k) * attn_scale; softmax; weighted sum of V.  [Ch 9, 9.5, 9.6
+ *      Figure 9.3, 9.7]
+ *   5. Sigmoid output gate: out[c] = attn[c] * 1 / (1 + exp(-gate[c])) for
+ *      every channel c = h * 128 + d.  [Ch 9, 9.8]
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless the comment says "host".
+ *   - The caller allocates and owns every buffer.  The library keeps no
+ *     pointer after a call returns.
+ *   - Activations, KV cache and output share one dtype (muse_dtype); all
+ *     arithmetic is f32 (bf16 operands feed bf16 matrix cores, accumulating
+ *     in f32).  Stores round to nearest, ties to even.
+ *   - Layouts are dense, row-major, innermost dimension last:
+ *       q          [n_seq][n_new][32][128]
+ *       k, v       [n_seq][n_new][2][128]
+ *       gate, out  [n_seq][n_new][4096]      (channel = head * 128 + dim)
+ *       cache k, v [n_seq][capacity][2][128] (token-major; row = position)
+ *       seq_len    int32 [n_seq]             (rows already cached)
+ *     Every pointer must be 16-byte aligned.
+ *   - Inputs q, k, v, gate and seq_len are read-only.  Cache rows
+ *     [seq_len[s], seq_len[s] + n_new) are written; other rows are only read.
+ *     seq_len is not advanced: the caller does that after the call.
+ *   - out must not overlap any other buffer; workspace must not overlap any
+ *     other buffer.
+ *   - Calls are asynchronous on `stream` (0 = the default stream): no host
+ *     synchronisation, no device-wide barrier.  Concurrent calls on different
+ *     streams are safe when their buffers are disjoint.
+ *   - Every argument is validated on the host BEFORE anything is enqueued;
+ *     on any error nothing is enqueued and nothing is written (fail closed).
+ *   - A sequence whose device-side seq_len lies outside [0, max_seq_len]
+ *     (which the host cannot check) is refused on the device: its cache is
+ *     not written and its output rows are filled with NaN.
+ */
+#ifndef MUSE_ATTN_H
+#define MUSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MUSE_OK = 0,
+    MUSE_ERR_NULL = 1,      /* a required pointer is NULL                        */
+    MUSE_ERR_SHAPE = 2,     /* head counts, head_dim or a size out of range      */
+    MUSE_ERR_LAYER = 3,     /* kind/window/theta/eps/gain/scale inconsistent     */
+    MUSE_ERR_CAPACITY = 4,  /* max_seq_len + n_new > capacity                    */
+    MUSE_ERR_WORKSPACE = 5, /* workspace_bytes below muse_attn_workspace_size    */
+    MUSE_ERR_DTYPE = 6,     /* dtype is not MUSE_F32 / MUSE_BF16                 */
+    MUSE_ERR_HIP = 7,       /* a HIP launch or event call failed                 */
+    MUSE_ERR_ALIGN = 8,     /* a pointer is not 16-byte aligned                  */
+    MUSE_ERR_ALIAS = 9      /* out or workspace overlaps another buffer          */
+} muse_status;
+
+typedef enum { MUSE_F32 = 0, MUSE_BF16 = 1 } muse_dtype;
+
+/* Layer kinds: ["Chapter 9" 9.4 listing and Figure 9.4] */
+typedef enum { MUSE_SLIDING_ROPE = 0, MUSE_FULL_NOPE = 1 } muse_layer_kind;
+
+/* Parameters of one attention layer.  All fields are validated:
+ *   n_heads, n_kv_heads, head_dim  must be 32, 2, 128 (else MUSE_ERR_SHAPE)
+ *   kind        MUSE_SLIDING_ROPE or MUSE_FULL_NOPE
+ *   window      sliding: >= 1 (the model uses 2048).  full: must be 0
+ *   rope_theta  sliding: finite and > 0 (the model uses 500000).
+ *               full: must be 0 (NoPE layers carry a zero RoPE base;
+ *               "How Muse Glimmer Fits an Agent on Your Device",
+ *               section "Global attention without RoPE")
+ *   rms_eps     finite and > 0 (the model uses 1e-5)
+ *   q_norm_gain, k_norm_gain  finite constant QK-norm weights (3.87 and 1.0;
+ *               ["Chapter 14" 14.3])
+ *   attn_scale  finite and > 0 (1/sqrt(128); ["Chapter 9" 9.5])
+ *   dtype       muse_dtype of activations, cache and output               */
+typedef struct {
+    int32_t n_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t kind;
+    int32_t window;
+    float rope_theta;
+    float rms_eps;
+    float q_norm_gain;
+    float k_norm_gain;
+    float attn_scale;
+    int32_t dtype;
+} muse_attn_layer;
+
+/* Contiguous per-sequence KV cache: k and v are DEVICE pointers to
+ * [n_seq][capacity][2][128] arrays of the layer dtype; capacity is in rows. */
+typedef struct {
+    void* k;
+    void* v;
+    int64_t capacity;
+} muse_kv_cache;
+
+/* Optional kernel timer.  When a call receives a non-NULL timer, `start` is
+ * recorded on `stream` immediately before the call's attention kernel and
+ * `stop` immediately after it (the events are the caller's, created with
+ * timing enabled).  Used to measure the attention kernel alone. */
+typedef struct {
+    hipEvent_t start;
+    hipEvent_t stop;
+} muse_kernel_timer;
+
+/*
+ * Prefill: append n_new tokens per sequence and attend, causally within the
+ * new chunk and over the cached prefix (chunked prefill when seq_len > 0).
+ *   layer        host pointer, validated as above
+ *   n_seq        >= 0 sequences;  n_new >= 0 new tokens per sequence
+ *   seq_len      device int32[n_seq]: rows already cached
+ *   max_seq_len  host upper bound of every seq_len[s]; sizes the grid and
+ *                the capacity check (max_seq_len + n_new <= capacity)
+ *   q, k, v, gate, out   device, layouts above
+ *   cache        host pointer to the cache descriptor
+ *   workspace    device scratch of at least muse_attn_workspace_size(...)
+ *                bytes (contents on entry are ignored; clobbered)
+ *   stream       HIP stream to enqueue on
+ *   timer        optional (NULL = none)
+ * n_seq == 0 or n_new == 0 is valid and enqueues nothing.
+ */
+muse_status muse_attn_prefill(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new,
+                              const int32_t* seq_len, int32_t max_seq_len,
+                              const void* q, const void* k, const void* v, const void* gate,
+                              const muse_kv_cache* cache, void* out,
+                              void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, const muse_kernel_timer* timer);
+
+/*
+ * Decode: exactly one new token per sequence (n_new = 1) at position
+ * seq_len[s]; the same five steps as prefill, with the attention split over
+ * the cache length (split-K) and merged on the device.  Arguments as for
+ * muse_attn_prefill with n_new = 1 (q [n_seq][1][32][128], etc.).
+ */
+muse_status muse_attn_decode(const muse_attn_layer* layer, int32_t n_seq,
+                             const int32_t* seq_len, int32_t max_seq_len,
+                             const void* q, const void* k, const void* v, const void* gate,
+                             const muse_kv_cache* cache, void* out,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream, const muse_kernel_timer* timer);
+
+/* Workspace bytes a call needs (is_decode != 0 selects decode, which ignores
+ * n_new).  Writes the size to *bytes (host).  Same validation as the calls. */
+muse_status muse_attn_workspace_size(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new,
+                                     int32_t max_seq_len, int32_t is_decode, size_t* bytes);
+
+/* Fill *layer (host) with the model's parameters for layer `layer_index`
+ * (0 <= layer_index < 52): kind by the l % 4 == 3 rule, window 2048 and
+ * theta 500000 on sliding layers (0 and 0 on full layers), eps 1e-5, gains
+ * 3.87 / 1.0, scale 1/sqrt(128), and the given dtype.
+ * ["Chapter 9" 9.4, 9.7; "Chapter 14" 14.3] */
+muse_status muse_attn_layer_init(muse_attn_layer* layer, int32_t layer_index, int32_t dtype);
+
+/* Layer kind of layer `layer_index` of an n_layers-deep model: FULL_NOPE iff
+ * layer_index % 4 == 3, else SLIDING_ROPE.  Returns -1 when layer_index is
+ * outside [0, n_layers) or n_layers < 1.  ["Chapter 9" 9.4 listing] */
+int32_t muse_layer_kind_for(int32_t layer_index, int32_t n_layers);
+
+/* The f32 RoPE frequency table the kernels use: out_host64[i] =
+ * base^(-2i/128) rounded once to f32, i < 64 (host array of 64 floats).
+ * ["Chapter 14" 14.4.1]  MUSE_ERR_LAYER unless theta is finite and > 0. */
+muse_status muse_rope_theta_table(float theta, float* out_host64);
+
+/* Static string naming a status code (never NULL). */
+const char* muse_status_str(muse_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUSE_ATTN_H */
