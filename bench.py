@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the Muse Glimmer attention core on one MI355X.
+
+Default workload (one "step"): a decode step of 64 sequences x 8,192 cached
+tokens, bf16, on one sliding layer (RoPE, window 2,048) and one full NoPE
+layer -- QK-norm, RoPE, KV append, split-K attention and the gate, for both
+layers.  `value` is decode attention KV bytes per second over the whole step
+(the visible K/V rows, 1,024 B per row per sequence).  The 8 x 8,192 bf16
+prefill (both layer kinds) is timed in the same run and reported under
+"prefill" in TFLOP/s (16,384 flop per visible (query, key) pair over 32
+heads), so the line carries both halves of the metric.
+
+Inputs are seeded synthetic tensors already resident in HBM.  Decode caches
+are rotated over enough copies that every step reads bytes the 256 MB
+Infinity Cache cannot still hold.  `roofline` uses the attention kernel's own
+launch time from HIP events recorded by the library around that kernel.
+`cpu_baseline` times the CPU oracle on the same step's inputs (rank 0, N=1).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode attn KV GB/s (% HBM peak) + prefill attn TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 / fp16 MFMA
+FLOP_PER_PAIR = 32 * 4 * 128     # 32 heads x (2*128 for Q.K + 2*128 for P.V)
+MALL_BYTES = 256 << 20
+
+
+def kv_row_bytes(dtype: int) -> int:
+    return 2 * 2 * 128 * (2 if dtype == 1 else 4)   # K and V, 2 kv heads x 128
+
+
+def visible_rows(spec, p: int) -> int:
+    return p + 1 if spec.window == 0 else min(spec.window, p + 1)
+
+
+def prefill_pairs(spec, L: int, N: int) -> int:
+    return sum(visible_rows(spec, L + t) for t in range(N))
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_64x8192_bf16")
+    ap.add_argument("--prefill-workload", default="prefill_8x8192_bf16")
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 1 GiB device copy first (scale for HBM byte counters)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class LayerRun:
+    def __init__(self, w, spec, copies, decode, fa, synth):
+        import torch
+        self.spec = spec
+        self.inp = synth.layer_inputs(w, spec, device="cuda", backend="torch")
+        self.caches = [(self.inp.cache_k, self.inp.cache_v)]
+        for _ in range(1, copies):
+            self.caches.append((self.inp.cache_k.clone(), self.inp.cache_v.clone()))
+        self.layer = fa.make_layer(spec.kind, window=spec.window, rope_theta=spec.rope_theta,
+                                   rms_eps=spec.rms_eps, q_norm_gain=spec.q_gain,
+                                   k_norm_gain=spec.k_gain, attn_scale=spec.scale, dtype=w.dtype)
+        self.decode = decode
+        self.ws = fa.workspace(self.layer, w.n_seq, w.n_new, w.prefix, decode)
+        self.out = torch.empty_like(self.inp.gate)
+        self.max_seq_len = w.prefix
+
+    def call(self, fa, copy, timer=None):
+        ck, cv = self.caches[copy]
+        fn = fa.decode if self.decode else fa.prefill
+        fn(self.layer, self.inp.q, self.inp.k, self.inp.v, self.inp.gate, ck, cv, self.inp.seq_len,
+           self.out, max_seq_len=self.max_seq_len, workspace=self.ws, timer=timer)
+
+
+def run_timed(runs, steps, warmup, copies, fa, torch):
+    """W untimed steps, then K timed steps between synchronisations."""
+    from full_gqa_attention_amd.timing import KernelTimers
+    timers = KernelTimers(steps * len(runs))
+    for i in range(warmup):
+        for r in runs:
+            r.call(fa, i % copies)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for j, r in enumerate(runs):
+            r.call(fa, (warmup + i) % copies, timers[i * len(runs) + j])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch = [timers.elapsed_ms(i) for i in range(len(timers))]
+    timers.close()
+    return wall, per_launch
+
+
+def bench_decode(w, args, fa, synth, torch):
+    per_step_unique = sum(kv_row_bytes(w.dtype) * w.n_seq * visible_rows(s, w.prefix) for s in w.layers)
+    copies = max(1, -(-(2 * MALL_BYTES) // max(per_step_unique, 1)) + 1)
+    copies = min(copies, 8)
+    log(f"decode {w.name}: {len(w.layers)} layers, {copies} cache copies, "
+        f"{per_step_unique / 1e6:.1f} MB KV per step")
+    runs = [LayerRun(w, spec, copies, True, fa, synth) for spec in w.layers]
+    torch.cuda.synchronize()
+    wall, per_launch = run_timed(runs, args.steps, args.warmup, copies, fa, torch)
+    kv_per_step = per_step_unique
+    ms_per_step = wall * 1e3 / args.steps
+    launches = len(per_launch)
+    avg_launch_ms = sum(per_launch) / launches
+    bytes_per_launch = kv_per_step / len(runs)
+    achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
+    per_layer = {}
+    for j, r in enumerate(runs):
+        lt = per_launch[j::len(runs)]
+        b = kv_row_bytes(w.dtype) * w.n_seq * visible_rows(r.spec, w.prefix)
+        per_layer[r.spec.name] = {"kernel_us": round(1e3 * sum(lt) / len(lt), 2),
+                                  "kv_MB": round(b / 1e6, 3),
+                                  "kernel_GBps": round(b / (sum(lt) / len(lt) * 1e-3) / 1e9, 1)}
+    res = {
+        "value": kv_per_step / (ms_per_step * 1e-3) / 1e9,
+        "ms_per_step": ms_per_step,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "muse::decode_kernel<bf16>" if w.dtype == 1 else "muse::decode_kernel<f32>",
+                     "launches": launches, "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": int(bytes_per_launch),
+                     "per_layer": per_layer},
+        "config": {"workload": w.name, "n_seq": w.n_seq, "cached_tokens": w.prefix, "new_tokens": 1,
+                   "layers": [f"{s.name}" + (f"_w{s.window}_theta{int(s.rope_theta)}" if s.window else "_nope")
+                              for s in w.layers],
+                   "q_heads": 32, "kv_heads": 2, "head_dim": 128, "cache_copies": copies,
+                   "kv_bytes_per_step": kv_per_step},
+    }
+    return res, runs
+
+
+def bench_prefill(w, steps, warmup, fa, synth, torch):
+    log(f"prefill {w.name}: {len(w.layers)} layers")
+    runs = [LayerRun(w, spec, 1, False, fa, synth) for spec in w.layers]
+    torch.cuda.synchronize()
+    wall, per_launch = run_timed(runs, steps, warmup, 1, fa, torch)
+    flops_step = sum(FLOP_PER_PAIR * w.n_seq * prefill_pairs(s, w.prefix, w.n_new) for s in w.layers)
+    ms_per_step = wall * 1e3 / steps
+    per_layer = {}
+    for j, r in enumerate(runs):
+        lt = per_launch[j::len(runs)]
+        f = FLOP_PER_PAIR * w.n_seq * prefill_pairs(r.spec, w.prefix, w.n_new)
+        avg = sum(lt) / len(lt)
+        per_layer[r.spec.name] = {"kernel_ms": round(avg, 4), "tflop": round(f / 1e12, 4),
+                                  "kernel_TFLOPs": round(f / (avg * 1e-3) / 1e12, 1)}
+    kern = sum(per_launch) / len(per_launch)
+    achieved = flops_step / len(runs) / (kern * 1e-3) / 1e12
+    return {
+        "workload": w.name,
+        "tflops": round(flops_step / (ms_per_step * 1e-3) / 1e12, 2),
+        "ms_per_step": round(ms_per_step, 4),
+        "frac_mfma_peak": round(flops_step / (ms_per_step * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "muse::prefill_kernel<bf16>", "avg_launch_ms": round(kern, 4),
+                     "per_layer": per_layer},
+        "flop_per_step": flops_step, "steps": steps, "warmup": warmup,
+    }
+
+
+def cpu_baseline_decode(w, runs, synth, torch):
+    """Time the CPU oracle on this step's inputs (all rows of both layers) and
+    check the benchmarked GPU output against it."""
+    import numpy as np
+    import oracle
+    rows = oracle.all_rows(w.n_seq, 1)
+    t_oracle = 0.0
+    worst = 0.0
+    ok = True
+    for r in runs:
+        ck, cv = r.caches[0]
+        pk, pv = synth.to_storage_numpy(ck), synth.to_storage_numpy(cv)   # rows < seq_len untouched
+        lay = oracle.Layer(kind=r.spec.kind, window=r.spec.window, rope_theta=r.spec.rope_theta,
+                           rms_eps=r.spec.rms_eps, q_gain=r.spec.q_gain, k_gain=r.spec.k_gain,
+                           scale=r.spec.scale, dtype=w.dtype)
+        args = (lay, r.inp.seq_len.cpu().numpy(), synth.to_storage_numpy(r.inp.k),
+                synth.to_storage_numpy(r.inp.v), pk, pv, rows,
+                synth.to_storage_numpy(r.inp.q).reshape(-1, 32, 128),
+                synth.to_storage_numpy(r.inp.gate).reshape(-1, 4096))
+        t0 = time.perf_counter()
+        ref = oracle.attn_rows(*args)
+        t_oracle += time.perf_counter() - t0
+        got = r.out.double().cpu().numpy().reshape(-1, 4096)
+        err = np.abs(got - ref)
+        worst = max(worst, float(err.max()))
+        ok = ok and bool(np.all(err <= 2e-2 + 1e-2 * np.abs(ref)))
+    kv = sum(kv_row_bytes(w.dtype) * w.n_seq * visible_rows(r.spec, w.prefix) for r in runs)
+    return {"value": round(kv / t_oracle / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"the whole step: {w.n_seq} sequences x {len(runs)} layers, all 32 heads "
+                      f"({t_oracle:.2f} s)",
+            "seconds": round(t_oracle, 3)}, {"max_abs_err": worst, "within_tolerance": ok}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path to measure.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import full_gqa_attention_amd as fa
+    from full_gqa_attention_amd import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    fa.lib()                                  # fails loudly when the HIP library is missing
+    if args.calibrate_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    w = synth.WORKLOADS[args.workload]
+    if not w.is_decode:
+        print(f"--workload must be a decode workload, got {w.name}", file=sys.stderr)
+        sys.exit(2)
+    res, runs = bench_decode(w, args, fa, synth, torch)
+    line = {
+        "metric": METRIC, "value": round(res["value"], 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == 1 else "f32",
+        "data": "synthetic: seeded N(0,1) inputs and cache prefixes, resident in HBM",
+        "config": res["config"], "roofline": res["roofline"],
+        "frac_hbm_peak": round(res["value"] / HBM_PEAK_GBS, 4),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the same step")
+        cb, parity = cpu_baseline_decode(w, runs, synth, torch)
+        line["cpu_baseline"] = cb
+        line["parity"] = parity
+    del runs
+    torch.cuda.empty_cache()
+    if not args.no_prefill:
+        pw = synth.WORKLOADS[args.prefill_workload]
+        line["prefill"] = bench_prefill(pw, args.prefill_steps, 2, fa, synth, torch)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,151 @@
+// device_common.h -- small device-side helpers shared by the gfx950 kernels:
+// storage types, conversions, wave reductions and MFMA wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muse {
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16_t;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kHeads = 32;      // query heads
+constexpr int kKvHeads = 2;     // KV heads
+constexpr int kHeadDim = 128;   // head_dim
+constexpr int kHeadsPerKv = 16; // query heads served by one KV head
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// f32 -> bf16 rounds to nearest, ties to even (v_cvt_pk_bf16_f32 on gfx950).
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return (bf16_t)x; }
+template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float x) { return (f16_t)x; }
+
+// Operand type of the Q.K^T products.  bf16 layers score in fp16: Q-hat keeps
+// 3 more mantissa bits than bf16 (its rounding is the dominant error of the
+// bf16 path), and a bf16 K row converts to fp16 exactly while its entries
+// stay inside fp16's normal range; normed keys are bounded by
+// |k_gain| * sqrt(128), which the host keeps far below 65504.  P.V stays in
+// the storage type (V is raw and unbounded).
+template <typename T> struct ScoreType;
+template <> struct ScoreType<bf16_t> { typedef f16_t type; };
+template <> struct ScoreType<float> { typedef float type; };
+
+// 16 bytes of storage-type K -> 16 bytes of score-type K (bf16 -> fp16;
+// f32 unchanged).
+__device__ __forceinline__ uint4 k_chunk_to_score(uint4 x, bf16_t) {
+    const bf16x8 b = __builtin_bit_cast(bf16x8, x);
+    f16x8 h;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) h[t] = (f16_t)(float)b[t];
+    return __builtin_bit_cast(uint4, h);
+}
+__device__ __forceinline__ uint4 k_chunk_to_score(uint4 x, float) { return x; }
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// 2^x on the hardware exp unit (v_exp_f32).  Softmax works in the log2
+// domain: scores are pre-multiplied by scale * log2(e).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// sigma(g) = 1 / (1 + e^-g).
+__device__ __forceinline__ float sigmoid(float g) { return 1.0f / (1.0f + __expf(-g)); }
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ---------------------------------------------------------------- MFMA
+// 32x32 tiles (prefill).  Operand layout for C = A * B (A: 32 x K, B: K x 32):
+// lane l holds A[l % 32][KPL * (l / 32) + t] and B[KPL * (l / 32) + t][l % 32]
+// for t < KPL; the f32 result has C[8 * (i / 4) + 4 * (l / 32) + i % 4][l % 32]
+// in item i of lane l.
+template <typename T> struct Mma32;
+template <> struct Mma32<bf16_t> {
+    static constexpr int KPL = 8;          // v_mfma_f32_32x32x16_bf16
+    typedef bf16x8 Frag;
+    static __device__ __forceinline__ floatx16 mma(Frag a, Frag b, floatx16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mma32<f16_t> {
+    static constexpr int KPL = 8;          // v_mfma_f32_32x32x16_f16
+    typedef f16x8 Frag;
+    static __device__ __forceinline__ floatx16 mma(Frag a, Frag b, floatx16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mma32<float> {
+    static constexpr int KPL = 1;          // v_mfma_f32_32x32x2_f32
+    typedef float Frag;
+    static __device__ __forceinline__ floatx16 mma(Frag a, Frag b, floatx16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// 16x16 tiles (decode).  lane l holds A[l % 16][KPL * (l / 16) + t] and
+// B[KPL * (l / 16) + t][l % 16]; C[4 * (l / 16) + i][l % 16] is item i.
+// "Wide" is the long-K instruction (Q.K over head_dim), "Narrow" the K = 16
+// (bf16) / K = 4 (f32) one used for P.V over 16 keys.
+template <typename T> struct Mma16Wide;
+template <> struct Mma16Wide<bf16_t> {
+    static constexpr int KPL = 8;          // v_mfma_f32_16x16x32_bf16
+    typedef bf16x8 Frag;
+    static __device__ __forceinline__ floatx4 mma(Frag a, Frag b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mma16Wide<f16_t> {
+    static constexpr int KPL = 8;          // v_mfma_f32_16x16x32_f16
+    typedef f16x8 Frag;
+    static __device__ __forceinline__ floatx4 mma(Frag a, Frag b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mma16Wide<float> {
+    static constexpr int KPL = 1;          // v_mfma_f32_16x16x4_f32
+    typedef float Frag;
+    static __device__ __forceinline__ floatx4 mma(Frag a, Frag b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+template <typename T> struct Mma16Narrow;
+template <> struct Mma16Narrow<bf16_t> {
+    static constexpr int KPL = 4;          // v_mfma_f32_16x16x16_bf16
+    typedef shortx4 Frag;
+    static __device__ __forceinline__ floatx4 mma(Frag a, Frag b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mma16Narrow<float> {
+    static constexpr int KPL = 1;          // v_mfma_f32_16x16x4_f32
+    typedef float Frag;
+    static __device__ __forceinline__ floatx4 mma(Frag a, Frag b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// Element t of a fragment (t is a compile-time constant after unrolling).
+__device__ __forceinline__ void frag_set(bf16x8& f, int t, float v) { f[t] = (bf16_t)v; }
+__device__ __forceinline__ void frag_set(float& f, int, float v) { f = v; }
+__device__ __forceinline__ void frag_set(shortx4& f, int t, float v) {
+    bf16_t b = (bf16_t)v;
+    f[t] = __builtin_bit_cast(short, b);
+}
+__device__ __forceinline__ void frag_set_raw(bf16x8& f, int t, bf16_t v) { f[t] = v; }
+__device__ __forceinline__ void frag_set_raw(float& f, int, float v) { f = v; }
+__device__ __forceinline__ void frag_set_raw(shortx4& f, int t, bf16_t v) {
+    f[t] = __builtin_bit_cast(short, v);
+}
+
+}  // namespace muse

@@ -1,0 +1,290 @@
+// muse_attn.cpp -- the C ABI of libmuse_attn (declared in include/muse_attn.h):
+// host-side validation (fail closed, before anything is enqueued), workspace
+// layout, the RoPE frequency table, and the kernel launch sequence.
+#include "muse_attn.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+using muse::AttnArgs;
+using muse::PrepArgs;
+
+constexpr int kHeads = 32, kKvHeads = 2, kHeadDim = 128;
+constexpr int kModelLayers = 52;          // "Chapter 9" 9.4: 52 blocks
+constexpr int64_t kMaxPositions = 1 << 24; // positions stay exact as f32 (RoPE angle)
+constexpr int32_t kMaxSeqs = 1 << 20;
+constexpr size_t kAlign = 256;
+constexpr float kMaxGain = 4096.0f;        // 4096 * sqrt(128) < 65504 (fp16 max)
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+size_t elem_bytes(int32_t dtype) { return dtype == MUSE_BF16 ? 2 : 4; }
+
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
+
+muse_status check_layer(const muse_attn_layer* l) {
+    if (!l) return MUSE_ERR_NULL;
+    if (l->n_heads != kHeads || l->n_kv_heads != kKvHeads || l->head_dim != kHeadDim)
+        return MUSE_ERR_SHAPE;
+    if (l->dtype != MUSE_F32 && l->dtype != MUSE_BF16) return MUSE_ERR_DTYPE;
+    if (l->kind == MUSE_SLIDING_ROPE) {
+        if (l->window < 1 || !finite_pos(l->rope_theta)) return MUSE_ERR_LAYER;
+    } else if (l->kind == MUSE_FULL_NOPE) {
+        if (l->window != 0 || l->rope_theta != 0.0f) return MUSE_ERR_LAYER;
+    } else {
+        return MUSE_ERR_LAYER;
+    }
+    if (!finite_pos(l->rms_eps) || !finite_pos(l->attn_scale)) return MUSE_ERR_LAYER;
+    // bf16 layers score with fp16 operands: normed rows are bounded by
+    // |gain| * sqrt(128), which must stay inside fp16's range.
+    if (!(std::fabs(l->q_norm_gain) <= kMaxGain) || !(std::fabs(l->k_norm_gain) <= kMaxGain))
+        return MUSE_ERR_LAYER;
+    return MUSE_OK;
+}
+
+muse_status check_sizes(int32_t n_seq, int32_t n_new, int32_t max_seq_len) {
+    if (n_seq < 0 || n_seq > kMaxSeqs || n_new < 0 || max_seq_len < 0) return MUSE_ERR_SHAPE;
+    if ((int64_t)max_seq_len + n_new > kMaxPositions) return MUSE_ERR_SHAPE;
+    if ((int64_t)n_seq * n_new > (int64_t)1 << 31) return MUSE_ERR_SHAPE;
+    return MUSE_OK;
+}
+
+// Decode split: about 2048 workgroups in total, chunks a multiple of the
+// 64-row tile.  The span of visible rows is at most window (sliding) or
+// max_seq_len + 1 (full).
+void decode_split(const muse_attn_layer* l, int32_t n_seq, int32_t max_seq_len,
+                  int32_t* chunk, int32_t* nsplit) {
+    int64_t span = (int64_t)max_seq_len + 1;
+    if (l->kind == MUSE_SLIDING_ROPE && l->window < span) span = l->window;
+    const int64_t pairs = (int64_t)(n_seq > 0 ? n_seq : 1) * kKvHeads;
+    int64_t want = (2048 + pairs - 1) / pairs;
+    const int64_t tiles = (span + muse::kDecodeTile - 1) / muse::kDecodeTile;
+    if (want > tiles) want = tiles;
+    if (want < 1) want = 1;
+    int64_t ch = (span + want - 1) / want;
+    ch = (ch + muse::kDecodeTile - 1) / muse::kDecodeTile * muse::kDecodeTile;
+    *chunk = (int32_t)ch;
+    *nsplit = (int32_t)((span + ch - 1) / ch);
+}
+
+struct WorkspaceLayout {
+    size_t qhat = 0, part_o = 0, part_m = 0, part_l = 0, total = 0;
+    int32_t chunk = 0, nsplit = 0;
+};
+
+WorkspaceLayout layout_for(const muse_attn_layer* l, int32_t n_seq, int32_t n_new,
+                           int32_t max_seq_len, bool decode) {
+    WorkspaceLayout w;
+    const size_t es = elem_bytes(l->dtype);
+    if (decode) n_new = 1;
+    size_t off = round_up((size_t)n_seq * n_new * kHeads * kHeadDim * es, kAlign);
+    w.qhat = 0;
+    if (decode) {
+        decode_split(l, n_seq, max_seq_len, &w.chunk, &w.nsplit);
+        const size_t parts = (size_t)n_seq * kHeads * w.nsplit;
+        w.part_o = off;
+        off += round_up(parts * kHeadDim * sizeof(float), kAlign);
+        w.part_m = off;
+        off += round_up(parts * sizeof(float), kAlign);
+        w.part_l = off;
+        off += round_up(parts * sizeof(float), kAlign);
+    }
+    w.total = off;
+    return w;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;
+};
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+void rope_table(float theta, float* out64) {
+    for (int i = 0; i < kHeadDim / 2; ++i)
+        out64[i] = (float)std::pow((double)theta, -(2.0 * i) / (double)kHeadDim);
+}
+
+muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, const int32_t* seq_len,
+                int32_t max_seq_len, const void* q, const void* k, const void* v, const void* gate,
+                const muse_kv_cache* cache, void* out, void* workspace, size_t workspace_bytes,
+                hipStream_t stream, const muse_kernel_timer* timer, bool decode) {
+    muse_status st = check_layer(layer);
+    if (st != MUSE_OK) return st;
+    if ((st = check_sizes(n_seq, n_new, max_seq_len)) != MUSE_OK) return st;
+    if (!cache) return MUSE_ERR_NULL;
+    if (cache->capacity < 0) return MUSE_ERR_CAPACITY;
+    if ((int64_t)max_seq_len + n_new > cache->capacity) return MUSE_ERR_CAPACITY;
+    if (n_seq == 0 || n_new == 0) return MUSE_OK;    // nothing to do
+    if (!seq_len || !q || !k || !v || !gate || !out || !cache->k || !cache->v || !workspace)
+        return MUSE_ERR_NULL;
+    if (timer && (!timer->start || !timer->stop)) return MUSE_ERR_NULL;
+    const void* ptrs[] = {seq_len, q, k, v, gate, out, cache->k, cache->v, workspace};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return MUSE_ERR_ALIGN;
+    const WorkspaceLayout wl = layout_for(layer, n_seq, n_new, max_seq_len, decode);
+    if (workspace_bytes < wl.total) return MUSE_ERR_WORKSPACE;
+
+    const size_t es = elem_bytes(layer->dtype);
+    const size_t tok = (size_t)n_seq * n_new;
+    auto R = [](const void* p, size_t n) { return Range{(uintptr_t)p, (uintptr_t)p + n}; };
+    const Range r_seq = R(seq_len, (size_t)n_seq * 4);
+    const Range r_q = R(q, tok * kHeads * kHeadDim * es);
+    const Range r_k = R(k, tok * kKvHeads * kHeadDim * es);
+    const Range r_v = R(v, tok * kKvHeads * kHeadDim * es);
+    const Range r_g = R(gate, tok * kHeads * kHeadDim * es);
+    const size_t cache_bytes = (size_t)n_seq * (size_t)cache->capacity * kKvHeads * kHeadDim * es;
+    const Range r_ck = R(cache->k, cache_bytes);
+    const Range r_cv = R(cache->v, cache_bytes);
+    const Range r_out = R(out, tok * kHeads * kHeadDim * es);
+    const Range r_ws = R(workspace, wl.total);
+    // every written buffer (out, workspace, cache k, cache v) is disjoint from every other
+    const Range all[] = {r_seq, r_q, r_k, r_v, r_g, r_ck, r_cv, r_out, r_ws};
+    const int written[] = {5, 6, 7, 8};
+    for (int wi : written)
+        for (int j = 0; j < 9; ++j)
+            if (j != wi && overlap(all[wi], all[j])) return MUSE_ERR_ALIAS;
+
+    char* ws = (char*)workspace;
+    PrepArgs pa;
+    std::memset(&pa, 0, sizeof pa);
+    pa.q = q;
+    pa.k = k;
+    pa.v = v;
+    pa.qhat = ws + wl.qhat;
+    pa.cache_k = cache->k;
+    pa.cache_v = cache->v;
+    pa.capacity = cache->capacity;
+    pa.seq_len = seq_len;
+    pa.max_seq_len = max_seq_len;
+    pa.n_seq = n_seq;
+    pa.n_new = n_new;
+    pa.rope = layer->kind == MUSE_SLIDING_ROPE ? 1 : 0;
+    pa.eps = layer->rms_eps;
+    pa.q_gain = layer->q_norm_gain;
+    pa.k_gain = layer->k_norm_gain;
+    if (pa.rope) rope_table(layer->rope_theta, pa.theta);
+
+    AttnArgs aa;
+    std::memset(&aa, 0, sizeof aa);
+    aa.qhat = pa.qhat;
+    aa.gate = gate;
+    aa.out = out;
+    aa.cache_k = cache->k;
+    aa.cache_v = cache->v;
+    aa.capacity = cache->capacity;
+    aa.seq_len = seq_len;
+    aa.max_seq_len = max_seq_len;
+    aa.n_seq = n_seq;
+    aa.n_new = n_new;
+    aa.window = layer->kind == MUSE_SLIDING_ROPE ? layer->window : 0;
+    aa.scale_log2 = (float)((double)layer->attn_scale * 1.4426950408889634);
+    aa.chunk = wl.chunk;
+    aa.nsplit = wl.nsplit;
+    aa.part_o = (float*)(ws + wl.part_o);
+    aa.part_m = (float*)(ws + wl.part_m);
+    aa.part_l = (float*)(ws + wl.part_l);
+
+    const int dt = layer->dtype;
+    if (muse::launch_prep(pa, dt, stream) != hipSuccess) return MUSE_ERR_HIP;
+    if (timer && hipEventRecord(timer->start, stream) != hipSuccess) return MUSE_ERR_HIP;
+    if (decode) {
+        if (muse::launch_decode(aa, dt, stream) != hipSuccess) return MUSE_ERR_HIP;
+    } else {
+        if (muse::launch_prefill(aa, dt, stream) != hipSuccess) return MUSE_ERR_HIP;
+    }
+    if (timer && hipEventRecord(timer->stop, stream) != hipSuccess) return MUSE_ERR_HIP;
+    if (decode && muse::launch_combine(aa, dt, stream) != hipSuccess) return MUSE_ERR_HIP;
+    return MUSE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+muse_status muse_attn_prefill(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new,
+                              const int32_t* seq_len, int32_t max_seq_len,
+                              const void* q, const void* k, const void* v, const void* gate,
+                              const muse_kv_cache* cache, void* out,
+                              void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, const muse_kernel_timer* timer) {
+    return run(layer, n_seq, n_new, seq_len, max_seq_len, q, k, v, gate, cache, out, workspace,
+               workspace_bytes, stream, timer, false);
+}
+
+muse_status muse_attn_decode(const muse_attn_layer* layer, int32_t n_seq,
+                             const int32_t* seq_len, int32_t max_seq_len,
+                             const void* q, const void* k, const void* v, const void* gate,
+                             const muse_kv_cache* cache, void* out,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream, const muse_kernel_timer* timer) {
+    return run(layer, n_seq, 1, seq_len, max_seq_len, q, k, v, gate, cache, out, workspace,
+               workspace_bytes, stream, timer, true);
+}
+
+muse_status muse_attn_workspace_size(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new,
+                                     int32_t max_seq_len, int32_t is_decode, size_t* bytes) {
+    if (!bytes) return MUSE_ERR_NULL;
+    muse_status st = check_layer(layer);
+    if (st != MUSE_OK) return st;
+    if (is_decode) n_new = 1;
+    if ((st = check_sizes(n_seq, n_new, max_seq_len)) != MUSE_OK) return st;
+    *bytes = layout_for(layer, n_seq, n_new, max_seq_len, is_decode != 0).total;
+    return MUSE_OK;
+}
+
+muse_status muse_attn_layer_init(muse_attn_layer* layer, int32_t layer_index, int32_t dtype) {
+    if (!layer) return MUSE_ERR_NULL;
+    if (layer_index < 0 || layer_index >= kModelLayers) return MUSE_ERR_SHAPE;
+    if (dtype != MUSE_F32 && dtype != MUSE_BF16) return MUSE_ERR_DTYPE;
+    muse_attn_layer l;
+    l.n_heads = kHeads;
+    l.n_kv_heads = kKvHeads;
+    l.head_dim = kHeadDim;
+    l.kind = muse_layer_kind_for(layer_index, kModelLayers);
+    l.window = l.kind == MUSE_SLIDING_ROPE ? 2048 : 0;
+    l.rope_theta = l.kind == MUSE_SLIDING_ROPE ? 500000.0f : 0.0f;
+    l.rms_eps = 1e-5f;
+    l.q_norm_gain = 3.87f;
+    l.k_norm_gain = 1.0f;
+    l.attn_scale = (float)(1.0 / std::sqrt(128.0));
+    l.dtype = dtype;
+    *layer = l;
+    return MUSE_OK;
+}
+
+int32_t muse_layer_kind_for(int32_t layer_index, int32_t n_layers) {
+    if (n_layers < 1 || layer_index < 0 || layer_index >= n_layers) return -1;
+    return layer_index % 4 == 3 ? MUSE_FULL_NOPE : MUSE_SLIDING_ROPE;
+}
+
+muse_status muse_rope_theta_table(float theta, float* out_host64) {
+    if (!out_host64) return MUSE_ERR_NULL;
+    if (!finite_pos(theta)) return MUSE_ERR_LAYER;
+    rope_table(theta, out_host64);
+    return MUSE_OK;
+}
+
+const char* muse_status_str(muse_status s) {
+    switch (s) {
+        case MUSE_OK: return "MUSE_OK";
+        case MUSE_ERR_NULL: return "MUSE_ERR_NULL: a required pointer is NULL";
+        case MUSE_ERR_SHAPE: return "MUSE_ERR_SHAPE: head counts, head_dim or a size out of range";
+        case MUSE_ERR_LAYER: return "MUSE_ERR_LAYER: inconsistent layer parameters";
+        case MUSE_ERR_CAPACITY: return "MUSE_ERR_CAPACITY: max_seq_len + n_new exceeds the cache capacity";
+        case MUSE_ERR_WORKSPACE: return "MUSE_ERR_WORKSPACE: workspace too small";
+        case MUSE_ERR_DTYPE: return "MUSE_ERR_DTYPE: unsupported dtype";
+        case MUSE_ERR_HIP: return "MUSE_ERR_HIP: a HIP launch or event call failed";
+        case MUSE_ERR_ALIGN: return "MUSE_ERR_ALIGN: a pointer is not 16-byte aligned";
+        case MUSE_ERR_ALIAS: return "MUSE_ERR_ALIAS: an output buffer overlaps another buffer";
+    }
+    return "unknown muse_status";
+}
+
+}  // extern "C"

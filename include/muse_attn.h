@@ -87,8 +87,12 @@ typedef enum { MUSE_SLIDING_ROPE = 0, MUSE_FULL_NOPE = 1 } muse_layer_kind;
  *               "How Muse Glimmer Fits an Agent on Your Device",
  *               section "Global attention without RoPE")
  *   rms_eps     finite and > 0 (the model uses 1e-5)
- *   q_norm_gain, k_norm_gain  finite constant QK-norm weights (3.87 and 1.0;
- *               ["Chapter 14" 14.3])
+ *   q_norm_gain, k_norm_gain  constant QK-norm weights (3.87 and 1.0;
+ *               ["Chapter 14" 14.3]), |gain| <= 4096
+ *               (bf16 layers compute Q.K with fp16 operands; normed rows
+ *               are bounded by |gain| * sqrt(128), which stays below fp16's
+ *               65504.  Cache K rows not written by this library must also
+ *               stay below 65504 in magnitude.)
  *   attn_scale  finite and > 0 (1/sqrt(128); ["Chapter 9" 9.5])
  *   dtype       muse_dtype of activations, cache and output               */
 typedef struct {

@@ -1,0 +1,219 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function the
+header declares, refuses bad arguments with the documented status codes
+before enqueueing anything, and its host helpers agree with the oracle.
+
+Every call below carries at least one violation, so none reaches a kernel
+launch; the pointers are fake addresses that are never dereferenced.
+"""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import full_gqa_attention_amd as fa
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muse_attn.h")
+
+OK, NULL, SHAPE, LAYER, CAPACITY, WORKSPACE, DTYPE, HIP, ALIGN, ALIAS = range(10)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muse_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(lib):
+    names = header_functions()
+    assert set(names) == set(fa.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(10):
+        assert fa.status_str(code).startswith(fa.STATUS[code])
+    assert fa.status_str(99) == "unknown muse_status"
+
+
+def test_layer_kind_rule_and_init():
+    full = [l for l in range(52) if fa.layer_kind_for(l) == fa.FULL_NOPE]
+    assert full == list(range(3, 52, 4))
+    assert fa.layer_kind_for(52) == -1 and fa.layer_kind_for(-1) == -1
+    assert fa.layer_kind_for(3, 0) == -1
+    for l in range(52):
+        assert fa.layer_kind_for(l) == oracle.layer_kind(l)
+        lay = fa.layer_init(l, fa.BF16)
+        assert (lay.n_heads, lay.n_kv_heads, lay.head_dim) == (32, 2, 128)
+        assert lay.kind == fa.layer_kind_for(l)
+        if lay.kind == fa.FULL_NOPE:
+            assert lay.window == 0 and lay.rope_theta == 0.0
+        else:
+            assert lay.window == 2048 and lay.rope_theta == 500000.0
+        assert lay.attn_scale == np.float32(1 / math.sqrt(128))
+        assert round(lay.attn_scale, 7) == 0.0883883
+        assert lay.q_norm_gain == np.float32(3.87) and lay.k_norm_gain == 1.0
+        assert lay.rms_eps == np.float32(1e-5)
+    with pytest.raises(fa.MuseError):
+        fa.layer_init(52)
+    with pytest.raises(fa.MuseError):
+        fa.layer_init(0, 7)
+
+
+@pytest.mark.parametrize("theta", [10000.0, 500000.0, 1e6, 2.5])
+def test_rope_table_matches_oracle_bitwise(theta):
+    got = np.array(fa.rope_theta_table(theta), dtype=np.float32)
+    want = oracle.rope_theta_table(theta)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_rope_table_rejects_bad_theta():
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(fa.MuseError) as e:
+            fa.rope_theta_table(bad)
+        assert e.value.code == LAYER
+
+
+# --------------------------------------------------------- validation
+
+BASE = 0x7F0000000000   # fake, 256-aligned addresses, never dereferenced
+MB = 1 << 20
+
+
+class Fake:
+    """A full set of argument values for one call, each buffer in its own range."""
+
+    def __init__(self, decode=False, dtype=fa.BF16, kind=fa.SLIDING_ROPE):
+        self.layer = fa.make_layer(kind, window=2048 if kind == fa.SLIDING_ROPE else 0,
+                                   rope_theta=500000.0 if kind == fa.SLIDING_ROPE else 0.0,
+                                   dtype=dtype)
+        self.decode = decode
+        self.n_seq, self.n_new, self.max_seq_len = 4, 1 if decode else 64, 100
+        self.cap = 256
+        addrs = iter(range(BASE, BASE + 64 * 512 * MB, 512 * MB))
+        self.seq_len, self.q, self.k, self.v, self.gate, self.out, self.ws = (next(addrs) for _ in range(7))
+        self.cache = fa.KvCache(next(addrs), next(addrs), self.cap)
+        self.ws_bytes = 1 << 28
+        self.timer = None
+
+    def call(self, lib):
+        vp = ctypes.c_void_p
+        c = ctypes.byref(self.cache) if self.cache is not None else None
+        lay = ctypes.byref(self.layer) if self.layer is not None else None
+        t = ctypes.byref(self.timer) if self.timer is not None else None
+        if self.decode:
+            return lib.muse_attn_decode(lay, self.n_seq, vp(self.seq_len), self.max_seq_len,
+                                        vp(self.q), vp(self.k), vp(self.v), vp(self.gate), c,
+                                        vp(self.out), vp(self.ws), self.ws_bytes, None, t)
+        return lib.muse_attn_prefill(lay, self.n_seq, self.n_new, vp(self.seq_len), self.max_seq_len,
+                                     vp(self.q), vp(self.k), vp(self.v), vp(self.gate), c,
+                                     vp(self.out), vp(self.ws), self.ws_bytes, None, t)
+
+
+def _mut(attr, value):
+    def f(x):
+        setattr(x, attr, value)
+    return f
+
+
+def _lay(attr, value):
+    def f(x):
+        setattr(x.layer, attr, value)
+    return f
+
+
+CASES = [
+    ("layer NULL", _mut("layer", None), NULL),
+    ("n_heads 16", _lay("n_heads", 16), SHAPE),
+    ("n_kv_heads 4", _lay("n_kv_heads", 4), SHAPE),
+    ("head_dim 64", _lay("head_dim", 64), SHAPE),
+    ("dtype 5", _lay("dtype", 5), DTYPE),
+    ("kind 7", _lay("kind", 7), LAYER),
+    ("sliding window 0", _lay("window", 0), LAYER),
+    ("sliding theta 0", _lay("rope_theta", 0.0), LAYER),
+    ("sliding theta nan", _lay("rope_theta", float("nan")), LAYER),
+    ("sliding theta inf", _lay("rope_theta", float("inf")), LAYER),
+    ("eps 0", _lay("rms_eps", 0.0), LAYER),
+    ("scale negative", _lay("attn_scale", -0.1), LAYER),
+    ("q gain inf", _lay("q_norm_gain", float("inf")), LAYER),
+    ("k gain nan", _lay("k_norm_gain", float("nan")), LAYER),
+    ("q gain above fp16-safe bound", _lay("q_norm_gain", 4097.0), LAYER),
+    ("k gain below -4096", _lay("k_norm_gain", -5000.0), LAYER),
+    ("n_seq negative", _mut("n_seq", -1), SHAPE),
+    ("max_seq_len negative", _mut("max_seq_len", -1), SHAPE),
+    ("max_seq_len beyond f32-exact positions", _mut("max_seq_len", 1 << 24), SHAPE),
+    ("capacity too small", _mut("max_seq_len", 256), CAPACITY),
+    ("cache NULL", _mut("cache", None), NULL),
+    ("q NULL", _mut("q", 0), NULL),
+    ("gate NULL", _mut("gate", 0), NULL),
+    ("seq_len NULL", _mut("seq_len", 0), NULL),
+    ("workspace NULL", _mut("ws", 0), NULL),
+    ("workspace too small", _mut("ws_bytes", 1024), WORKSPACE),
+    ("q misaligned", _mut("q", BASE + 512 * MB * 1 + 8), ALIGN),
+    ("out overlaps q", _mut("out", BASE + 512 * MB * 1 + 4096), ALIAS),
+    ("workspace overlaps cache k", _mut("ws", BASE + 512 * MB * 7 + 4096), ALIAS),
+]
+
+
+@pytest.mark.parametrize("decode", [False, True])
+@pytest.mark.parametrize("name,mutate,code", CASES, ids=[c[0] for c in CASES])
+def test_validation_fails_closed(lib, name, mutate, code, decode):
+    f = Fake(decode=decode)
+    mutate(f)
+    assert f.call(lib) == code
+
+
+@pytest.mark.parametrize("decode", [False, True])
+def test_validation_layer_kinds(lib, decode):
+    f = Fake(decode=decode, kind=fa.FULL_NOPE)
+    f.layer.window = 2048            # a full layer must not carry a window
+    assert f.call(lib) == LAYER
+    f = Fake(decode=decode, kind=fa.FULL_NOPE)
+    f.layer.rope_theta = 500000.0    # nor a RoPE base
+    assert f.call(lib) == LAYER
+    f = Fake(decode=decode)
+    f.cache = fa.KvCache(f.cache.k, f.cache.k, f.cap)   # K and V caches alias
+    assert f.call(lib) == ALIAS
+    f = Fake(decode=decode)
+    f.cache.v = 0
+    assert f.call(lib) == NULL
+    f = Fake(decode=decode)
+    f.timer = fa.KernelTimer(None, None)
+    assert f.call(lib) == NULL
+
+
+def test_empty_batches_are_valid_noops(lib):
+    f = Fake()
+    f.n_seq = 0
+    assert f.call(lib) == OK
+    f = Fake()
+    f.n_new = 0
+    assert f.call(lib) == OK
+    f = Fake(decode=True)
+    f.n_seq = 0
+    assert f.call(lib) == OK
+
+
+def test_workspace_sizes():
+    lay = fa.make_layer(fa.FULL_NOPE, dtype=fa.BF16)
+    assert fa.workspace_size(lay, 8, 8192, 0, False) == 8 * 8192 * 4096 * 2
+    f32 = fa.make_layer(fa.FULL_NOPE, dtype=fa.F32)
+    assert fa.workspace_size(f32, 1, 512, 0, False) == 512 * 4096 * 4
+    d1 = fa.workspace_size(lay, 64, 1, 8192, True)
+    d2 = fa.workspace_size(lay, 64, 1, 131072, True)
+    assert 64 * 4096 * 2 < d1 <= d2
+    sl = fa.make_layer(fa.SLIDING_ROPE, window=2048, rope_theta=5e5, dtype=fa.BF16)
+    # a sliding layer's split depends on the window, not the context
+    assert fa.workspace_size(sl, 16, 1, 131072, True) == fa.workspace_size(sl, 16, 1, 4096, True)
+    with pytest.raises(fa.MuseError):
+        fa.workspace_size(lay, -1, 1, 10, True)
