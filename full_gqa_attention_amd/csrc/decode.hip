@@ -1,48 +1,100 @@
-// decode.hip -- kernel (c): split-K decode attention for one new token per
-// sequence, and the combine kernel that merges the splits and applies the
+// decode.hip -- kernel (c): the whole decode step (one new token per
+// sequence) in a single launch: QK-norm and RoPE of the new Q and K, the KV
+// append, split-K attention over the cache, the merge of the splits and the
 // sigmoid gate.
 //
 // The step is bound by reading the cache: 1,024 bytes of K and V per visible
 // row per sequence ("Chapter 9 - The Muse Glimmer architecture" 9.5, 9.6),
-// shared by the 16 query heads of each KV head (Ch 9, Figure 9.3).  So one
-// workgroup owns one (sequence, KV head, split) and computes all 16 heads
-// from a single pass over its rows: scores are a 16-keys x 16-heads MFMA
-// tile (S^T = K Q^T, fp16 16x16x32 on bf16 layers with K converted as it is
-// staged), P.V a second MFMA (O^T = V^T P^T, bf16 16x16x16) whose B operand is the score tile as it sits in registers.
-// Rows stream through LDS in 64-row tiles with 16-byte coalesced loads; the
-// next tile is fetched into registers while the current one is computed.
-// Within a wave the row max over 16 keys needs two lane exchanges (xor 16,
-// 32); the 4 waves of a workgroup merge their (max, sum, O) in LDS and the
-// workgroup writes one partial per head.  Visible rows are [p - W + 1, p] on
-// sliding layers and [0, p] on full layers (Ch 9, 9.7), with p = seq_len.
+// shared by the 16 query heads of each KV head (Ch 9, Figure 9.3).  One
+// workgroup owns one (sequence, KV head, split) and computes all 16 heads in
+// a single pass over its rows.
+//
+// Streaming: each wave owns every fourth 16-row sub-tile of the split and
+// keeps DEPTH sub-tiles of loads in flight in registers; there is no
+// workgroup barrier inside the loop, so the waves of a CU overlap freely.
+//   * K goes straight from HBM into the A-operand layout of a 16x16x32 MFMA
+//     (16 rows x 16 heads per tile, S^T = K Q^T).  On bf16 layers Q-hat is
+//     split into bf16 hi + lo parts (two MFMAs), which scores with about 16
+//     significant bits and takes the stored bf16 keys as they are.
+//   * V rows are written to a wave-private LDS buffer and read back with the
+//     transposing LDS load (ds_read_b64_tr_b16), which delivers the A operand
+//     of O^T = V^T P^T (16x16x16 MFMA) directly; P^T is the score tile as it
+//     sits in registers.
+//   * Online softmax in the log2 domain; the row max over 16 keys needs two
+//     lane exchanges (xor 16, 32).
+//
+// Before the loop each workgroup computes Q-hat of its 16 heads from the raw
+// Q (norm, gain, RoPE on sliding layers: "Chapter 14 - QK-norm and RoPE"
+// 14.3-14.5).  The workgroup whose split holds position p also normalises and
+// rotates the new K, stores K-hat and V to cache row p (Ch 14, 14.7) and
+// substitutes that row in its registers.
+//
+// After the loop the 4 waves merge in LDS; each split writes a partial (max,
+// sum, O); the last split of a (sequence, KV head) to arrive merges all of
+// them and applies the gate (Ch 9, 9.8).  Arrivals are counted in a 64-bit
+// word holding (call tag, count): a word carrying another call's tag counts
+// as zero, so the workspace needs no clearing; the merging split resets the
+// count.  Splits that would cover no row of a shorter sequence exit at once.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
+#ifndef MUSE_DECODE_WAVES
+#define MUSE_DECODE_WAVES 2        // waves per SIMD the register budget targets
+#endif
+#ifndef MUSE_DECODE_DEPTH
+#define MUSE_DECODE_DEPTH 3        // 16-row sub-tiles in flight per wave
+#endif
+
 namespace muse {
 
+// Split partials cross workgroups (and XCDs): written and read with
+// agent-scope atomic accesses, which are coherent per access.
+__device__ __forceinline__ void publish(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float observe(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T> struct DecodeTraits;
+// bf16: K in registers in MFMA layout (4 x 16 B per lane), V row-major (4 x 16 B)
+template <> struct DecodeTraits<bf16_t> {
+    static constexpr int KREG = 4, VREG = 4;
+    static constexpr int LDV = kHeadDim + 16;          // V row stride in LDS (elements)
+    static constexpr int LDKW = 0;                     // no K staging in LDS
+};
+// f32 (parity path): K and V both row-major through LDS (8 x 16 B each)
+template <> struct DecodeTraits<float> {
+    static constexpr int KREG = 8, VREG = 8;
+    static constexpr int LDV = kHeadDim + 4;
+    static constexpr int LDKW = kHeadDim + 4;
+};
+
 template <typename T>
-__global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
-    typedef typename ScoreType<T>::type TQ;         // Q.K^T operand type
-    using MW = Mma16Wide<TQ>;
-    using MN = Mma16Narrow<T>;
-    constexpr int D = kHeadDim, BT = kDecodeTile;
-    constexpr int LDK = D + 16 / (int)sizeof(T);
-    static_assert(sizeof(TQ) == sizeof(T), "K staging keeps the row size");
-    constexpr int KW = MW::KPL, KN = MN::KPL;
-    constexpr int NSTQ = D / (4 * KW);                 // K-steps of Q.K
-    constexpr int NSTP = 4 / KN;                       // K-steps of P.V (16 keys)
-    constexpr int CPR = D * (int)sizeof(T) / 16;       // 16-byte chunks per row
-    constexpr int NCH = BT * CPR;
-    constexpr int PER_THREAD = NCH / 256;
-    static_assert(NCH % 256 == 0, "tile chunks must divide the workgroup");
-    // LDS: K and V tiles; reused at the end for the 4-wave merge
-    constexpr int TILE_ELEMS = BT * LDK;
-    constexpr int MERGE_FLOATS = 4 * kHeadsPerKv * (D + 2);
-    constexpr int LDS_BYTES = (2 * TILE_ELEMS * (int)sizeof(T) > MERGE_FLOATS * 4)
-                                  ? 2 * TILE_ELEMS * (int)sizeof(T) : MERGE_FLOATS * 4;
+struct SubTile {
+    u32x4 k[DecodeTraits<T>::KREG];
+    u32x4 v[DecodeTraits<T>::VREG];
+};
+
+template <typename T, int DEPTH>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MUSE_DECODE_WAVES, MUSE_DECODE_WAVES)))
+void decode_kernel(DecodeArgs a) {
+    using Tr = DecodeTraits<T>;
+    constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
+    constexpr int D = kHeadDim, HG = kHeadsPerKv, SUB = 16;
+    constexpr int LDV = Tr::LDV, LDKW = Tr::LDKW, LDQ = D + 4;
+    constexpr int ES = (int)sizeof(T);
+    constexpr int WAVE_V = SUB * LDV * ES, WAVE_K = SUB * LDKW * ES;
+    constexpr int LOOP_BYTES = 4 * (WAVE_V + WAVE_K) + HG * LDQ * 4;
+    constexpr int MERGE_BYTES = 4 * HG * (D + 2) * 4;
+    constexpr int LDS_BYTES = LOOP_BYTES > MERGE_BYTES ? LOOP_BYTES : MERGE_BYTES;
+    // per-wave V (and f32 K) buffers and the f32 Q-hat; the 4-wave merge after the loop
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
-    TQ* Ks = (TQ*)lds;
-    T* Vs = (T*)(Ks + TILE_ELEMS);
+    __shared__ __attribute__((aligned(16))) T knew[D];    // new key row p (stored values)
+    __shared__ __attribute__((aligned(16))) T vnew[D];    // new value row p
+    __shared__ int last_flag;
 
     const int b = blockIdx.x;
     const int c = b % a.nsplit;
@@ -52,96 +104,178 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
     const int l16 = lane & 15, q4 = lane >> 4;
     const int L = a.seq_len[s];
     const int W = a.window;
+    const int64_t obase = ((int64_t)s * kHeads + g * HG) * D;     // out/gate/q of head 16g
 
+    if (L < 0 || L > a.max_seq_len) {                  // refused on the device
+        if (c == 0)
+            for (int i = tid; i < HG * D; i += 256) ((T*)a.out)[obase + i] = from_f32<T>(__builtin_nanf(""));
+        return;
+    }
     const int64_t p = L;
     const int64_t lo = (W > 0) ? max((int64_t)0, p - W + 1) : 0;
     const int64_t cs = lo + (int64_t)c * a.chunk;
-    const int64_t ce = min(cs + (int64_t)a.chunk, p + 1);     // exclusive
+    if (cs > p) return;                                // split beyond this sequence's rows
+    const int64_t ce = min(cs + (int64_t)a.chunk, p + 1);   // exclusive
+    const int n_live = (int)((p - lo) / a.chunk) + 1;       // splits with rows
+    const bool owns_p = (ce == p + 1);
+    const int n_sub = (int)((ce - cs + SUB - 1) / SUB);
+    const int my_cnt = n_sub > wave ? (n_sub - wave + 3) / 4 : 0;  // sub-tiles wave, wave+4, ...
 
-    const int64_t pbase = ((int64_t)s * kHeads + g * kHeadsPerKv) * a.nsplit + c;  // head 16g, split c
-    if (L < 0 || L > a.max_seq_len || cs >= ce) {
-        // empty split (or a refused sequence): a neutral partial
-        for (int i = tid; i < kHeadsPerKv * D; i += 256) {
-            const int hh = i / D, d = i % D;
-            a.part_o[(pbase + (int64_t)hh * a.nsplit) * D + d] = 0.0f;
-        }
-        if (tid < kHeadsPerKv) {
-            a.part_m[pbase + (int64_t)tid * a.nsplit] = kNegInf;
-            a.part_l[pbase + (int64_t)tid * a.nsplit] = 0.0f;
-        }
-        return;
-    }
+    char* wave_lds = lds + wave * (WAVE_V + WAVE_K);
+    T* Vw = (T*)wave_lds;
+    T* Kw = (T*)(wave_lds + WAVE_V);
+    float* Qf = (float*)(lds + 4 * (WAVE_V + WAVE_K));
 
-    // Q-hat of head 16g + l16 as the B operand of S^T = K Q^T
-    typename MW::Frag qf[NSTQ];
-    {
-        const TQ* qrow = (const TQ*)a.qhat + ((int64_t)s * kHeads + g * kHeadsPerKv + l16) * D;
+    // ---- loads of one 16-row sub-tile (rows >= ce and row p are zero)
+    const int64_t row_stride = (int64_t)kKvHeads * D * ES;          // bytes per position
+    const char* gk = (const char*)a.cache_k + ((int64_t)s * a.capacity * kKvHeads + g) * D * ES;
+    const char* gv = (const char*)a.cache_v + ((int64_t)s * a.capacity * kKvHeads + g) * D * ES;
+    auto issue = [&](SubTile<T>& t, int k) __attribute__((always_inline)) {
+        const int64_t j0 = cs + (int64_t)SUB * (wave + 4 * k);
+        if constexpr (kBf16) {
+            const int64_t jr = j0 + l16;               // K: row l16, MFMA A layout
 #pragma unroll
-        for (int st = 0; st < NSTQ; ++st) qf[st] = *(const typename MW::Frag*)(qrow + 4 * KW * st + KW * q4);
-    }
-
-    const char* gk = (const char*)a.cache_k;
-    const char* gv = (const char*)a.cache_v;
-    const int ntiles = (int)((ce - cs + BT - 1) / BT);
-    uint4 kr[PER_THREAD], vr[PER_THREAD];
-    auto fetch = [&](int it) {
-        const int64_t j0 = cs + (int64_t)it * BT;
+            for (int st = 0; st < 4; ++st) {
+                t.k[st] = u32x4{0, 0, 0, 0};
+                if (jr < ce && jr != p)
+                    t.k[st] = *(const u32x4*)(gk + jr * row_stride + (8 * q4 + 32 * st) * ES);
+            }
 #pragma unroll
-        for (int u = 0; u < PER_THREAD; ++u) {
-            const int cidx = tid + 256 * u;
-            const int r = cidx / CPR, cc = cidx % CPR;
-            const int64_t jj = j0 + r;
-            kr[u] = uint4{0, 0, 0, 0};
-            vr[u] = uint4{0, 0, 0, 0};
-            if (jj < ce) {
-                const int64_t off = ((((int64_t)s * a.capacity + jj) * kKvHeads + g) * D) * (int64_t)sizeof(T) + cc * 16;
-                kr[u] = *(const uint4*)(gk + off);
-                vr[u] = *(const uint4*)(gv + off);
+            for (int u = 0; u < 4; ++u) {              // V: rows 4u + lane/16, 16-B chunk lane%16
+                const int64_t jv = j0 + 4 * u + q4;
+                t.v[u] = u32x4{0, 0, 0, 0};
+                if (jv < ce && jv != p) t.v[u] = *(const u32x4*)(gv + jv * row_stride + l16 * 16);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {              // rows 2u + lane/32, 16-B chunk lane%32
+                const int64_t jj = j0 + 2 * u + (lane >> 5);
+                t.k[u] = u32x4{0, 0, 0, 0};
+                t.v[u] = u32x4{0, 0, 0, 0};
+                if (jj < ce && jj != p) {
+                    t.k[u] = *(const u32x4*)(gk + jj * row_stride + (lane & 31) * 16);
+                    t.v[u] = *(const u32x4*)(gv + jj * row_stride + (lane & 31) * 16);
+                }
             }
         }
     };
+
+    // pipeline stages as named variables (an indexed array of them ends up in scratch)
+    static_assert(DEPTH >= 1 && DEPTH <= 4, "pipeline depth 1..4");
+    SubTile<T> b0, b1, b2, b3;
+    if (0 < my_cnt) issue(b0, 0);
+    if constexpr (DEPTH > 1) if (1 < my_cnt) issue(b1, 1);
+    if constexpr (DEPTH > 2) if (2 < my_cnt) issue(b2, 2);
+    if constexpr (DEPTH > 3) if (3 < my_cnt) issue(b3, 3);
+
+    // ---- prologue: Q-hat of the 16 heads (f32 in LDS); the owner of p also
+    // makes the new K/V row
+    {
+        float sn = 0.0f, cs_ = 1.0f;
+        if (a.rope) rope_sincos(a.theta, lane, p, sn, cs_);
+        const T* q = (const T*)a.q + obase;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int hh = wave * 4 + i;
+            float y0, y1;
+            norm_rope_pair(to_f32(q[hh * D + 2 * lane]), to_f32(q[hh * D + 2 * lane + 1]), a.eps,
+                           a.q_gain, a.rope, sn, cs_, y0, y1);
+            Qf[hh * LDQ + 2 * lane] = y0;
+            Qf[hh * LDQ + 2 * lane + 1] = y1;
+        }
+        if (owns_p && wave == 0) {
+            const T* kr = (const T*)a.k + ((int64_t)s * kKvHeads + g) * D;
+            float y0, y1;
+            norm_rope_pair(to_f32(kr[2 * lane]), to_f32(kr[2 * lane + 1]), a.eps, a.k_gain, a.rope,
+                           sn, cs_, y0, y1);
+            const T k0 = from_f32<T>(y0), k1 = from_f32<T>(y1);
+            T* dst = (T*)a.cache_k + (((int64_t)s * a.capacity + p) * kKvHeads + g) * D;
+            dst[2 * lane] = k0;
+            dst[2 * lane + 1] = k1;
+            knew[2 * lane] = k0;
+            knew[2 * lane + 1] = k1;
+        }
+        if (owns_p && wave == 1) {
+            const T* vr = (const T*)a.v + ((int64_t)s * kKvHeads + g) * D;
+            T* dst = (T*)a.cache_v + (((int64_t)s * a.capacity + p) * kKvHeads + g) * D;
+            const T v0 = vr[2 * lane], v1 = vr[2 * lane + 1];
+            dst[2 * lane] = v0;
+            dst[2 * lane + 1] = v1;
+            vnew[2 * lane] = v0;
+            vnew[2 * lane + 1] = v1;
+        }
+    }
+    __syncthreads();
+
+    // Q-hat as the B operand of S^T = K Q^T: lane holds head l16, k-group q4
+    constexpr int NSTQ = kBf16 ? 4 : 32;               // 16x16x32 bf16 / 16x16x4 f32 steps
+    using MW = Mma16Wide<T>;
+    using MN = Mma16Narrow<T>;
+    typename MW::Frag qhi[NSTQ], qlo[kBf16 ? NSTQ : 1];
+    {
+        const float* qrow = Qf + l16 * LDQ;
+        if constexpr (kBf16) {
+#pragma unroll
+            for (int st = 0; st < NSTQ; ++st) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const float x = qrow[32 * st + 8 * q4 + t];
+                    const bf16_t hi = (bf16_t)x;
+                    qhi[st][t] = hi;
+                    qlo[st][t] = (bf16_t)(x - (float)hi);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int st = 0; st < NSTQ; ++st) qhi[st] = qrow[4 * st + q4];
+        }
+    }
 
     floatx4 o[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{};
     float m_run = kNegInf, l_run = 0.0f;
 
-    fetch(0);
-    for (int it = 0; it < ntiles; ++it) {
-        const int64_t j0 = cs + (int64_t)it * BT;
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < PER_THREAD; ++u) {
-            const int cidx = tid + 256 * u;
-            const int r = cidx / CPR, cc = cidx % CPR;
-            *(uint4*)((char*)Ks + (r * LDK) * (int)sizeof(TQ) + cc * 16) = k_chunk_to_score(kr[u], T{});
-            *(uint4*)((char*)Vs + (r * LDK) * (int)sizeof(T) + cc * 16) = vr[u];
-        }
-        __syncthreads();
-        if (it + 1 < ntiles) fetch(it + 1);
-
-        // this wave's 16 keys: rows 16*wave .. +15 of the tile
-        const int64_t jw = j0 + 16 * wave;
-        if (jw >= ce) continue;
+    auto process = [&](SubTile<T>& t, int k) __attribute__((always_inline)) {
+        const int64_t j0 = cs + (int64_t)SUB * (wave + 4 * k);
+        // ---- scores S^T[key j0 + 4*q4 + i][head l16]
         floatx4 sc = floatx4{};
+        if constexpr (kBf16) {
+            const bool krow_p = (j0 + l16 == p);
 #pragma unroll
-        for (int st = 0; st < NSTQ; ++st) {
-            const typename MW::Frag kf =
-                *(const typename MW::Frag*)(Ks + (16 * wave + l16) * LDK + 4 * KW * st + KW * q4);
-            sc = MW::mma(kf, qf[st], sc);
+            for (int st = 0; st < 4; ++st) {
+                u32x4 kraw = t.k[st];
+                if (krow_p) kraw = *(const u32x4*)(knew + 8 * q4 + 32 * st);
+                const bf16x8 kf = __builtin_bit_cast(bf16x8, kraw);
+                sc = MW::mma(kf, qhi[st], sc);
+                sc = MW::mma(kf, qlo[st], sc);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int r = 2 * u + (lane >> 5);
+                u32x4 kraw = t.k[u], vraw = t.v[u];
+                if (j0 + r == p) {
+                    kraw = *(const u32x4*)(knew + (lane & 31) * 4);
+                    vraw = *(const u32x4*)(vnew + (lane & 31) * 4);
+                }
+                *(u32x4*)(Kw + r * LDKW + (lane & 31) * 4) = kraw;
+                *(u32x4*)(Vw + r * LDV + (lane & 31) * 4) = vraw;
+            }
+#pragma unroll
+            for (int st = 0; st < NSTQ; ++st) sc = MW::mma(Kw[l16 * LDKW + 4 * st + q4], qhi[st], sc);
         }
-        // sc[i]: key jw + 4*q4 + i, head 16g + l16
         float mx = kNegInf;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float x = sc[i] * a.scale_log2;
-            if (jw + 4 * q4 + i >= ce) x = kNegInf;
+            if (j0 + 4 * q4 + i >= ce) x = kNegInf;
             sc[i] = x;
             mx = fmaxf(mx, x);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);            // finite: key jw is visible
+        const float m_new = fmaxf(m_run, mx);            // finite: key j0 is visible
         const float alpha = fast_exp2(m_run - m_new);
         float rs = 0.0f;
 #pragma unroll
@@ -154,20 +288,50 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
 
+        // ---- O^T += V^T P^T
+        if constexpr (kBf16) {
 #pragma unroll
-        for (int st = 0; st < NSTP; ++st) {
+            for (int u = 0; u < 4; ++u) {
+                u32x4 vraw = t.v[u];
+                if (j0 + 4 * u + q4 == p) vraw = *(const u32x4*)(vnew + l16 * 8);
+                *(u32x4*)(Vw + (4 * u + q4) * LDV + l16 * 8) = vraw;
+            }
             typename MN::Frag pf;
 #pragma unroll
-            for (int t = 0; t < KN; ++t) frag_set(pf, t, sc[st * KN + t]);
+            for (int i = 0; i < 4; ++i) frag_set(pf, i, sc[i]);
+            // source lane i of each 16-lane group q4 points at V row 4*q4 + i/4,
+            // columns 4*(i%4) .. +3 of the 16-column block dt
+            typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+            const int vrow = 4 * q4 + (l16 >> 2);
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt) {
-                typename MN::Frag vf;
-#pragma unroll
-                for (int t = 0; t < KN; ++t)
-                    frag_set_raw(vf, t, Vs[(16 * wave + 4 * q4 + st * KN + t) * LDK + 16 * dt + l16]);
+                const T* src = Vw + vrow * LDV + 16 * dt + 4 * (l16 & 3);
+                const shortx4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_shortx4*)(__attribute__((address_space(3))) void*)src);
                 o[dt] = MN::mma(vf, pf, o[dt]);
             }
+        } else {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {           // 16x16x4 f32: key 4*q4 + st
+                const float pf = sc[st];
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt)
+                    o[dt] = MN::mma(Vw[(4 * q4 + st) * LDV + 16 * dt + l16], pf, o[dt]);
+            }
         }
+    };
+
+    auto stage = [&](SubTile<T>& t, int k) __attribute__((always_inline)) {
+        if (k < my_cnt) {
+            process(t, k);
+            if (k + DEPTH < my_cnt) issue(t, k + DEPTH);
+        }
+    };
+    for (int k0 = 0; k0 < my_cnt; k0 += DEPTH) {
+        stage(b0, k0);
+        if constexpr (DEPTH > 1) stage(b1, k0 + 1);
+        if constexpr (DEPTH > 2) stage(b2, k0 + 2);
+        if constexpr (DEPTH > 3) stage(b3, k0 + 3);
     }
 
     // ---- merge the 4 waves: LDS holds per wave [16 heads][128 + 2] floats
@@ -175,7 +339,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
     l_run += __shfl_xor(l_run, 32, 64);
     __syncthreads();
     float* mg = (float*)lds;
-    float* mw = mg + (wave * kHeadsPerKv + l16) * (D + 2);
+    float* mw = mg + (wave * HG + l16) * (D + 2);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
@@ -185,71 +349,92 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
         mw[D + 1] = l_run;
     }
     __syncthreads();
-    for (int i = tid; i < kHeadsPerKv * D; i += 256) {
+    const T* gate = (const T*)a.gate + obase;
+    T* out = (T*)a.out + obase;
+    const int64_t pbase = ((int64_t)s * kHeads + g * HG) * a.nsplit + c;   // head 16g, split c
+    for (int i = tid; i < HG * D; i += 256) {
         const int hh = i / D, d = i % D;
         float M = kNegInf;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, mg[(w * kHeadsPerKv + hh) * (D + 2) + D]);
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, mg[(w * HG + hh) * (D + 2) + D]);
         float acc = 0.0f, den = 0.0f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const float* row = mg + (w * kHeadsPerKv + hh) * (D + 2);
+            const float* row = mg + (w * HG + hh) * (D + 2);
             const float e = (row[D] == kNegInf) ? 0.0f : fast_exp2(row[D] - M);
             acc += row[d] * e;
             den += row[D + 1] * e;
         }
-        const int64_t pi = pbase + (int64_t)hh * a.nsplit;
-        a.part_o[pi * D + d] = acc;
-        if (d == 0) {
-            a.part_m[pi] = M;
-            a.part_l[pi] = den;
+        if (n_live == 1) {                             // the only split: finish here
+            out[i] = from_f32<T>(acc / den * sigmoid(to_f32(gate[i])));
+        } else {
+            const int64_t pi = pbase + (int64_t)hh * a.nsplit;
+            publish(a.part_o + pi * D + d, acc);
+            if (d == 0) {
+                publish(a.part_m + pi, M);
+                publish(a.part_l + pi, den);
+            }
         }
     }
-}
+    if (n_live == 1) return;
 
-// Merge the splits of one (sequence, head): m = max m_c, l = sum l_c 2^(m_c - m),
-// o = sum o_c 2^(m_c - m) / l, then out = o * sigma(gate).
-template <typename T>
-__global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
-    const int sh = blockIdx.x;                         // s * 32 + h
-    const int s = sh / kHeads;
-    const int d = threadIdx.x;
-    const int L = a.seq_len[s];
-    const int64_t obase = (int64_t)sh * kHeadDim;      // n_new == 1
-    T* out = (T*)a.out;
-    if (L < 0 || L > a.max_seq_len) {
-        out[obase + d] = from_f32<T>(__builtin_nanf(""));
-        return;
+    // ---- arrival; the last split merges every split's partial.  The
+    // partials were written with agent-coherent stores (see publish); waiting
+    // for them to complete before the barrier orders them before the arrival
+    // count, and the merging split reads them with agent-coherent loads.  No
+    // agent-scope fence is used: on this GPU one writes back / invalidates
+    // the whole L2 of an XCD, which costs more than the attention itself.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        unsigned long long* word = a.arrivals + (s * kKvHeads + g);
+        unsigned long long old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        unsigned int arrived = 0;
+        for (;;) {                                     // retries only on contention
+            const unsigned int cnt = ((unsigned int)(old >> 32) == a.tag) ? (unsigned int)old : 0u;
+            const unsigned long long want = ((unsigned long long)a.tag << 32) | (cnt + 1);
+            if (__hip_atomic_compare_exchange_strong(word, &old, want, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                arrived = cnt + 1;
+                break;
+            }
+        }
+        last_flag = (arrived == (unsigned int)n_live);
+        if (last_flag)                                 // ready for a replay with the same tag
+            __hip_atomic_store(word, (unsigned long long)a.tag << 32, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
-    const int64_t pb = (int64_t)sh * a.nsplit;
+    __syncthreads();
+    if (!last_flag) return;
+
+    // thread -> (head hh, 8 consecutive dims)
+    const int hh = tid >> 4, d0 = (tid & 15) * 8;
+    const int64_t hb = ((int64_t)s * kHeads + g * HG + hh) * a.nsplit;
     float M = kNegInf;
-    for (int c = 0; c < a.nsplit; ++c) M = fmaxf(M, a.part_m[pb + c]);
-    float acc = 0.0f, den = 0.0f;
-    for (int c = 0; c < a.nsplit; ++c) {
-        const float mc = a.part_m[pb + c];
-        const float e = (mc == kNegInf) ? 0.0f : fast_exp2(mc - M);
-        acc += a.part_o[(pb + c) * kHeadDim + d] * e;
-        den += a.part_l[pb + c] * e;
+    for (int cc = 0; cc < n_live; ++cc) M = fmaxf(M, observe(a.part_m + hb + cc));
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float den = 0.0f;
+    for (int cc = 0; cc < n_live; ++cc) {
+        const float e = fast_exp2(observe(a.part_m + hb + cc) - M);
+        den += observe(a.part_l + hb + cc) * e;
+        const float* po = a.part_o + (hb + cc) * D + d0;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[x] += observe(po + x) * e;
     }
-    const float gv = to_f32(((const T*)a.gate)[obase + d]);
-    out[obase + d] = from_f32<T>(acc / den * sigmoid(gv));
+    const float inv = 1.0f / den;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+        const int i = hh * D + d0 + x;
+        out[i] = from_f32<T>(acc[x] * inv * sigmoid(to_f32(gate[i])));
+    }
 }
 
-hipError_t launch_decode(const AttnArgs& a, int dtype, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream) {
     const dim3 grid((unsigned)(a.n_seq * kKvHeads * a.nsplit)), block(256);
     if (dtype == 1)
-        hipLaunchKernelGGL(decode_kernel<bf16_t>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL((decode_kernel<bf16_t, MUSE_DECODE_DEPTH>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL(decode_kernel<float>, grid, block, 0, stream, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_combine(const AttnArgs& a, int dtype, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.n_seq * kHeads)), block(128);
-    if (dtype == 1)
-        hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL((decode_kernel<float, 2>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

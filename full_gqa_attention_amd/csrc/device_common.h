@@ -12,6 +12,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16_t;
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // 16 raw bytes
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
@@ -64,6 +65,38 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float sigmoid(float g) { return 1.0f / (1.0f + __expf(-g)); }
 
 constexpr float kNegInf = -__builtin_huge_valf();
+
+// ----------------------------------------------------- QK-norm and RoPE
+// One head vector of 128 values per wave: lane i holds the adjacent pair
+// (x[2i], x[2i+1]), which is RoPE pair i.
+
+// sin/cos of the f32 angle f32(p) * theta[lane] (accurate sincosf).  The
+// table sits in kernel arguments; the unrolled select keeps every access at
+// a constant index.
+__device__ __forceinline__ void rope_sincos(const float (&theta)[64], int lane, int64_t p,
+                                            float& sn, float& cs) {
+    float th = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) th = (lane == i) ? theta[i] : th;
+    const float ang = (float)p * th;
+    sincosf(ang, &sn, &cs);
+}
+
+// RMS-normalise the wave's 128-vector, scale by gain, then (rope) rotate the
+// lane's pair by the angle whose sin/cos are given.
+__device__ __forceinline__ void norm_rope_pair(float x0, float x1, float eps, float gain, bool rope,
+                                               float sn, float cs, float& y0, float& y1) {
+    const float ss = wave_sum(x0 * x0 + x1 * x1);
+    const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps);
+    y0 = (x0 * r) * gain;
+    y1 = (x1 * r) * gain;
+    if (rope) {
+        const float z0 = y0 * cs - y1 * sn;
+        const float z1 = y0 * sn + y1 * cs;
+        y0 = z0;
+        y1 = z1;
+    }
+}
 
 // ---------------------------------------------------------------- MFMA
 // 32x32 tiles (prefill).  Operand layout for C = A * B (A: 32 x K, B: K x 32):

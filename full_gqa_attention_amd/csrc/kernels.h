@@ -27,7 +27,7 @@ struct PrepArgs {
     float theta[64];        // f32 RoPE frequency table
 };
 
-// Kernels (b) and (c): attention over the cache with the gate epilogue.
+// Kernel (b): prefill attention over the cache with the gate epilogue.
 struct AttnArgs {
     const void* qhat;       // workspace Q-hat [S][N][32][128]
     const void* gate;       // [S][N][4096]
@@ -41,12 +41,37 @@ struct AttnArgs {
     int32_t n_new;
     int32_t window;         // 0: full causal; else keys with p - j < window
     float scale_log2;       // attn_scale * log2(e)
-    // decode split-K
+};
+
+// Kernel (c): the whole decode step for one new token per sequence in one
+// launch -- QK-norm/RoPE of Q and K, the KV append, split-K attention, the
+// merge of the splits and the gate.
+struct DecodeArgs {
+    const void* q;          // [S][32][128]
+    const void* k;          // [S][2][128]
+    const void* v;          // [S][2][128]
+    const void* gate;       // [S][4096]
+    void* out;              // [S][4096]
+    void* cache_k;          // [S][cap][2][128]
+    void* cache_v;
+    int64_t capacity;
+    const int32_t* seq_len; // device [S]
+    int32_t max_seq_len;
+    int32_t n_seq;
+    int32_t window;         // 0: full causal; else keys with p - j < window
+    int32_t rope;           // 1: sliding layer (rotate), 0: NoPE
+    float eps;
+    float q_gain;
+    float k_gain;
+    float scale_log2;       // attn_scale * log2(e)
     int32_t chunk;          // keys per split
     int32_t nsplit;         // splits per (sequence, KV head)
+    uint32_t tag;           // nonzero, distinct per call: marks this call's arrivals
     float* part_o;          // [S][32][nsplit][128] unnormalised partial outputs
     float* part_m;          // [S][32][nsplit] partial maxima (log2 domain)
     float* part_l;          // [S][32][nsplit] partial softmax denominators
+    unsigned long long* arrivals;  // [S][2] (tag << 32 | splits arrived)
+    float theta[64];        // f32 RoPE frequency table
 };
 
 // Launch geometry shared by the host code and the kernels.
@@ -58,7 +83,6 @@ int prefill_grid(int n_seq, int n_new);
 
 hipError_t launch_prep(const PrepArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_prefill(const AttnArgs& a, int dtype, hipStream_t stream);
-hipError_t launch_decode(const AttnArgs& a, int dtype, hipStream_t stream);
-hipError_t launch_combine(const AttnArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
 
 }  // namespace muse

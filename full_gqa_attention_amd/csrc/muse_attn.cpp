@@ -5,8 +5,10 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "kernels.h"
@@ -14,6 +16,7 @@
 namespace {
 
 using muse::AttnArgs;
+using muse::DecodeArgs;
 using muse::PrepArgs;
 
 constexpr int kHeads = 32, kKvHeads = 2, kHeadDim = 128;
@@ -55,15 +58,22 @@ muse_status check_sizes(int32_t n_seq, int32_t n_new, int32_t max_seq_len) {
     return MUSE_OK;
 }
 
-// Decode split: about 2048 workgroups in total, chunks a multiple of the
-// 64-row tile.  The span of visible rows is at most window (sliding) or
-// max_seq_len + 1 (full).
+int64_t decode_target_blocks() {
+    const char* e = std::getenv("MUSE_DECODE_TARGET_BLOCKS");
+    const long v = e ? std::strtol(e, nullptr, 10) : 0;
+    return v > 0 ? v : 256;
+}
+
+// Decode split: about decode_target_blocks() workgroups in total, chunks a
+// multiple of the 64-row tile.  The span of visible rows is at most window
+// (sliding) or max_seq_len + 1 (full).
 void decode_split(const muse_attn_layer* l, int32_t n_seq, int32_t max_seq_len,
                   int32_t* chunk, int32_t* nsplit) {
     int64_t span = (int64_t)max_seq_len + 1;
     if (l->kind == MUSE_SLIDING_ROPE && l->window < span) span = l->window;
     const int64_t pairs = (int64_t)(n_seq > 0 ? n_seq : 1) * kKvHeads;
-    int64_t want = (2048 + pairs - 1) / pairs;
+    const int64_t target = decode_target_blocks();
+    int64_t want = (target + pairs - 1) / pairs;
     const int64_t tiles = (span + muse::kDecodeTile - 1) / muse::kDecodeTile;
     if (want > tiles) want = tiles;
     if (want < 1) want = 1;
@@ -73,8 +83,10 @@ void decode_split(const muse_attn_layer* l, int32_t n_seq, int32_t max_seq_len,
     *nsplit = (int32_t)((span + ch - 1) / ch);
 }
 
+// Prefill: Q-hat [S][N][32][128] (score type, same element size as the layer
+// dtype).  Decode: arrival words [S][2] (u64), then the split partials.
 struct WorkspaceLayout {
-    size_t qhat = 0, part_o = 0, part_m = 0, part_l = 0, total = 0;
+    size_t qhat = 0, arrivals = 0, part_o = 0, part_m = 0, part_l = 0, total = 0;
     int32_t chunk = 0, nsplit = 0;
 };
 
@@ -82,10 +94,13 @@ WorkspaceLayout layout_for(const muse_attn_layer* l, int32_t n_seq, int32_t n_ne
                            int32_t max_seq_len, bool decode) {
     WorkspaceLayout w;
     const size_t es = elem_bytes(l->dtype);
-    if (decode) n_new = 1;
-    size_t off = round_up((size_t)n_seq * n_new * kHeads * kHeadDim * es, kAlign);
-    w.qhat = 0;
-    if (decode) {
+    size_t off = 0;
+    if (!decode) {
+        w.qhat = 0;
+        off = round_up((size_t)n_seq * n_new * kHeads * kHeadDim * es, kAlign);
+    } else {
+        w.arrivals = 0;
+        off = round_up((size_t)n_seq * kKvHeads * sizeof(unsigned long long), kAlign);
         decode_split(l, n_seq, max_seq_len, &w.chunk, &w.nsplit);
         const size_t parts = (size_t)n_seq * kHeads * w.nsplit;
         w.part_o = off;
@@ -105,6 +120,17 @@ struct Range {
     uintptr_t lo, hi;
 };
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// A distinct nonzero 32-bit tag per decode call (see the arrival words in
+// decode.hip); process-wide, never repeats within 2^32 calls.
+uint32_t next_tag() {
+    static std::atomic<uint32_t> counter{0x6d757365u};
+    uint32_t t;
+    do {
+        t = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+    } while (t == 0);
+    return t;
+}
 
 void rope_table(float theta, float* out64) {
     for (int i = 0; i < kHeadDim / 2; ++i)
@@ -152,6 +178,44 @@ muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, cons
             if (j != wi && overlap(all[wi], all[j])) return MUSE_ERR_ALIAS;
 
     char* ws = (char*)workspace;
+    const int dt = layer->dtype;
+    const bool rope = layer->kind == MUSE_SLIDING_ROPE;
+    const float scale_log2 = (float)((double)layer->attn_scale * 1.4426950408889634);
+
+    if (decode) {
+        DecodeArgs da;
+        std::memset(&da, 0, sizeof da);
+        da.q = q;
+        da.k = k;
+        da.v = v;
+        da.gate = gate;
+        da.out = out;
+        da.cache_k = cache->k;
+        da.cache_v = cache->v;
+        da.capacity = cache->capacity;
+        da.seq_len = seq_len;
+        da.max_seq_len = max_seq_len;
+        da.n_seq = n_seq;
+        da.window = rope ? layer->window : 0;
+        da.rope = rope ? 1 : 0;
+        da.eps = layer->rms_eps;
+        da.q_gain = layer->q_norm_gain;
+        da.k_gain = layer->k_norm_gain;
+        da.scale_log2 = scale_log2;
+        da.chunk = wl.chunk;
+        da.nsplit = wl.nsplit;
+        da.tag = next_tag();
+        da.part_o = (float*)(ws + wl.part_o);
+        da.part_m = (float*)(ws + wl.part_m);
+        da.part_l = (float*)(ws + wl.part_l);
+        da.arrivals = (unsigned long long*)(ws + wl.arrivals);
+        if (rope) rope_table(layer->rope_theta, da.theta);
+        if (timer && hipEventRecord(timer->start, stream) != hipSuccess) return MUSE_ERR_HIP;
+        if (muse::launch_decode(da, dt, stream) != hipSuccess) return MUSE_ERR_HIP;
+        if (timer && hipEventRecord(timer->stop, stream) != hipSuccess) return MUSE_ERR_HIP;
+        return MUSE_OK;
+    }
+
     PrepArgs pa;
     std::memset(&pa, 0, sizeof pa);
     pa.q = q;
@@ -165,11 +229,11 @@ muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, cons
     pa.max_seq_len = max_seq_len;
     pa.n_seq = n_seq;
     pa.n_new = n_new;
-    pa.rope = layer->kind == MUSE_SLIDING_ROPE ? 1 : 0;
+    pa.rope = rope ? 1 : 0;
     pa.eps = layer->rms_eps;
     pa.q_gain = layer->q_norm_gain;
     pa.k_gain = layer->k_norm_gain;
-    if (pa.rope) rope_table(layer->rope_theta, pa.theta);
+    if (rope) rope_table(layer->rope_theta, pa.theta);
 
     AttnArgs aa;
     std::memset(&aa, 0, sizeof aa);
@@ -183,24 +247,13 @@ muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, cons
     aa.max_seq_len = max_seq_len;
     aa.n_seq = n_seq;
     aa.n_new = n_new;
-    aa.window = layer->kind == MUSE_SLIDING_ROPE ? layer->window : 0;
-    aa.scale_log2 = (float)((double)layer->attn_scale * 1.4426950408889634);
-    aa.chunk = wl.chunk;
-    aa.nsplit = wl.nsplit;
-    aa.part_o = (float*)(ws + wl.part_o);
-    aa.part_m = (float*)(ws + wl.part_m);
-    aa.part_l = (float*)(ws + wl.part_l);
+    aa.window = rope ? layer->window : 0;
+    aa.scale_log2 = scale_log2;
 
-    const int dt = layer->dtype;
     if (muse::launch_prep(pa, dt, stream) != hipSuccess) return MUSE_ERR_HIP;
     if (timer && hipEventRecord(timer->start, stream) != hipSuccess) return MUSE_ERR_HIP;
-    if (decode) {
-        if (muse::launch_decode(aa, dt, stream) != hipSuccess) return MUSE_ERR_HIP;
-    } else {
-        if (muse::launch_prefill(aa, dt, stream) != hipSuccess) return MUSE_ERR_HIP;
-    }
+    if (muse::launch_prefill(aa, dt, stream) != hipSuccess) return MUSE_ERR_HIP;
     if (timer && hipEventRecord(timer->stop, stream) != hipSuccess) return MUSE_ERR_HIP;
-    if (decode && muse::launch_combine(aa, dt, stream) != hipSuccess) return MUSE_ERR_HIP;
     return MUSE_OK;
 }
 

@@ -172,3 +172,60 @@ def test_empty_inputs():
                      workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
     assert out.shape == (S, 0, 4096)
     assert torch.count_nonzero(ck) == 0
+
+
+def test_decode_workspace_reuse_and_garbage():
+    """The split-arrival words need no clearing: a workspace full of random
+    bytes, reused across calls of different batch sizes, gives the same
+    results as a fresh one."""
+    spec = synth.full()
+    w = _custom("ws", synth.BF16, 6, 3000, 1, [spec])
+    inp = _ragged_inputs(w, spec, [3000, 2500, 100, 3000, 1, 2048], 1)
+    lay = fa.make_layer(spec.kind, dtype=w.dtype)
+
+    def call(n_seq, ws=None):
+        return fa.decode(lay, inp.q[:n_seq], inp.k[:n_seq], inp.v[:n_seq], inp.gate[:n_seq],
+                         inp.cache_k[:n_seq].clone(), inp.cache_v[:n_seq].clone(), inp.seq_len[:n_seq],
+                         max_seq_len=3000, workspace=ws).clone()
+
+    fresh = {n: call(n) for n in (6, 3, 1)}          # the split count depends on the batch
+    n = max(fa.workspace_size(lay, k, 1, 3000, True) for k in (6, 3, 1))
+    ws = torch.randint(0, 256, (n,), dtype=torch.uint8, device=DEV)
+    for n_seq in (6, 3, 6, 1, 6, 3):
+        out = call(n_seq, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, fresh[n_seq])
+
+
+@pytest.mark.parametrize("spec", [synth.sliding(2048, 500000.0), synth.full()], ids=["w2048", "full"])
+def test_decode_graph_replays_match_eager(spec):
+    """A captured decode call replays with the same arrival tag every time;
+    every replay (with new inputs copied in and eager work in between) must
+    equal the eager result on the same inputs."""
+    S, L = 4, 5000
+    w = _custom("graph", synth.BF16, S, L, 1, [spec])
+    inp = _ragged_inputs(w, spec, [L, 4000, 2999, 17], 1)
+    lay = fa.make_layer(spec.kind, window=spec.window, rope_theta=spec.rope_theta, dtype=w.dtype)
+    ws = fa.workspace(lay, S, 1, L, True)
+    q, k, v, g = inp.q.clone(), inp.k.clone(), inp.v.clone(), inp.gate.clone()
+    out = torch.empty_like(g)
+    ck, cv = inp.cache_k.clone(), inp.cache_v.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                      # warm-up outside the capture
+        fa.decode(lay, q, k, v, g, ck, cv, inp.seq_len, out, max_seq_len=L, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fa.decode(lay, q, k, v, g, ck, cv, inp.seq_len, out, max_seq_len=L, workspace=ws)
+    for rep in range(4):
+        new = synth.layer_inputs(w, spec, device=DEV, n_new=1, prefix=0, step=10 + rep, with_cache=False)
+        q.copy_(new.q); k.copy_(new.k); v.copy_(new.v); g.copy_(new.gate)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        eager = fa.decode(lay, q, k, v, g, ck.clone(), cv.clone(), inp.seq_len, max_seq_len=L)
+        torch.cuda.synchronize()
+        assert torch.equal(got, eager), f"replay {rep}"
