@@ -42,14 +42,14 @@ template <> struct ScoreType<float> { typedef float type; };
 
 // 16 bytes of storage-type K -> 16 bytes of score-type K (bf16 -> fp16;
 // f32 unchanged).
-__device__ __forceinline__ uint4 k_chunk_to_score(uint4 x, bf16_t) {
+__device__ __forceinline__ u32x4 k_chunk_to_score(u32x4 x, bf16_t) {
     const bf16x8 b = __builtin_bit_cast(bf16x8, x);
     f16x8 h;
 #pragma unroll
     for (int t = 0; t < 8; ++t) h[t] = (f16_t)(float)b[t];
-    return __builtin_bit_cast(uint4, h);
+    return __builtin_bit_cast(u32x4, h);
 }
-__device__ __forceinline__ uint4 k_chunk_to_score(uint4 x, float) { return x; }
+__device__ __forceinline__ u32x4 k_chunk_to_score(u32x4 x, float) { return x; }
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

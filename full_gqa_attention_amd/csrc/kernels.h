@@ -24,23 +24,30 @@ struct PrepArgs {
     float eps;
     float q_gain;
     float k_gain;
+    float q_scale;          // attn_scale * log2(e), folded into Q-hat
+    // bf16 layers: fp16 copy of the keys the attention kernel reads,
+    // [S][kq_capacity][2][128] (NULL on f32 layers, which read the cache)
+    void* kq;
+    int64_t kq_capacity;
+    int32_t window;         // 0: full; else only rows > p_first - window are copied
+    int32_t conv_blocks;    // prefix-conversion workgroups per sequence
     float theta[64];        // f32 RoPE frequency table
 };
 
 // Kernel (b): prefill attention over the cache with the gate epilogue.
 struct AttnArgs {
-    const void* qhat;       // workspace Q-hat [S][N][32][128]
+    const void* qhat;       // workspace Q-hat [S][N][32][128], scaled by attn_scale * log2(e)
     const void* gate;       // [S][N][4096]
     void* out;              // [S][N][4096]
-    const void* cache_k;    // [S][cap][2][128]
-    const void* cache_v;
+    const void* kq;         // keys in the score type [S][kq_capacity][2][128]
+    int64_t kq_capacity;
+    const void* cache_v;    // [S][capacity][2][128]
     int64_t capacity;
     const int32_t* seq_len; // device [S]
     int32_t max_seq_len;
     int32_t n_seq;
     int32_t n_new;
     int32_t window;         // 0: full causal; else keys with p - j < window
-    float scale_log2;       // attn_scale * log2(e)
 };
 
 // Kernel (c): the whole decode step for one new token per sequence in one

@@ -84,9 +84,11 @@ void decode_split(const muse_attn_layer* l, int32_t n_seq, int32_t max_seq_len,
 }
 
 // Prefill: Q-hat [S][N][32][128] (score type, same element size as the layer
-// dtype).  Decode: arrival words [S][2] (u64), then the split partials.
+// dtype), then on bf16 layers the fp16 key copy [S][max_seq_len + N][2][128].
+// Decode: arrival words [S][2] (u64), then the split partials.
 struct WorkspaceLayout {
-    size_t qhat = 0, arrivals = 0, part_o = 0, part_m = 0, part_l = 0, total = 0;
+    size_t qhat = 0, kq = 0, arrivals = 0, part_o = 0, part_m = 0, part_l = 0, total = 0;
+    int64_t kq_capacity = 0;
     int32_t chunk = 0, nsplit = 0;
 };
 
@@ -98,6 +100,11 @@ WorkspaceLayout layout_for(const muse_attn_layer* l, int32_t n_seq, int32_t n_ne
     if (!decode) {
         w.qhat = 0;
         off = round_up((size_t)n_seq * n_new * kHeads * kHeadDim * es, kAlign);
+        if (l->dtype == MUSE_BF16) {
+            w.kq = off;
+            w.kq_capacity = (int64_t)max_seq_len + n_new;
+            off += round_up((size_t)n_seq * (size_t)w.kq_capacity * kKvHeads * kHeadDim * 2, kAlign);
+        }
     } else {
         w.arrivals = 0;
         off = round_up((size_t)n_seq * kKvHeads * sizeof(unsigned long long), kAlign);
@@ -233,6 +240,17 @@ muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, cons
     pa.eps = layer->rms_eps;
     pa.q_gain = layer->q_norm_gain;
     pa.k_gain = layer->k_norm_gain;
+    pa.q_scale = scale_log2;
+    pa.window = rope ? layer->window : 0;
+    if (layer->dtype == MUSE_BF16) {
+        // prefix rows the chunk can see: [0, L) on full layers, at most
+        // window - 1 rows below L on sliding layers
+        int64_t prefix = max_seq_len;
+        if (rope && (int64_t)layer->window - 1 < prefix) prefix = (int64_t)layer->window - 1;
+        pa.kq = ws + wl.kq;
+        pa.kq_capacity = wl.kq_capacity;
+        pa.conv_blocks = (int32_t)((prefix + 63) / 64);
+    }
     if (rope) rope_table(layer->rope_theta, pa.theta);
 
     AttnArgs aa;
@@ -240,7 +258,8 @@ muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, cons
     aa.qhat = pa.qhat;
     aa.gate = gate;
     aa.out = out;
-    aa.cache_k = cache->k;
+    aa.kq = layer->dtype == MUSE_BF16 ? (const void*)(ws + wl.kq) : cache->k;
+    aa.kq_capacity = layer->dtype == MUSE_BF16 ? wl.kq_capacity : cache->capacity;
     aa.cache_v = cache->v;
     aa.capacity = cache->capacity;
     aa.seq_len = seq_len;
@@ -248,7 +267,6 @@ muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, cons
     aa.n_seq = n_seq;
     aa.n_new = n_new;
     aa.window = rope ? layer->window : 0;
-    aa.scale_log2 = scale_log2;
 
     if (muse::launch_prep(pa, dt, stream) != hipSuccess) return MUSE_ERR_HIP;
     if (timer && hipEventRecord(timer->start, stream) != hipSuccess) return MUSE_ERR_HIP;

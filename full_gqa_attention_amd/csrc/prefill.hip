@@ -1,7 +1,7 @@
 // prefill.hip -- kernel (b): causal / sliding-window GQA attention over the
 // KV cache for a chunk of new tokens, with the sigmoid gate fused into the
 // epilogue.  Flash-style: the score matrix is never stored; softmax is online
-// in the log2 domain (scores pre-multiplied by attn_scale * log2 e).
+// in the log2 domain (Q-hat arrives pre-multiplied by attn_scale * log2 e).
 //
 // Math (pages cited by title and section):
 //   key j is visible to the query at position p iff j <= p and, on sliding
@@ -11,19 +11,25 @@
 //   (Ch 9, 9.8).
 //
 // Shape of the work: one workgroup = 128 query rows of one head (4 waves x
-// 32 rows).  KV tiles of 64 keys are staged in LDS and shared by the 4 waves.
+// 32 rows).  KV tiles of 64 keys are double-buffered in LDS: while the waves
+// compute on one buffer, the next tile's loads are in flight in registers,
+// and land in the other buffer after the compute (one barrier per tile).
 // Each wave computes S^T = K Q^T on 32x32 MFMA tiles (fp16 32x32x16 on bf16
-// layers, with K converted to fp16 as it is staged; f32 32x32x2 on f32
-// layers), so a lane holds one query's scores: the row max
-// and sum need one exchange with lane l ^ 32 only.  P.V is computed as O^T =
-// V^T P^T, reusing the score registers directly as the B operand (the key
-// order inside a K-step is permuted identically in P and V).
+// layers, reading the fp16 key copy the prep kernel made; f32 32x32x2 on f32
+// layers), so a lane holds one query's scores: the row max and sum need one
+// exchange with lane l ^ 32 only.  P.V is computed as O^T = V^T P^T: the
+// score registers are the B operand as they are (the key order inside a
+// K-step is permuted identically in P and V), and the V^T A operand comes
+// from the transposing LDS load (ds_read_b64_tr_b16), two per MFMA.
 // Window-aware tile skipping: only tiles intersecting [p_lo - W + 1, p_hi]
-// are visited; masks are applied only on tiles that straddle a boundary.
+// are visited; masks are applied only on tiles that straddle a boundary; the
+// O rescale is skipped when no running maximum of the wave changed.
 // Workgroups are numbered so that the 16 heads sharing one KV head and one
 // query block land on the same XCD (round-robin dispatch over 8 XCDs), so
 // their K/V tiles are served by that XCD's L2; heavy (late) query blocks are
 // dispatched first.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -35,22 +41,38 @@ int prefill_grid(int n_seq, int n_new) {
     return ((units + 7) / 8) * 8 * kHeadsPerKv;
 }
 
+template <typename T> struct PrefillTraits;
+template <> struct PrefillTraits<bf16_t> {
+    static constexpr int LDK = kHeadDim + 8;           // 272-byte K rows: b128 reads conflict-free
+    static constexpr int LDV = kHeadDim + 32;          // 320-byte V rows: transposing reads conflict-free
+    static constexpr int WAVES = 2;
+};
+template <> struct PrefillTraits<float> {
+    static constexpr int LDK = kHeadDim + 4;
+    static constexpr int LDV = kHeadDim + 4;
+    static constexpr int WAVES = 1;
+};
+
 template <typename T>
-__global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PrefillTraits<T>::WAVES)))
+void prefill_kernel(AttnArgs a) {
     typedef typename ScoreType<T>::type TQ;         // Q.K^T operand type
+    constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
     using MQ = Mma32<TQ>;
     using MP = Mma32<T>;                               // P.V in the storage type
     using FragQ = typename MQ::Frag;
     using FragP = typename MP::Frag;
     constexpr int KPLQ = MQ::KPL, KPLP = MP::KPL;
     constexpr int BM = kPrefillBM, BN = kPrefillBN, D = kHeadDim;
-    constexpr int LDK = D + 16 / (int)sizeof(TQ);     // padded LDS rows (elements)
-    constexpr int LDV = D + 16 / (int)sizeof(T);
+    constexpr int LDK = PrefillTraits<T>::LDK, LDV = PrefillTraits<T>::LDV;
     constexpr int NST = D / (2 * KPLQ);                // K-steps of Q.K
     constexpr int NSTP = BN / (2 * KPLP);              // K-steps of P.V
+    constexpr int ES = (int)sizeof(T);
     static_assert(sizeof(TQ) == sizeof(T), "K staging keeps the row size");
-    __shared__ __attribute__((aligned(16))) TQ Ks[BN * LDK];
-    __shared__ __attribute__((aligned(16))) T Vs[BN * LDV];
+    constexpr int CPR = D * ES / 16;                   // 16-byte chunks per row
+    constexpr int NCH = BN * CPR / 256;                // chunks per thread per tile
+    __shared__ __attribute__((aligned(16))) TQ Ks[2][BN * LDK];
+    __shared__ __attribute__((aligned(16))) T Vs[2][BN * LDV];
 
     // ---- work item: 16 heads of one (q-block, seq, kv head) per XCD
     const int nqb = (a.n_new + BM - 1) / BM;
@@ -81,12 +103,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
         return;
     }
 
+    // positions fit in int32 (the host bounds them by 2^24)
     const int tq = q0 + wave * 32 + l32;               // this lane's query (new-token index)
-    const int64_t pq = (int64_t)L + tq;                // its position
+    const int pq = L + tq;                             // its position
     const int tw0 = q0 + wave * 32;
     const int tw1 = min(tw0 + 31, N - 1);
     const bool wave_live = tw0 < N;
-    const int64_t pw0 = (int64_t)L + tw0, pw1 = (int64_t)L + tw1;
+    const int pw0 = L + tw0, pw1 = L + tw1;
     const int W = a.window;
 
     // ---- Q-hat fragments (B operand of S^T = K Q^T), held for the whole loop
@@ -104,111 +127,164 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
 
     // ---- keys this block can see
     const int tb1 = min(q0 + BM - 1, N - 1);
-    const int64_t P0 = (int64_t)L + q0, P1 = (int64_t)L + tb1;
-    int64_t kv_lo = 0;
-    if (W > 0) kv_lo = max((int64_t)0, P0 - W + 1);
-    const int64_t kv_hi = P1;
-    const int64_t kv_end = (int64_t)L + N;             // rows present in the cache
-    const int64_t tile_lo = kv_lo / BN, tile_hi = kv_hi / BN;
+    const int P0 = L + q0, P1 = L + tb1;
+    const int kv_lo = (W > 0) ? max(0, P0 - W + 1) : 0;
+    const int kv_end = L + N;                          // rows present in the cache
+    const int tile_lo = kv_lo / BN, tile_hi = P1 / BN;
+    const int ntiles = tile_hi - tile_lo + 1;
 
-    const char* gk = (const char*)a.cache_k;
-    const char* gv = (const char*)a.cache_v;
-    constexpr int CPR = D * (int)sizeof(T) / 16;       // 16-byte chunks per row
-    constexpr int NCH = BN * CPR;
+    const char* gk = (const char*)a.kq + (((int64_t)s * a.kq_capacity) * kKvHeads + g) * D * ES;
+    const char* gv = (const char*)a.cache_v + (((int64_t)s * a.capacity) * kKvHeads + g) * D * ES;
+    constexpr int64_t ROW = (int64_t)kKvHeads * D * ES;   // bytes per position
+    u32x4 kreg[NCH], vreg[NCH];
+    auto load_tile = [&](int tile) __attribute__((always_inline)) {
+        const int j0 = tile * BN;
+#pragma unroll
+        for (int u = 0; u < NCH; ++u) {
+            const int c = tid + 256 * u;
+            const int r = c / CPR, cc = c % CPR;
+            const int jj = j0 + r;
+            kreg[u] = u32x4{0, 0, 0, 0};
+            vreg[u] = u32x4{0, 0, 0, 0};
+            if (jj >= kv_lo && jj < kv_end) {
+                kreg[u] = *(const u32x4*)(gk + jj * ROW + cc * 16);
+                vreg[u] = *(const u32x4*)(gv + jj * ROW + cc * 16);
+            }
+        }
+    };
+    auto store_tile = [&](int bufi) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < NCH; ++u) {
+            const int c = tid + 256 * u;
+            const int r = c / CPR, cc = c % CPR;
+            *(u32x4*)((char*)Ks[bufi] + r * LDK * ES + cc * 16) = kreg[u];
+            *(u32x4*)((char*)Vs[bufi] + r * LDV * ES + cc * 16) = vreg[u];
+        }
+    };
 
     floatx16 o[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt] = floatx16{};
     float m_run = kNegInf, l_run = 0.0f;
 
-    for (int64_t tile = tile_lo; tile <= tile_hi; ++tile) {
-        const int64_t j0 = tile * BN;
-        __syncthreads();
-        for (int c = tid; c < NCH; c += 256) {
-            const int r = c / CPR, cc = c % CPR;
-            const int64_t jj = j0 + r;
-            uint4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
-            if (jj >= kv_lo && jj < kv_end) {
-                const int64_t off = ((((int64_t)s * a.capacity + jj) * kKvHeads + g) * D) * (int64_t)sizeof(T) + cc * 16;
-                kx = *(const uint4*)(gk + off);
-                vx = *(const uint4*)(gv + off);
-            }
-            *(uint4*)((char*)Ks + (r * LDK) * (int)sizeof(TQ) + cc * 16) = k_chunk_to_score(kx, T{});
-            *(uint4*)((char*)Vs + (r * LDV) * (int)sizeof(T) + cc * 16) = vx;
-        }
-        __syncthreads();
-        if (!wave_live) continue;
-        const bool any = (j0 <= pw1) && (W == 0 || pw0 - (j0 + BN - 1) < W);
-        if (!any) continue;
-        const bool need_mask = (j0 + BN - 1 > pw0) || (W > 0 && pw1 - j0 >= W);
+    load_tile(tile_lo);
+    store_tile(0);
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+        const int cur = it & 1;
+        const int j0 = (tile_lo + it) * BN;
+        if (it + 1 < ntiles) load_tile(tile_lo + it + 1);   // in flight during the compute
+        const bool any = wave_live && (j0 <= pw1) && (W == 0 || pw0 - (j0 + BN - 1) < W);
+        if (any) {
+            const bool need_mask = (j0 + BN - 1 > pw0) || (W > 0 && pw1 - j0 >= W);
+            const TQ* Kc = Ks[cur];
+            const T* Vc = Vs[cur];
 
-        // S^T tiles: keys 32kt..32kt+31 x this wave's 32 queries
-        floatx16 sacc[2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            sacc[kt] = floatx16{};
+            // S^T tiles: keys 32kt..32kt+31 x this wave's 32 queries (log2 domain)
+            floatx16 sacc[2] = {floatx16{}, floatx16{}};
 #pragma unroll
             for (int st = 0; st < NST; ++st) {
-                const FragQ kf = *(const FragQ*)(Ks + (32 * kt + l32) * LDK + 2 * KPLQ * st + KPLQ * gl);
-                sacc[kt] = MQ::mma(kf, qf[st], sacc[kt]);
-            }
-        }
-
-        // online softmax for query l32 (its other 32 keys sit in lane l ^ 32)
-        float mx = kNegInf;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float x = sacc[kt][i] * a.scale_log2;
-                if (need_mask) {
-                    const int64_t jj = j0 + 32 * kt + 8 * (i / 4) + 4 * gl + (i % 4);
-                    if (jj > pq || (W > 0 && pq - jj >= W)) x = kNegInf;
+                for (int kt = 0; kt < 2; ++kt) {
+                    const FragQ kf = *(const FragQ*)(Kc + (32 * kt + l32) * LDK + 2 * KPLQ * st + KPLQ * gl);
+                    sacc[kt] = MQ::mma(kf, qf[st], sacc[kt]);
                 }
-                sacc[kt][i] = x;
-                mx = fmaxf(mx, x);
             }
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        float rs = 0.0f;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float pv = fast_exp2(sacc[kt][i] - m_use);
-                sacc[kt][i] = pv;
-                rs += pv;
-            }
-        }
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
 
-        // O^T += V^T P^T over the 64 keys of the tile
+            // online softmax for query l32 (its other 32 keys sit in lane l ^ 32).
+            // Scores are relative to a per-row reference m_run; the reference
+            // moves only when a row's maximum exceeds it by more than 2^8 (so
+            // P <= 256) -- the common tile takes exp2 of the scores as they are.
+            if (need_mask) {
+                const unsigned wlim = W > 0 ? (unsigned)W : 0x7fffffffu;
 #pragma unroll
-        for (int st = 0; st < NSTP; ++st) {
-            FragP pf;
+                for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-            for (int t = 0; t < KPLP; ++t) {
-                const int I = st * KPLP + t;
-                frag_set(pf, t, sacc[I / 16][I % 16]);
+                    for (int i = 0; i < 16; ++i) {
+                        const int jj = j0 + 32 * kt + 8 * (i / 4) + 4 * gl + (i % 4);
+                        sacc[kt][i] = ((unsigned)(pq - jj) < wlim) ? sacc[kt][i] : kNegInf;
+                    }
+                }
             }
+            float mx = kNegInf;
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                FragP vf;
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            // a row (re)starts its reference at its first visible scores, or when
+            // its max exceeds the reference by more than 8 (log2 units)
+            const bool fresh = (m_run == kNegInf);
+            const bool grow = fresh ? (mx > kNegInf) : (mx - m_run > 8.0f);
+            if (__ballot(grow) != 0) {
+                const float m_new = grow ? mx : m_run;
+                const float alpha = fresh ? 1.0f : fast_exp2(m_run - m_new);   // 1 unless grown
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+                m_run = m_new;
+            }
+            const float ref = (m_run == kNegInf) ? 0.0f : m_run;   // rows with nothing visible stay -inf
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sacc[kt][i] -= ref;
+            float rs = 0.0f;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float pv = fast_exp2(sacc[kt][i]);
+                    sacc[kt][i] = pv;
+                    rs += pv;
+                }
+            }
+            l_run += rs;
+
+            // O^T += V^T P^T over the 64 keys of the tile
+#pragma unroll
+            for (int st = 0; st < NSTP; ++st) {
+                FragP pf;
 #pragma unroll
                 for (int t = 0; t < KPLP; ++t) {
                     const int I = st * KPLP + t;
-                    const int key = 32 * (I / 16) + 8 * ((I % 16) / 4) + 4 * gl + (I % 4);
-                    frag_set_raw(vf, t, Vs[key * LDV + 32 * dt + l32]);
+                    frag_set(pf, t, sacc[I / 16][I % 16]);
                 }
-                o[dt] = MP::mma(vf, pf, o[dt]);
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    FragP vf;
+                    if constexpr (kBf16) {
+                        // item t of lane group gl is key kb + 8*(t/4) + t%4 with
+                        // kb = 32(st/2) + 16(st%2) + 4gl; each run of 4 keys is one
+                        // transposing read: source lane i of a 16-lane group points at
+                        // row kb + 8r + i/4, columns 32dt + 16*(group%2) + 4*(i%4)..+3
+                        typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+                        const int kb = 32 * (st / 2) + 16 * (st % 2) + 4 * gl;
+                        const int i16 = lane & 15;
+                        const int col = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+                        const T* src0 = Vc + (kb + (i16 >> 2)) * LDV + col;
+                        const T* src1 = src0 + 8 * LDV;
+                        const shortx4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_shortx4*)(__attribute__((address_space(3))) void*)src0);
+                        const shortx4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_shortx4*)(__attribute__((address_space(3))) void*)src1);
+                        typedef short shortx8 __attribute__((ext_vector_type(8)));
+                        const shortx8 both = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        vf = __builtin_bit_cast(FragP, both);
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < KPLP; ++t) {
+                            const int I = st * KPLP + t;
+                            const int key = 32 * (I / 16) + 8 * ((I % 16) / 4) + 4 * gl + (I % 4);
+                            frag_set_raw(vf, t, Vc[key * LDV + 32 * dt + l32]);
+                        }
+                    }
+                    o[dt] = MP::mma(vf, pf, o[dt]);
+                }
             }
         }
+        if (it + 1 < ntiles) store_tile(cur ^ 1);
+        __syncthreads();
     }
 
     // ---- epilogue: normalise, gate, store (lane: 4 consecutive dims per item group)

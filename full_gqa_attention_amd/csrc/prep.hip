@@ -1,9 +1,13 @@
-// prep.hip -- kernel (a): per-head QK-norm, RoPE on sliding layers, KV append.
+// prep.hip -- kernel (a): per-head QK-norm, RoPE on sliding layers, KV append
+// for a chunk of new tokens (the prefill path; decode does this inside its
+// own kernel).
 //
-// One workgroup (4 wave64s) per new token.  A head vector of 128 values is
-// one wave: lane i holds the adjacent pair (x[2i], x[2i+1]), which is exactly
-// RoPE pair i, so the rotation needs no data exchange and each lane computes
-// its sin/cos once for all 34 vectors of the token.
+// One workgroup (256 threads) per new token.  A head vector of 128 values is
+// handled by 16 lanes, 8 values (16 bytes, RoPE pairs 4i..4i+3) per lane, so
+// one wave covers four vectors and the 36 vectors of a token (32 Q heads, 2 K
+// heads, 2 V heads) take three passes of the workgroup.  The 64 sin/cos
+// pairs of the token's position are computed once, by the first 64 threads,
+// and shared through LDS.
 //   * QK-norm: RMS over the 128 values of one head, then the constant gain
 //     ("Chapter 9 - The Muse Glimmer architecture" 9.5 RMSNorm formula;
 //     "Chapter 14 - QK-norm and RoPE" 14.3: Q gain about 3.87, K gain 1).
@@ -12,95 +16,155 @@
 //     (Ch 14, 14.4.1 table, 14.4.2 rotation, 14.5 kernel).
 //   * Append: the rotated K goes to cache row p, V is copied unchanged
 //     (Ch 14, 14.7: keys rotate before the store; V never rotates).
-// Q-hat goes to the workspace in the score type of the attention kernels
-// (fp16 on bf16 layers, f32 on f32 layers).
+// Q-hat goes to the workspace in the score type of the attention kernel
+// (fp16 on bf16 layers, f32 on f32 layers), pre-multiplied by
+// attn_scale * log2(e) so that the attention kernel's scores are already in
+// the log2 domain of its softmax.  On bf16 layers the attention kernel reads
+// keys from an fp16 copy (converted once here rather than per tile): the new
+// rows are written to it as they are appended, and extra workgroups convert
+// the cached prefix rows the chunk can see.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace muse {
 
 template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&x)[8]) {
+    if constexpr (sizeof(T) == 2) {
+        const bf16x8 v = *(const bf16x8*)p;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
+    } else {
+        const floatx4 a = *(const floatx4*)p, b = *(const floatx4*)(p + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = a[i];
+            x[4 + i] = b[i];
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float (&y)[8]) {
+    if constexpr (sizeof(T) == 2) {
+        typedef T T8 __attribute__((ext_vector_type(8)));
+        T8 v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = from_f32<T>(y[i]);
+        *(T8*)p = v;
+    } else {
+        floatx4 a, b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a[i] = y[i];
+            b[i] = y[4 + i];
+        }
+        *(floatx4*)p = a;
+        *(floatx4*)(p + 4) = b;
+    }
+}
+
+// Rows [lo, L) of sequence s that the chunk's queries can see, 64 rows per
+// workgroup: bf16 cache -> fp16 score copy (exact for the normed keys).
+__device__ __forceinline__ void convert_prefix(const PrepArgs& a, int idx) {
+    const int s = idx / a.conv_blocks, blk = idx % a.conv_blocks;
+    const int L = a.seq_len[s];
+    if (L < 0 || L > a.max_seq_len) return;
+    const int lo = a.window > 0 ? max(0, L - a.window + 1) : 0;
+    const int r0 = lo + 64 * blk;
+    for (int c = threadIdx.x; c < 64 * 32; c += 256) {   // 32 chunks of 16 B per position
+        const int row = r0 + c / 32, piece = c % 32;
+        if (row >= L) break;
+        const int64_t e = ((int64_t)s * a.capacity + row) * kKvHeads * kHeadDim + piece * 8;
+        const int64_t f = ((int64_t)s * a.kq_capacity + row) * kKvHeads * kHeadDim + piece * 8;
+        *(u32x4*)((f16_t*)a.kq + f) = k_chunk_to_score(*(const u32x4*)((const bf16_t*)a.cache_k + e), bf16_t{});
+    }
+}
+
+template <typename T>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
+    typedef typename ScoreType<T>::type TQ;
+    __shared__ float2 rot[64];                     // (cos, sin) of pair i at this token's position
+    const int n_tok = a.n_seq * a.n_new;
+    if ((int)blockIdx.x >= n_tok) {                // fp16 copy of visible prefix keys
+        if constexpr (sizeof(T) == 2) convert_prefix(a, (int)blockIdx.x - n_tok);
+        return;
+    }
     const int tok = blockIdx.x;                    // s * n_new + t
     const int s = tok / a.n_new;
     const int t = tok - s * a.n_new;
     const int L = a.seq_len[s];
     // Fail closed on a device-side length the host could not check: the
-    // attention kernels refuse the same sequence and fill its output with NaN.
+    // attention kernel refuses the same sequence and fills its output with NaN.
     if (L < 0 || L > a.max_seq_len) return;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
     const int64_t p = (int64_t)L + t;
-
-    float sn = 0.0f, cs = 1.0f;
-    if (a.rope) {
-        float th = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 64; ++i) th = (lane == i) ? a.theta[i] : th;
-        const float ang = (float)p * th;           // f32 product, as in the table's use
-        sincosf(ang, &sn, &cs);
+    const int tid = threadIdx.x;
+    if (a.rope && tid < 64) {
+        float sn, cs;
+        rope_sincos(a.theta, tid, p, sn, cs);
+        rot[tid] = make_float2(cs, sn);
     }
+    __syncthreads();
 
-    const T* q = (const T*)a.q;
-    const T* k = (const T*)a.k;
-    const T* v = (const T*)a.v;
-    typedef typename ScoreType<T>::type TQ;
-    TQ* qhat = (TQ*)a.qhat;
-    T* ck = (T*)a.cache_k;
-    T* cv = (T*)a.cache_v;
-
-    for (int vec = wave; vec < kHeads + 2 * kKvHeads; vec += 4) {
-        const T* src;
-        T* dst = nullptr;
-        TQ* qdst = nullptr;
-        float gain = 1.0f;
-        bool norm = true;
-        if (vec < kHeads) {
-            const int64_t off = ((int64_t)tok * kHeads + vec) * kHeadDim;
-            src = q + off;
-            qdst = qhat + off;
-            gain = a.q_gain;
-        } else if (vec < kHeads + kKvHeads) {
-            const int g = vec - kHeads;
-            src = k + ((int64_t)tok * kKvHeads + g) * kHeadDim;
-            dst = ck + (((int64_t)s * a.capacity + p) * kKvHeads + g) * kHeadDim;
-            gain = a.k_gain;
-        } else {
+    const int sub = tid & 15;                      // 8 values: dims 8*sub .. 8*sub+7
+    for (int vec = tid >> 4; vec < kHeads + 2 * kKvHeads; vec += 16) {
+        float x[8];
+        if (vec >= kHeads + kKvHeads) {            // V: exact copy
             const int g = vec - kHeads - kKvHeads;
-            src = v + ((int64_t)tok * kKvHeads + g) * kHeadDim;
-            dst = cv + (((int64_t)s * a.capacity + p) * kKvHeads + g) * kHeadDim;
-            norm = false;
-        }
-        const T r0 = src[2 * lane];
-        const T r1 = src[2 * lane + 1];
-        if (!norm) {                               // V: exact copy
-            dst[2 * lane] = r0;
-            dst[2 * lane + 1] = r1;
+            const T* src = (const T*)a.v + ((int64_t)tok * kKvHeads + g) * kHeadDim + 8 * sub;
+            T* dst = (T*)a.cache_v + (((int64_t)s * a.capacity + p) * kKvHeads + g) * kHeadDim + 8 * sub;
+            *(u32x4*)dst = *(const u32x4*)src;
+            if constexpr (sizeof(T) == 4) *(u32x4*)(dst + 4) = *(const u32x4*)(src + 4);
             continue;
         }
-        const float x0 = to_f32(r0), x1 = to_f32(r1);
-        const float ss = wave_sum(x0 * x0 + x1 * x1);
+        const bool is_q = vec < kHeads;
+        const T* src = is_q ? (const T*)a.q + ((int64_t)tok * kHeads + vec) * kHeadDim
+                            : (const T*)a.k + ((int64_t)tok * kKvHeads + (vec - kHeads)) * kHeadDim;
+        load8(src + 8 * sub, x);
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);   // the 16 lanes of this head
         const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
-        float y0 = (x0 * r) * gain;
-        float y1 = (x1 * r) * gain;
+        const float gain = is_q ? a.q_gain : a.k_gain;
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = (x[i] * r) * gain;
         if (a.rope) {
-            const float z0 = y0 * cs - y1 * sn;
-            const float z1 = y0 * sn + y1 * cs;
-            y0 = z0;
-            y1 = z1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float2 cs = rot[4 * sub + j];
+                const float y0 = y[2 * j], y1 = y[2 * j + 1];
+                y[2 * j] = y0 * cs.x - y1 * cs.y;
+                y[2 * j + 1] = y0 * cs.y + y1 * cs.x;
+            }
         }
-        if (qdst) {
-            qdst[2 * lane] = from_f32<TQ>(y0);
-            qdst[2 * lane + 1] = from_f32<TQ>(y1);
+        if (is_q) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) y[i] *= a.q_scale;
+            store8((TQ*)a.qhat + ((int64_t)tok * kHeads + vec) * kHeadDim + 8 * sub, y);
         } else {
-            dst[2 * lane] = from_f32<T>(y0);
-            dst[2 * lane + 1] = from_f32<T>(y1);
+            const int g = vec - kHeads;
+            T* dst = (T*)a.cache_k + (((int64_t)s * a.capacity + p) * kKvHeads + g) * kHeadDim + 8 * sub;
+            if constexpr (sizeof(T) == 2) {
+                bf16x8 kv;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) kv[i] = from_f32<bf16_t>(y[i]);
+                const u32x4 raw = __builtin_bit_cast(u32x4, kv);
+                *(u32x4*)dst = raw;
+                // the score copy holds the stored values
+                TQ* kq = (TQ*)a.kq + (((int64_t)s * a.kq_capacity + p) * kKvHeads + g) * kHeadDim + 8 * sub;
+                *(u32x4*)kq = k_chunk_to_score(raw, T{});
+            } else {
+                store8(dst, y);
+            }
         }
     }
 }
 
 hipError_t launch_prep(const PrepArgs& a, int dtype, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.n_seq * a.n_new)), block(256);
+    const dim3 grid((unsigned)(a.n_seq * a.n_new + a.n_seq * a.conv_blocks)), block(256);
     if (dtype == 1)
         hipLaunchKernelGGL(prep_kernel<bf16_t>, grid, block, 0, stream, a);
     else
