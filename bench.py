@@ -47,6 +47,100 @@ def prefill_pairs(spec, L: int, N: int) -> int:
     return sum(visible_rows(spec, L + t) for t in range(N))
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+COUNTERS_FILE = os.path.join(PROFILES, "decode_64x8192_bf16_hbm_counters.md")
+DECODE_SOURCES = ["full_gqa_attention_amd/csrc/decode.hip", "full_gqa_attention_amd/csrc/device_common.h",
+                  "full_gqa_attention_amd/csrc/kernels.h", "full_gqa_attention_amd/csrc/muse_attn.cpp"]
+# A plain 1 GiB device copy read back 524,315 KiB on FETCH_SIZE and 1,048,576 KiB
+# on WRITE_SIZE: the factors that turn the counters into bytes.
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+
+
+def sources_hash(paths) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per decode-kernel launch from the committed counter summary,
+    or None when the decode kernel's sources changed since it was taken."""
+    try:
+        kv = {}
+        with open(COUNTERS_FILE) as f:
+            for line in f:
+                if line.startswith("    ") and ":" in line:
+                    k, v = line.strip().split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("decode_sources_sha256_16") != sources_hash(DECODE_SOURCES):
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def summarize_trace(stats_csv: str, out: str, command: str):
+    """Write a kernel-trace summary (text) from rocprofv3's kernel_stats.csv."""
+    import csv
+    rows = [r for r in csv.DictReader(open(stats_csv)) if "muse" in r["Name"]]
+    lines = ["# Kernel trace summary", "", "Command (from /tmp, repository at $ROOT):", "", "```",
+             command, "```", "", "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    import re
+    for r in rows:
+        name = r["Name"]
+        m = re.match(r"_ZN4muse(\d+)", name)
+        if m:
+            n = int(m.group(1))
+            kname = name[m.end():m.end() + n]
+            dt = "bf16" if "DF16b" in name[m.end() + n:] else "f32"
+            name = f"muse::{kname}<{dt}>"
+        lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, out: str, command: str):
+    """Write the decode kernel's HBM-traffic summary from two --pmc runs."""
+    import csv
+
+    def per_kernel(path):
+        copy, dec = [], []
+        for r in csv.DictReader(open(path)):
+            v = float(r["Counter_Value"])
+            if "decode_kernel" in r["Kernel_Name"]:
+                dec.append(v)
+            elif "copyBuffer" in r["Kernel_Name"]:
+                copy.append(v)
+        return copy, dec
+
+    fc, fd = per_kernel(fetch_csv)
+    wc, wd = per_kernel(write_csv)
+    # launches alternate sliding, full (the benchmark's layer order)
+    f_sl, f_fu = sum(fd[0::2]) / len(fd[0::2]), sum(fd[1::2]) / len(fd[1::2])
+    w_sl, w_fu = sum(wd[0::2]) / len(wd[0::2]), sum(wd[1::2]) / len(wd[1::2])
+    fetch_b = [x * 1024 * FETCH_SCALE for x in (f_sl, f_fu)]
+    write_b = [x * 1024 * WRITE_SCALE for x in (w_sl, w_fu)]
+    per_launch = (sum(fetch_b) + sum(write_b)) / 2
+    lines = ["# HBM traffic of the decode kernel: 64 x 8,192 bf16 decode step", "",
+             "Two counter runs (from /tmp, repository at $ROOT):", "", "```", command, "```", "",
+             f"Calibration: the first copy in each run is a 1 GiB device copy (`--calibrate-copy`); it read "
+             f"{fc[0]:.1f} KiB on FETCH_SIZE and {wc[0]:.1f} KiB on WRITE_SIZE, so FETCH_SIZE is scaled by "
+             f"{FETCH_SCALE} and WRITE_SIZE by {WRITE_SCALE}.", "",
+             "| launch | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB | algorithmic KV MB |",
+             "|---|---|---|---|---|---|",
+             f"| sliding (W 2048) | {f_sl:.1f} | {w_sl:.1f} | {fetch_b[0] / 1e6:.1f} | {write_b[0] / 1e6:.2f} | 134.2 |",
+             f"| full | {f_fu:.1f} | {w_fu:.1f} | {fetch_b[1] / 1e6:.1f} | {write_b[1] / 1e6:.2f} | 536.9 |",
+             "", "Values read by bench.py (traffic is reported only while these sources are unchanged):", "",
+             f"    decode_sources_sha256_16: {sources_hash(DECODE_SOURCES)}",
+             f"    hbm_bytes_per_launch: {per_launch:.0f}", ""]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -59,6 +153,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device copy first (scale for HBM byte counters)")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT", "COMMAND"),
+                    help="write a kernel-trace summary from rocprofv3 kernel_stats.csv and exit")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT", "COMMAND"),
+                    help="write the decode kernel's HBM-traffic summary from two --pmc runs and exit")
     return ap.parse_args()
 
 
@@ -134,7 +232,8 @@ def bench_decode(w, args, fa, synth, torch):
         "value": kv_per_step / (ms_per_step * 1e-3) / 1e9,
         "ms_per_step": ms_per_step,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": counter_traffic() if w.name == "decode_64x8192_bf16" else None,
                      "kernel": "muse::decode_kernel<bf16>" if w.dtype == 1 else "muse::decode_kernel<f32>",
                      "launches": launches, "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": int(bytes_per_launch),
@@ -213,6 +312,12 @@ def cpu_baseline_decode(w, runs, synth, torch):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
               "multi-GPU path to measure.", file=sys.stderr)

@@ -133,32 +133,43 @@ void prefill_kernel(AttnArgs a) {
     const int tile_lo = kv_lo / BN, tile_hi = P1 / BN;
     const int ntiles = tile_hi - tile_lo + 1;
 
-    const char* gk = (const char*)a.kq + (((int64_t)s * a.kq_capacity) * kKvHeads + g) * D * ES;
-    const char* gv = (const char*)a.cache_v + (((int64_t)s * a.capacity) * kKvHeads + g) * D * ES;
     constexpr int64_t ROW = (int64_t)kKvHeads * D * ES;   // bytes per position
+    constexpr int RSTEP = 256 / CPR;                       // tile rows per chunk step
+    // this thread's chunk: row tid / CPR (+ RSTEP * u), 16-byte column tid % CPR
+    const int r_t = tid / CPR, c_t = tid % CPR;
+    const char* kbase = (const char*)a.kq + (((int64_t)s * a.kq_capacity) * kKvHeads + g) * D * ES +
+                        r_t * ROW + c_t * 16;
+    const char* vbase = (const char*)a.cache_v + (((int64_t)s * a.capacity) * kKvHeads + g) * D * ES +
+                        r_t * ROW + c_t * 16;
     u32x4 kreg[NCH], vreg[NCH];
     auto load_tile = [&](int tile) __attribute__((always_inline)) {
         const int j0 = tile * BN;
+        const char* kp = kbase + (int64_t)j0 * ROW;
+        const char* vp = vbase + (int64_t)j0 * ROW;
+        if (j0 >= kv_lo && j0 + BN <= kv_end) {           // interior tile: every row present
 #pragma unroll
-        for (int u = 0; u < NCH; ++u) {
-            const int c = tid + 256 * u;
-            const int r = c / CPR, cc = c % CPR;
-            const int jj = j0 + r;
-            kreg[u] = u32x4{0, 0, 0, 0};
-            vreg[u] = u32x4{0, 0, 0, 0};
-            if (jj >= kv_lo && jj < kv_end) {
-                kreg[u] = *(const u32x4*)(gk + jj * ROW + cc * 16);
-                vreg[u] = *(const u32x4*)(gv + jj * ROW + cc * 16);
+            for (int u = 0; u < NCH; ++u) {
+                kreg[u] = *(const u32x4*)(kp + u * RSTEP * ROW);
+                vreg[u] = *(const u32x4*)(vp + u * RSTEP * ROW);
+            }
+        } else {
+            asm volatile("");                              // keep this a branch
+#pragma unroll
+            for (int u = 0; u < NCH; ++u) {
+                const int jj = j0 + r_t + u * RSTEP;
+                const bool in = jj >= kv_lo && jj < kv_end;
+                kreg[u] = in ? *(const u32x4*)(kp + u * RSTEP * ROW) : u32x4{0, 0, 0, 0};
+                vreg[u] = in ? *(const u32x4*)(vp + u * RSTEP * ROW) : u32x4{0, 0, 0, 0};
             }
         }
     };
     auto store_tile = [&](int bufi) __attribute__((always_inline)) {
+        char* kd = (char*)Ks[bufi] + r_t * LDK * ES + c_t * 16;
+        char* vd = (char*)Vs[bufi] + r_t * LDV * ES + c_t * 16;
 #pragma unroll
         for (int u = 0; u < NCH; ++u) {
-            const int c = tid + 256 * u;
-            const int r = c / CPR, cc = c % CPR;
-            *(u32x4*)((char*)Ks[bufi] + r * LDK * ES + cc * 16) = kreg[u];
-            *(u32x4*)((char*)Vs[bufi] + r * LDV * ES + cc * 16) = vreg[u];
+            *(u32x4*)(kd + u * RSTEP * LDK * ES) = kreg[u];
+            *(u32x4*)(vd + u * RSTEP * LDV * ES) = vreg[u];
         }
     };
 
@@ -196,6 +207,7 @@ void prefill_kernel(AttnArgs a) {
             // moves only when a row's maximum exceeds it by more than 2^8 (so
             // P <= 256) -- the common tile takes exp2 of the scores as they are.
             if (need_mask) {
+                asm volatile("");                          // keep this a branch
                 const unsigned wlim = W > 0 ? (unsigned)W : 0x7fffffffu;
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {
@@ -217,6 +229,7 @@ void prefill_kernel(AttnArgs a) {
             const bool fresh = (m_run == kNegInf);
             const bool grow = fresh ? (mx > kNegInf) : (mx - m_run > 8.0f);
             if (__ballot(grow) != 0) {
+                asm volatile("");                          // keep this a branch
                 const float m_new = grow ? mx : m_run;
                 const float alpha = fresh ? 1.0f : fast_exp2(m_run - m_new);   // 1 unless grown
                 l_run *= alpha;
