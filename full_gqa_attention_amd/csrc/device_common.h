@@ -51,6 +51,24 @@ __device__ __forceinline__ u32x4 k_chunk_to_score(u32x4 x, bf16_t) {
 }
 __device__ __forceinline__ u32x4 k_chunk_to_score(u32x4 x, float) { return x; }
 
+// The value of x held by lane l ^ 32, paired with this lane's own: after
+// v_permlane32_swap of x with itself, one of the two results is x of this
+// lane and the other x of lane l ^ 32 (which is which depends on the half),
+// so a symmetric combination of the pair is the same in lanes l and l ^ 32.
+struct HalfPair { float a, b; };
+__device__ __forceinline__ HalfPair halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return HalfPair{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float max_halves(float x) {
+    const HalfPair p = halves(x);
+    return fmaxf(p.a, p.b);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const HalfPair p = halves(x);
+    return p.a + p.b;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);

@@ -33,6 +33,10 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#ifndef MUSE_PREFILL_QG
+#define MUSE_PREFILL_QG 1   // 32-row query groups per wave on bf16 layers
+#endif
+
 namespace muse {
 
 int prefill_grid(int n_seq, int n_new) {
@@ -218,12 +222,14 @@ void prefill_kernel(AttnArgs a) {
                     }
                 }
             }
-            float mx = kNegInf;
+            // four independent max chains (short dependency chains), then the
+            // partner half of the row
+            float m4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                for (int i = 0; i < 16; ++i) m4[i % 4] = fmaxf(m4[i % 4], sacc[kt][i]);
+            const float mx = max_halves(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
             // a row (re)starts its reference at its first visible scores, or when
             // its max exceeds the reference by more than 8 (log2 units)
             const bool fresh = (m_run == kNegInf);
@@ -242,17 +248,17 @@ void prefill_kernel(AttnArgs a) {
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) sacc[kt][i] -= ref;
-            float rs = 0.0f;
+            float r4[4] = {0.0f, 0.0f, 0.0f, 0.0f};          // four partial row sums
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float pv = fast_exp2(sacc[kt][i]);
                     sacc[kt][i] = pv;
-                    rs += pv;
+                    r4[i % 4] += pv;
                 }
             }
-            l_run += rs;
+            l_run += (r4[0] + r4[1]) + (r4[2] + r4[3]);
 
             // O^T += V^T P^T over the 64 keys of the tile
 #pragma unroll
@@ -301,7 +307,7 @@ void prefill_kernel(AttnArgs a) {
     }
 
     // ---- epilogue: normalise, gate, store (lane: 4 consecutive dims per item group)
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = sum_halves(l_run);
     if (!wave_live || tq >= N) return;
     const float inv = 1.0f / l_tot;
     const int64_t base = (((int64_t)s * N + tq) * kHeads + h) * D;
@@ -321,12 +327,363 @@ void prefill_kernel(AttnArgs a) {
     }
 }
 
+// ---- bf16 layers: four heads of one GQA group per workgroup, one head per
+// wave, 64 query rows per wave.  Each K/V fragment read from LDS feeds two
+// MFMAs (query rows 0-31 and 32-63 of the wave), which halves the LDS bytes
+// per flop of the 32-row layout above (with 32 rows per wave the LDS read
+// rate, not the matrix cores, bounds the loop).  A one-wave-per-SIMD launch
+// gives each wave the 512-entry register file: Q (64 rows), a tile's scores
+// and the O accumulators stay in registers.  The four waves share one row
+// range, so tile ranges and masks are uniform across the workgroup.
+//
+// Softmax reference.  Each row's reference is fixed at the maximum of the
+// first 32-key half in which it sees a key, and never moves: later
+// exponentials are exp2(s - ref) with s - ref possibly > 0.  Softmax is
+// invariant to the reference (O and l carry the same factor), the maximum
+// key has P >= 1 so nothing underflows that matters, and the only failure is
+// an overflow to inf in P, l or O -- checked at the end.  Under QK-norm the
+// scores are bounded by |q-hat| |k-hat|, so this does not happen with the
+// model's gains; if it does, the workgroup recomputes its rows with the
+// exact row maxima from a Q.K-only pass (then P <= 1).  A fixed reference
+// removes the running maximum and the O rescale from the tile loop, and lets
+// the Q.K MFMAs start from -ref instead of 0, so no subtraction is left
+// either.  Row sums are taken from the bf16 P values that enter the P.V
+// product (v_dot2 against (1, 1)).
+template <int QG> struct Gqa4Traits {
+    static constexpr int WAVES = QG == 1 ? 2 : 1;      // waves per SIMD the registers allow
+};
+
+int prefill_grid_gqa4(int n_seq, int n_new, int rows_per_wave) {
+    const int nqb = (n_new + rows_per_wave - 1) / rows_per_wave;
+    const int units = n_seq * kKvHeads * nqb;          // (q-block, seq, kv head)
+    return ((units + 7) / 8) * 8 * (kHeadsPerKv / 4);
+}
+
+template <int QG>                                      // 32-row query groups per wave
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Gqa4Traits<QG>::WAVES)))
+void prefill_gqa4_kernel(AttnArgs a) {
+    typedef bf16_t T;
+    typedef f16_t TQ;
+    using MQ = Mma32<TQ>;
+    using MP = Mma32<T>;
+    using FragQ = MQ::Frag;
+    using FragP = MP::Frag;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    constexpr int BMW = 32 * QG, BN = kPrefillBN, D = kHeadDim;
+    constexpr int LDK = D + 8, LDV = D + 32;           // conflict-free b128 / transposing reads
+    constexpr int NST = D / (2 * MQ::KPL);             // K-steps of Q.K (8)
+    constexpr int ES = 2;
+    constexpr int CPR = D * ES / 16;                   // 16-byte chunks per row
+    constexpr int NCH = BN * CPR / 256;                // chunks per thread per tile
+    __shared__ __attribute__((aligned(16))) TQ Ks[2][BN * LDK];
+    __shared__ __attribute__((aligned(16))) T Vs[2][BN * LDV];
+
+    // ---- work item: block b runs head quad (b >> 3) & 3 of unit (b >> 5) * 8 + (b & 7),
+    // so the four workgroups of a unit (its 16 heads) share an XCD
+    const int nqb = (a.n_new + BMW - 1) / BMW;
+    const int b = blockIdx.x;
+    const int hq = (b >> 3) & 3;
+    const int unit = (b >> 5) * 8 + (b & 7);
+    const int per_qb = a.n_seq * kKvHeads;
+    if (unit >= per_qb * nqb) return;
+    const int qb = nqb - 1 - unit / per_qb;            // heavy blocks first
+    const int s = (unit % per_qb) >> 1;
+    const int g = (unit % per_qb) & 1;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, gl = lane >> 5;
+    const int h = g * kHeadsPerKv + hq * 4 + wave;
+    const int q0 = qb * BMW;
+    const int N = a.n_new;
+    const int L = a.seq_len[s];
+
+    T* out = (T*)a.out;
+    if (L < 0 || L > a.max_seq_len) {                  // refused on the device
+        const int rows = min(BMW, N - q0);
+        for (int i = lane; i < rows * D; i += 64) {
+            const int t = q0 + i / D;
+            out[(((int64_t)s * N + t) * kHeads + h) * D + (i % D)] = from_f32<T>(__builtin_nanf(""));
+        }
+        return;
+    }
+
+    // ---- Q-hat fragments of the wave's two 32-row groups (B operand of S^T = K Q^T)
+    FragQ qf[QG][NST];
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+        const int tq = q0 + 32 * qg + l32;
+        const TQ* qrow = (const TQ*)a.qhat + (((int64_t)s * N + tq) * kHeads + h) * D;
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+            qf[qg][st] = tq < N ? *(const FragQ*)(qrow + 2 * MQ::KPL * st + MQ::KPL * gl) : FragQ{};
+    }
+
+    // ---- keys the workgroup can see (positions fit in int32: bounded by 2^24)
+    const int W = a.window;
+    const int P0 = L + q0, P1 = L + min(q0 + BMW - 1, N - 1);
+    const int kv_lo = (W > 0) ? max(0, P0 - W + 1) : 0;
+    const int kv_end = L + N;
+    const int tile_lo = kv_lo / BN, tile_hi = P1 / BN;
+    const int ntiles = tile_hi - tile_lo + 1;
+    const int pq0 = L + q0 + l32;                      // position of this lane's row in group 0
+
+    constexpr int64_t ROW = (int64_t)kKvHeads * D * ES;
+    constexpr int RSTEP = 256 / CPR;
+    const int r_t = tid / CPR, c_t = tid % CPR;
+    const char* kbase = (const char*)a.kq + (((int64_t)s * a.kq_capacity) * kKvHeads + g) * D * ES +
+                        r_t * ROW + c_t * 16;
+    const char* vbase = (const char*)a.cache_v + (((int64_t)s * a.capacity) * kKvHeads + g) * D * ES +
+                        r_t * ROW + c_t * 16;
+    u32x4 kreg[NCH], vreg[NCH];
+    // tile rows into registers (interior tiles skip the per-row bounds checks)
+    auto load_tile = [&](int tile, bool with_v) __attribute__((always_inline)) {
+        const int j0 = tile * BN;
+        const char* kp = kbase + (int64_t)j0 * ROW;
+        const char* vp = vbase + (int64_t)j0 * ROW;
+        if (j0 >= kv_lo && j0 + BN <= kv_end) {
+#pragma unroll
+            for (int u = 0; u < NCH; ++u) {
+                kreg[u] = *(const u32x4*)(kp + u * RSTEP * ROW);
+                if (with_v) vreg[u] = *(const u32x4*)(vp + u * RSTEP * ROW);
+            }
+        } else {
+            asm volatile("");                              // keep this a branch
+#pragma unroll
+            for (int u = 0; u < NCH; ++u) {
+                const int jj = j0 + r_t + u * RSTEP;
+                const bool in = jj >= kv_lo && jj < kv_end;
+                kreg[u] = in ? *(const u32x4*)(kp + u * RSTEP * ROW) : u32x4{0, 0, 0, 0};
+                if (with_v) vreg[u] = in ? *(const u32x4*)(vp + u * RSTEP * ROW) : u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+    auto store_tile = [&](int bufi, bool with_v) __attribute__((always_inline)) {
+        char* kd = (char*)Ks[bufi] + r_t * LDK * ES + c_t * 16;
+        char* vd = (char*)Vs[bufi] + r_t * LDV * ES + c_t * 16;
+#pragma unroll
+        for (int u = 0; u < NCH; ++u) {
+            *(u32x4*)(kd + u * RSTEP * LDK * ES) = kreg[u];
+            if (with_v) *(u32x4*)(vd + u * RSTEP * LDV * ES) = vreg[u];
+        }
+    };
+
+    // S^T halves (keys 32kt..32kt+31 x the wave's two row groups), started at c0
+    auto qk = [&](floatx16 (&sc)[2][QG], const TQ* Kc, const floatx16 (&c0)[QG]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) sc[kt][qg] = c0[qg];
+#pragma unroll
+            for (int st = 0; st < NST; ++st) {
+                const FragQ kf = *(const FragQ*)(Kc + (32 * kt + l32) * LDK + 2 * MQ::KPL * st + MQ::KPL * gl);
+#pragma unroll
+                for (int qg = 0; qg < QG; ++qg) sc[kt][qg] = MQ::mma(kf, qf[qg][st], sc[kt][qg]);
+            }
+        }
+    };
+    // key 32kt + 8(i/4) + 4gl + i%4 of the tile at j0 is visible to row (qg, l32)
+    // iff 0 <= p - key < W (W = infinity on full layers)
+    auto apply_mask = [&](floatx16 (&sc)[2][QG], int j0) __attribute__((always_inline)) {
+        const unsigned wlim = W > 0 ? (unsigned)W : 0x7fffffffu;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int jj = j0 + 32 * kt + 8 * (i / 4) + 4 * gl + (i % 4);
+                    sc[kt][qg][i] = ((unsigned)(pq0 + 32 * qg - jj) < wlim) ? sc[kt][qg][i] : kNegInf;
+                }
+    };
+    auto row_max = [&](const floatx16& v) __attribute__((always_inline)) {
+        float m4[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+        for (int i = 4; i < 16; ++i) m4[i % 4] = fmaxf(m4[i % 4], v[i]);
+        return max_halves(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+    };
+
+    float ref[QG];                                     // row references; -inf until set
+    floatx16 nref[QG];                                 // -ref broadcast (0 while unset)
+    floatx16 o[4][QG];                                 // O^T tiles [dims 32dt..][row group]
+    float l_run[QG];
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+        ref[qg] = kNegInf;
+        nref[qg] = floatx16{};
+    }
+    auto set_nref = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) {
+            const float v = ref[qg] == kNegInf ? 0.0f : -ref[qg];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) nref[qg][i] = v;
+        }
+    };
+
+    for (int pass = 0; pass < 2; ++pass) {
+        if (pass == 1) {
+            // exact row maxima from a Q.K-only sweep over the same tiles
+            float mx[QG];
+            floatx16 zero[QG];
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) {
+                mx[qg] = kNegInf;
+                zero[qg] = floatx16{};
+            }
+            load_tile(tile_lo, false);
+            store_tile(0, false);
+            __syncthreads();
+            for (int it = 0; it < ntiles; ++it) {
+                const int cur = it & 1;
+                const int j0 = (tile_lo + it) * BN;
+                if (it + 1 < ntiles) load_tile(tile_lo + it + 1, false);
+                floatx16 sc[2][QG];
+                qk(sc, Ks[cur], zero);
+                apply_mask(sc, j0);
+#pragma unroll
+                for (int qg = 0; qg < QG; ++qg) mx[qg] = fmaxf(mx[qg], fmaxf(row_max(sc[0][qg]), row_max(sc[1][qg])));
+                if (it + 1 < ntiles) store_tile(cur ^ 1, false);
+                __syncthreads();
+            }
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) ref[qg] = mx[qg];
+            set_nref();
+        }
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) {
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o[dt][qg] = floatx16{};
+            l_run[qg] = 0.0f;
+        }
+
+        load_tile(tile_lo, true);
+        store_tile(0, true);
+        __syncthreads();
+        for (int it = 0; it < ntiles; ++it) {
+            const int cur = it & 1;
+            const int j0 = (tile_lo + it) * BN;
+            const bool has_next = it + 1 < ntiles;
+            if (has_next) load_tile(tile_lo + it + 1, true);   // in flight during the compute
+            const bool masked = (j0 + BN - 1 > P0) || (W > 0 && P1 - j0 >= W);
+            bool unset[QG], any_unset = false;
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) {
+                unset[qg] = ref[qg] == kNegInf;
+                any_unset = any_unset || unset[qg];
+            }
+
+            floatx16 sc[2][QG];
+            qk(sc, Ks[cur], nref);
+            if (has_next) store_tile(cur ^ 1, true);       // that buffer is free since the last barrier
+            if (masked) {
+                asm volatile("");                          // keep this a branch
+                apply_mask(sc, j0);
+            }
+            if (__ballot(any_unset) != 0) {
+                // rows still without a reference take the maximum of their first
+                // visible half; their scores were computed from 0, not -ref
+                asm volatile("");                          // keep this a branch
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int qg = 0; qg < QG; ++qg) {
+                        const float m = row_max(sc[kt][qg]);
+                        if (ref[qg] == kNegInf && m > kNegInf) ref[qg] = m;
+                        const float r = (unset[qg] && ref[qg] != kNegInf) ? ref[qg] : 0.0f;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) sc[kt][qg][i] -= r;
+                    }
+                set_nref();
+            }
+
+            // P = exp2(S - ref) in bf16; l += sum of those P; O^T += V^T P^T
+            const T* Vc = Vs[cur];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {               // 16 keys per K-step
+                FragP pf[QG];
+#pragma unroll
+                for (int qg = 0; qg < QG; ++qg) {
+#pragma unroll
+                    for (int t = 0; t < MP::KPL; ++t) frag_set(pf[qg], t, fast_exp2(sc[st / 2][qg][8 * (st % 2) + t]));
+                    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+                    float acc = l_run[qg];
+                    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[qg], pf[qg], 0, 1), one, acc, false);
+                    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[qg], pf[qg], 2, 3), one, acc, false);
+                    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[qg], pf[qg], 4, 5), one, acc, false);
+                    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[qg], pf[qg], 6, 7), one, acc, false);
+                    l_run[qg] = acc;
+                }
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    // item t of lane group gl is key kb + 8*(t/4) + t%4 with
+                    // kb = 32(st/2) + 16(st%2) + 4gl; each run of 4 keys is one
+                    // transposing read: source lane i of a 16-lane group points at
+                    // row kb + 8r + i/4, columns 32dt + 16*(group%2) + 4*(i%4)..+3
+                    typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+                    const int kb = 32 * (st / 2) + 16 * (st % 2) + 4 * gl;
+                    const int i16 = lane & 15;
+                    const int col = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+                    const T* src0 = Vc + (kb + (i16 >> 2)) * LDV + col;
+                    const T* src1 = src0 + 8 * LDV;
+                    const shortx4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_shortx4*)(__attribute__((address_space(3))) void*)src0);
+                    const shortx4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_shortx4*)(__attribute__((address_space(3))) void*)src1);
+                    const FragP vf = __builtin_bit_cast(FragP, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                    for (int qg = 0; qg < QG; ++qg) o[dt][qg] = MP::mma(vf, pf[qg], o[dt][qg]);
+                }
+            }
+            __syncthreads();
+        }
+
+        // an overflow anywhere shows up as a non-finite l or O
+        float chk = 0.0f;
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) chk += l_run[qg];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) chk += o[dt][qg][i];
+        if (!__syncthreads_or(!__builtin_isfinite(chk))) break;
+    }
+
+    // ---- epilogue: normalise, gate, store
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+        const float l_tot = sum_halves(l_run[qg]);
+        const int tq = q0 + 32 * qg + l32;
+        if (tq >= N) continue;
+        const float inv = 1.0f / l_tot;
+        const int64_t base = (((int64_t)s * N + tq) * kHeads + h) * D;
+        const T* gate = (const T*)a.gate + base;
+        T* dst = out + base;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+            for (int ig = 0; ig < 4; ++ig) {
+                const int d0 = 32 * dt + 8 * ig + 4 * gl;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const float gv = to_f32(gate[d0 + x]);
+                    dst[d0 + x] = from_f32<T>(o[dt][qg][4 * ig + x] * inv * sigmoid(gv));
+                }
+            }
+        }
+    }
+}
+
 hipError_t launch_prefill(const AttnArgs& a, int dtype, hipStream_t stream) {
-    const dim3 grid((unsigned)prefill_grid(a.n_seq, a.n_new)), block(256);
+    const dim3 block(256);
     if (dtype == 1)
-        hipLaunchKernelGGL(prefill_kernel<bf16_t>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL(prefill_gqa4_kernel<MUSE_PREFILL_QG>,
+                           dim3((unsigned)prefill_grid_gqa4(a.n_seq, a.n_new, 32 * MUSE_PREFILL_QG)), block, 0, stream, a);
     else
-        hipLaunchKernelGGL(prefill_kernel<float>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL(prefill_kernel<float>, dim3((unsigned)prefill_grid(a.n_seq, a.n_new)), block, 0,
+                           stream, a);
     return hipGetLastError();
 }
 

@@ -57,6 +57,36 @@ def test_prefill_ragged(spec, seq_lens, dtype):
     _check_layer(w, spec, inp, decode=False)
 
 
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F32], ids=["bf16", "f32"])
+def test_prefill_reference_far_below_row_max(dtype):
+    """Scores that climb by far more than 2^128 after a row's first keys.
+
+    Full (NoPE) layer with Q gain 16, every query along one direction u: keys
+    0..31 point along -u (score -B), key 100 along +u (score +B), the rest are
+    random; B = |q-hat| |k-hat| * scale * log2(e) = 16 * 128 * scale * log2(e)
+    ~ 261 in log2 units.  A reference taken from a row's first keys sits 2B
+    below its maximum, so exp2(s - ref) overflows f32: the kernel has to
+    notice and redo those rows with the exact maxima.  Rows >= 100 reduce to
+    V[100] * sigmoid(gate); rows 32..99 to a softmax over the random keys.
+    """
+    spec = synth.full(q_gain=16.0)
+    B = spec.q_gain * spec.k_gain * 128 * spec.scale * np.log2(np.e)
+    assert 2 * B > 300                                  # far beyond the f32 range of exp2
+    N = 200
+    w = _custom("overflow_prefill", dtype, 1, 0, N, [spec])
+    inp = synth.layer_inputs(w, spec, device=DEV)
+    gen = torch.Generator(device="cpu").manual_seed(2024)
+    u = torch.randn(128, generator=gen, dtype=torch.float64)
+    tdt = inp.q.dtype
+    q = u.view(1, 1, 1, 128) + 0.05 * torch.randn(1, N, 32, 128, generator=gen, dtype=torch.float64)
+    inp.q.copy_(q.to(tdt))
+    k = inp.k.double().cpu()
+    k[0, :32] = -u
+    k[0, 100] = u
+    inp.k.copy_(k.to(tdt))
+    _check_layer(w, spec, inp, decode=False)
+
+
 @pytest.mark.parametrize("N", [1, 2, 31, 129])
 def test_prefill_tiny_chunks(N):
     spec = synth.sliding(16, 500000.0)
