@@ -36,6 +36,9 @@
 #ifndef MUSE_PREFILL_QG
 #define MUSE_PREFILL_QG 1   // 32-row query groups per wave on bf16 layers
 #endif
+#ifndef MUSE_PREFILL_WPB
+#define MUSE_PREFILL_WPB 4   // waves (heads of one KV group) per workgroup on bf16 layers
+#endif
 
 namespace muse {
 
@@ -349,19 +352,19 @@ void prefill_kernel(AttnArgs a) {
 // the Q.K MFMAs start from -ref instead of 0, so no subtraction is left
 // either.  Row sums are taken from the bf16 P values that enter the P.V
 // product (v_dot2 against (1, 1)).
-template <int QG> struct Gqa4Traits {
+template <int QG> struct GroupTraits {
     static constexpr int WAVES = QG == 1 ? 2 : 1;      // waves per SIMD the registers allow
 };
 
-int prefill_grid_gqa4(int n_seq, int n_new, int rows_per_wave) {
+int prefill_grid_group(int n_seq, int n_new, int rows_per_wave, int heads_per_block) {
     const int nqb = (n_new + rows_per_wave - 1) / rows_per_wave;
     const int units = n_seq * kKvHeads * nqb;          // (q-block, seq, kv head)
-    return ((units + 7) / 8) * 8 * (kHeadsPerKv / 4);
+    return ((units + 7) / 8) * 8 * (kHeadsPerKv / heads_per_block);
 }
 
-template <int QG>                                      // 32-row query groups per wave
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Gqa4Traits<QG>::WAVES)))
-void prefill_gqa4_kernel(AttnArgs a) {
+template <int QG, int WPB>                             // 32-row query groups per wave, waves (heads) per block
+__global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(GroupTraits<QG>::WAVES)))
+void prefill_group_kernel(AttnArgs a) {
     typedef bf16_t T;
     typedef f16_t TQ;
     using MQ = Mma32<TQ>;
@@ -374,16 +377,18 @@ void prefill_gqa4_kernel(AttnArgs a) {
     constexpr int NST = D / (2 * MQ::KPL);             // K-steps of Q.K (8)
     constexpr int ES = 2;
     constexpr int CPR = D * ES / 16;                   // 16-byte chunks per row
-    constexpr int NCH = BN * CPR / 256;                // chunks per thread per tile
+    constexpr int NT = 64 * WPB;                       // threads per block
+    constexpr int HQ = kHeadsPerKv / WPB;              // blocks per (q-block, seq, kv head)
+    constexpr int NCH = BN * CPR / NT;                 // chunks per thread per tile
     __shared__ __attribute__((aligned(16))) TQ Ks[2][BN * LDK];
     __shared__ __attribute__((aligned(16))) T Vs[2][BN * LDV];
 
-    // ---- work item: block b runs head quad (b >> 3) & 3 of unit (b >> 5) * 8 + (b & 7),
-    // so the four workgroups of a unit (its 16 heads) share an XCD
+    // ---- work item: block b runs head group (b >> 3) % HQ of unit (b >> 3) / HQ * 8 + (b & 7),
+    // so the workgroups of a unit (its 16 heads) share an XCD
     const int nqb = (a.n_new + BMW - 1) / BMW;
     const int b = blockIdx.x;
-    const int hq = (b >> 3) & 3;
-    const int unit = (b >> 5) * 8 + (b & 7);
+    const int hq = (b >> 3) % HQ;
+    const int unit = (b >> 3) / HQ * 8 + (b & 7);
     const int per_qb = a.n_seq * kKvHeads;
     if (unit >= per_qb * nqb) return;
     const int qb = nqb - 1 - unit / per_qb;            // heavy blocks first
@@ -393,7 +398,7 @@ void prefill_gqa4_kernel(AttnArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, gl = lane >> 5;
-    const int h = g * kHeadsPerKv + hq * 4 + wave;
+    const int h = g * kHeadsPerKv + hq * WPB + wave;
     const int q0 = qb * BMW;
     const int N = a.n_new;
     const int L = a.seq_len[s];
@@ -429,33 +434,24 @@ void prefill_gqa4_kernel(AttnArgs a) {
     const int pq0 = L + q0 + l32;                      // position of this lane's row in group 0
 
     constexpr int64_t ROW = (int64_t)kKvHeads * D * ES;
-    constexpr int RSTEP = 256 / CPR;
+    constexpr int RSTEP = NT / CPR;
     const int r_t = tid / CPR, c_t = tid % CPR;
-    const char* kbase = (const char*)a.kq + (((int64_t)s * a.kq_capacity) * kKvHeads + g) * D * ES +
-                        r_t * ROW + c_t * 16;
-    const char* vbase = (const char*)a.cache_v + (((int64_t)s * a.capacity) * kKvHeads + g) * D * ES +
-                        r_t * ROW + c_t * 16;
+    const char* kbase = (const char*)a.kq + (((int64_t)s * a.kq_capacity) * kKvHeads + g) * D * ES + c_t * 16;
+    const char* vbase = (const char*)a.cache_v + (((int64_t)s * a.capacity) * kKvHeads + g) * D * ES + c_t * 16;
     u32x4 kreg[NCH], vreg[NCH];
-    // tile rows into registers (interior tiles skip the per-row bounds checks)
+    // Tile rows into registers.  Rows past the last cached position are
+    // clamped to it (in-bounds, finite data): every key there lies after
+    // every query of the workgroup, so the mask gives it P = 0.  Rows before
+    // the window start are real cache rows and are masked the same way.  No
+    // branch here: a zero-fill path would make the compiler wait for all
+    // loads where the two paths meet.
     auto load_tile = [&](int tile, bool with_v) __attribute__((always_inline)) {
         const int j0 = tile * BN;
-        const char* kp = kbase + (int64_t)j0 * ROW;
-        const char* vp = vbase + (int64_t)j0 * ROW;
-        if (j0 >= kv_lo && j0 + BN <= kv_end) {
 #pragma unroll
-            for (int u = 0; u < NCH; ++u) {
-                kreg[u] = *(const u32x4*)(kp + u * RSTEP * ROW);
-                if (with_v) vreg[u] = *(const u32x4*)(vp + u * RSTEP * ROW);
-            }
-        } else {
-            asm volatile("");                              // keep this a branch
-#pragma unroll
-            for (int u = 0; u < NCH; ++u) {
-                const int jj = j0 + r_t + u * RSTEP;
-                const bool in = jj >= kv_lo && jj < kv_end;
-                kreg[u] = in ? *(const u32x4*)(kp + u * RSTEP * ROW) : u32x4{0, 0, 0, 0};
-                if (with_v) vreg[u] = in ? *(const u32x4*)(vp + u * RSTEP * ROW) : u32x4{0, 0, 0, 0};
-            }
+        for (int u = 0; u < NCH; ++u) {
+            const int64_t off = (int64_t)min(j0 + r_t + u * RSTEP, kv_end - 1) * ROW;
+            kreg[u] = *(const u32x4*)(kbase + off);
+            if (with_v) vreg[u] = *(const u32x4*)(vbase + off);
         }
     };
     auto store_tile = [&](int bufi, bool with_v) __attribute__((always_inline)) {
@@ -537,13 +533,13 @@ void prefill_gqa4_kernel(AttnArgs a) {
             for (int it = 0; it < ntiles; ++it) {
                 const int cur = it & 1;
                 const int j0 = (tile_lo + it) * BN;
-                if (it + 1 < ntiles) load_tile(tile_lo + it + 1, false);
+                load_tile(min(tile_lo + it + 1, tile_hi), false);   // the last one is a harmless repeat
                 floatx16 sc[2][QG];
                 qk(sc, Ks[cur], zero);
                 apply_mask(sc, j0);
 #pragma unroll
                 for (int qg = 0; qg < QG; ++qg) mx[qg] = fmaxf(mx[qg], fmaxf(row_max(sc[0][qg]), row_max(sc[1][qg])));
-                if (it + 1 < ntiles) store_tile(cur ^ 1, false);
+                store_tile(cur ^ 1, false);
                 __syncthreads();
             }
 #pragma unroll
@@ -563,8 +559,7 @@ void prefill_gqa4_kernel(AttnArgs a) {
         for (int it = 0; it < ntiles; ++it) {
             const int cur = it & 1;
             const int j0 = (tile_lo + it) * BN;
-            const bool has_next = it + 1 < ntiles;
-            if (has_next) load_tile(tile_lo + it + 1, true);   // in flight during the compute
+            load_tile(min(tile_lo + it + 1, tile_hi), true);   // in flight during the compute (last: a repeat)
             const bool masked = (j0 + BN - 1 > P0) || (W > 0 && P1 - j0 >= W);
             bool unset[QG], any_unset = false;
 #pragma unroll
@@ -575,7 +570,7 @@ void prefill_gqa4_kernel(AttnArgs a) {
 
             floatx16 sc[2][QG];
             qk(sc, Ks[cur], nref);
-            if (has_next) store_tile(cur ^ 1, true);       // that buffer is free since the last barrier
+            store_tile(cur ^ 1, true);                     // that buffer is free since the last barrier
             if (masked) {
                 asm volatile("");                          // keep this a branch
                 apply_mask(sc, j0);
@@ -677,12 +672,12 @@ void prefill_gqa4_kernel(AttnArgs a) {
 }
 
 hipError_t launch_prefill(const AttnArgs& a, int dtype, hipStream_t stream) {
-    const dim3 block(256);
     if (dtype == 1)
-        hipLaunchKernelGGL(prefill_gqa4_kernel<MUSE_PREFILL_QG>,
-                           dim3((unsigned)prefill_grid_gqa4(a.n_seq, a.n_new, 32 * MUSE_PREFILL_QG)), block, 0, stream, a);
+        hipLaunchKernelGGL((prefill_group_kernel<MUSE_PREFILL_QG, MUSE_PREFILL_WPB>),
+                           dim3((unsigned)prefill_grid_group(a.n_seq, a.n_new, 32 * MUSE_PREFILL_QG, MUSE_PREFILL_WPB)),
+                           dim3(64 * MUSE_PREFILL_WPB), 0, stream, a);
     else
-        hipLaunchKernelGGL(prefill_kernel<float>, dim3((unsigned)prefill_grid(a.n_seq, a.n_new)), block, 0,
+        hipLaunchKernelGGL(prefill_kernel<float>, dim3((unsigned)prefill_grid(a.n_seq, a.n_new)), dim3(256), 0,
                            stream, a);
     return hipGetLastError();
 }
