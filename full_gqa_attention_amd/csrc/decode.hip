@@ -126,47 +126,49 @@ void decode_kernel(DecodeArgs a) {
     T* Kw = (T*)(wave_lds + WAVE_V);
     float* Qf = (float*)(lds + 4 * (WAVE_V + WAVE_K));
 
-    // ---- loads of one 16-row sub-tile (rows >= ce and row p are zero)
+    // ---- loads of one 16-row sub-tile.  Every lane always loads (a load
+    // skipped by some waves would make the compiler wait for all of them):
+    // rows past the split are clamped to its last row ce - 1, whose score is
+    // masked to P = 0 later; a lane whose (clamped) row is p gets the new
+    // K/V row from LDS instead of the cache row being written.
     const int64_t row_stride = (int64_t)kKvHeads * D * ES;          // bytes per position
     const char* gk = (const char*)a.cache_k + ((int64_t)s * a.capacity * kKvHeads + g) * D * ES;
     const char* gv = (const char*)a.cache_v + ((int64_t)s * a.capacity * kKvHeads + g) * D * ES;
+    auto clamp_row = [&](int64_t j) __attribute__((always_inline)) { return j < ce ? j : ce - 1; };
     auto issue = [&](SubTile<T>& t, int k) __attribute__((always_inline)) {
         const int64_t j0 = cs + (int64_t)SUB * (wave + 4 * k);
         if constexpr (kBf16) {
-            const int64_t jr = j0 + l16;               // K: row l16, MFMA A layout
+            const int64_t jr = clamp_row(j0 + l16);    // K: row l16, MFMA A layout
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                t.k[st] = u32x4{0, 0, 0, 0};
-                if (jr < ce && jr != p)
-                    t.k[st] = *(const u32x4*)(gk + jr * row_stride + (8 * q4 + 32 * st) * ES);
-            }
+            for (int st = 0; st < 4; ++st)
+                t.k[st] = __builtin_nontemporal_load((const u32x4*)(gk + jr * row_stride + (8 * q4 + 32 * st) * ES));
 #pragma unroll
             for (int u = 0; u < 4; ++u) {              // V: rows 4u + lane/16, 16-B chunk lane%16
-                const int64_t jv = j0 + 4 * u + q4;
-                t.v[u] = u32x4{0, 0, 0, 0};
-                if (jv < ce && jv != p) t.v[u] = *(const u32x4*)(gv + jv * row_stride + l16 * 16);
+                const int64_t jv = clamp_row(j0 + 4 * u + q4);
+                t.v[u] = __builtin_nontemporal_load((const u32x4*)(gv + jv * row_stride + l16 * 16));
             }
         } else {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {              // rows 2u + lane/32, 16-B chunk lane%32
-                const int64_t jj = j0 + 2 * u + (lane >> 5);
-                t.k[u] = u32x4{0, 0, 0, 0};
-                t.v[u] = u32x4{0, 0, 0, 0};
-                if (jj < ce && jj != p) {
-                    t.k[u] = *(const u32x4*)(gk + jj * row_stride + (lane & 31) * 16);
-                    t.v[u] = *(const u32x4*)(gv + jj * row_stride + (lane & 31) * 16);
-                }
+                const int64_t jj = clamp_row(j0 + 2 * u + (lane >> 5));
+                t.k[u] = __builtin_nontemporal_load((const u32x4*)(gk + jj * row_stride + (lane & 31) * 16));
+                t.v[u] = __builtin_nontemporal_load((const u32x4*)(gv + jj * row_stride + (lane & 31) * 16));
             }
         }
     };
 
     // pipeline stages as named variables (an indexed array of them ends up in scratch)
-    static_assert(DEPTH >= 1 && DEPTH <= 4, "pipeline depth 1..4");
-    SubTile<T> b0, b1, b2, b3;
-    if (0 < my_cnt) issue(b0, 0);
-    if constexpr (DEPTH > 1) if (1 < my_cnt) issue(b1, 1);
-    if constexpr (DEPTH > 2) if (2 < my_cnt) issue(b2, 2);
-    if constexpr (DEPTH > 3) if (3 < my_cnt) issue(b3, 3);
+    static_assert(DEPTH >= 1 && DEPTH <= 8, "pipeline depth 1..8");
+    SubTile<T> b0, b1, b2, b3, b4, b5, b6, b7;
+    // (sub-tiles past the wave's share load clamped rows and are never processed)
+    issue(b0, 0);
+    if constexpr (DEPTH > 1) issue(b1, 1);
+    if constexpr (DEPTH > 2) issue(b2, 2);
+    if constexpr (DEPTH > 3) issue(b3, 3);
+    if constexpr (DEPTH > 4) issue(b4, 4);
+    if constexpr (DEPTH > 5) issue(b5, 5);
+    if constexpr (DEPTH > 6) issue(b6, 6);
+    if constexpr (DEPTH > 7) issue(b7, 7);
 
     // ---- prologue: Q-hat of the 16 heads (f32 in LDS); the owner of p also
     // makes the new K/V row
@@ -241,7 +243,7 @@ void decode_kernel(DecodeArgs a) {
         // ---- scores S^T[key j0 + 4*q4 + i][head l16]
         floatx4 sc = floatx4{};
         if constexpr (kBf16) {
-            const bool krow_p = (j0 + l16 == p);
+            const bool krow_p = (clamp_row(j0 + l16) == p);
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 u32x4 kraw = t.k[st];
@@ -255,7 +257,7 @@ void decode_kernel(DecodeArgs a) {
             for (int u = 0; u < 8; ++u) {
                 const int r = 2 * u + (lane >> 5);
                 u32x4 kraw = t.k[u], vraw = t.v[u];
-                if (j0 + r == p) {
+                if (clamp_row(j0 + r) == p) {
                     kraw = *(const u32x4*)(knew + (lane & 31) * 4);
                     vraw = *(const u32x4*)(vnew + (lane & 31) * 4);
                 }
@@ -293,7 +295,7 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 u32x4 vraw = t.v[u];
-                if (j0 + 4 * u + q4 == p) vraw = *(const u32x4*)(vnew + l16 * 8);
+                if (clamp_row(j0 + 4 * u + q4) == p) vraw = *(const u32x4*)(vnew + l16 * 8);
                 *(u32x4*)(Vw + (4 * u + q4) * LDV + l16 * 8) = vraw;
             }
             typename MN::Frag pf;
@@ -321,17 +323,21 @@ void decode_kernel(DecodeArgs a) {
         }
     };
 
+    // the same number of loads in every stage keeps the compiler's load
+    // counting exact (it waits for one stage's loads, not for all)
     auto stage = [&](SubTile<T>& t, int k) __attribute__((always_inline)) {
-        if (k < my_cnt) {
-            process(t, k);
-            if (k + DEPTH < my_cnt) issue(t, k + DEPTH);
-        }
+        if (k < my_cnt) process(t, k);
+        issue(t, k + DEPTH);
     };
     for (int k0 = 0; k0 < my_cnt; k0 += DEPTH) {
         stage(b0, k0);
         if constexpr (DEPTH > 1) stage(b1, k0 + 1);
         if constexpr (DEPTH > 2) stage(b2, k0 + 2);
         if constexpr (DEPTH > 3) stage(b3, k0 + 3);
+        if constexpr (DEPTH > 4) stage(b4, k0 + 4);
+        if constexpr (DEPTH > 5) stage(b5, k0 + 5);
+        if constexpr (DEPTH > 6) stage(b6, k0 + 6);
+        if constexpr (DEPTH > 7) stage(b7, k0 + 7);
     }
 
     // ---- merge the 4 waves: LDS holds per wave [16 heads][128 + 2] floats
