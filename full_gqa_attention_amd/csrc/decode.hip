@@ -12,8 +12,8 @@
 // Streaming: each wave owns every fourth 16-row sub-tile of the split and
 // keeps DEPTH sub-tiles of loads in flight in registers; there is no
 // workgroup barrier inside the loop, so the waves of a CU overlap freely.
-//   * K goes straight from HBM into the A-operand layout of a 16x16x32 MFMA
-//     (16 rows x 16 heads per tile, S^T = K Q^T).  On bf16 layers Q-hat is
+//   * K rows go through a wave-private LDS buffer into the A-operand layout of
+//     a 16x16x32 MFMA (16 rows x 16 heads per tile, S^T = K Q^T).  On bf16 layers Q-hat is
 //     split into bf16 hi + lo parts (two MFMAs), which scores with about 16
 //     significant bits and takes the stored bf16 keys as they are.
 //   * V rows are written to a wave-private LDS buffer and read back with the
@@ -60,10 +60,12 @@ __device__ __forceinline__ float observe(const float* p) {
 
 template <typename T> struct DecodeTraits;
 // bf16: K in registers in MFMA layout (4 x 16 B per lane), V row-major (4 x 16 B)
+// bf16: K and V rows loaded alike (4 rows x 256 B per load instruction) and
+// staged in LDS; K is read back in the A-operand layout of the 16x16x32 MFMA
 template <> struct DecodeTraits<bf16_t> {
     static constexpr int KREG = 4, VREG = 4;
     static constexpr int LDV = kHeadDim + 16;          // V row stride in LDS (elements)
-    static constexpr int LDKW = 0;                     // no K staging in LDS
+    static constexpr int LDKW = kHeadDim + 8;          // K row stride in LDS: b128 reads conflict-free
 };
 // f32 (parity path): K and V both row-major through LDS (8 x 16 B each)
 template <> struct DecodeTraits<float> {
@@ -138,13 +140,13 @@ void decode_kernel(DecodeArgs a) {
     auto issue = [&](SubTile<T>& t, int k) __attribute__((always_inline)) {
         const int64_t j0 = cs + (int64_t)SUB * (wave + 4 * k);
         if constexpr (kBf16) {
-            const int64_t jr = clamp_row(j0 + l16);    // K: row l16, MFMA A layout
+            // K and V: rows 4u + lane/16, 16-B chunk lane%16 (whole 256-B rows per
+            // 16 lanes; loading K straight into the MFMA layout, 64 B from each of
+            // 16 rows per instruction, streams far slower)
 #pragma unroll
-            for (int st = 0; st < 4; ++st)
-                t.k[st] = __builtin_nontemporal_load((const u32x4*)(gk + jr * row_stride + (8 * q4 + 32 * st) * ES));
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {              // V: rows 4u + lane/16, 16-B chunk lane%16
+            for (int u = 0; u < 4; ++u) {
                 const int64_t jv = clamp_row(j0 + 4 * u + q4);
+                t.k[u] = __builtin_nontemporal_load((const u32x4*)(gk + jv * row_stride + l16 * 16));
                 t.v[u] = __builtin_nontemporal_load((const u32x4*)(gv + jv * row_stride + l16 * 16));
             }
         } else {
@@ -243,12 +245,21 @@ void decode_kernel(DecodeArgs a) {
         // ---- scores S^T[key j0 + 4*q4 + i][head l16]
         floatx4 sc = floatx4{};
         if constexpr (kBf16) {
-            const bool krow_p = (clamp_row(j0 + l16) == p);
+            // stage K and V rows (row p from the new row), then K back in the A layout
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = 4 * u + q4;
+                u32x4 kraw = t.k[u], vraw = t.v[u];
+                if (clamp_row(j0 + r) == p) {
+                    kraw = *(const u32x4*)(knew + l16 * 8);
+                    vraw = *(const u32x4*)(vnew + l16 * 8);
+                }
+                *(u32x4*)(Kw + r * LDKW + l16 * 8) = kraw;
+                *(u32x4*)(Vw + r * LDV + l16 * 8) = vraw;
+            }
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
-                u32x4 kraw = t.k[st];
-                if (krow_p) kraw = *(const u32x4*)(knew + 8 * q4 + 32 * st);
-                const bf16x8 kf = __builtin_bit_cast(bf16x8, kraw);
+                const bf16x8 kf = *(const bf16x8*)(Kw + l16 * LDKW + 8 * q4 + 32 * st);
                 sc = MW::mma(kf, qhi[st], sc);
                 sc = MW::mma(kf, qlo[st], sc);
             }
@@ -292,12 +303,6 @@ void decode_kernel(DecodeArgs a) {
 
         // ---- O^T += V^T P^T
         if constexpr (kBf16) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                u32x4 vraw = t.v[u];
-                if (clamp_row(j0 + 4 * u + q4) == p) vraw = *(const u32x4*)(vnew + l16 * 8);
-                *(u32x4*)(Vw + (4 * u + q4) * LDV + l16 * 8) = vraw;
-            }
             typename MN::Frag pf;
 #pragma unroll
             for (int i = 0; i < 4; ++i) frag_set(pf, i, sc[i]);
