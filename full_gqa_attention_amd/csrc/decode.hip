@@ -395,11 +395,19 @@ void decode_kernel(DecodeArgs a) {
     // count, and the merging split reads them with agent-coherent loads.  No
     // agent-scope fence is used: on this GPU one writes back / invalidates
     // the whole L2 of an XCD, which costs more than the attention itself.
+    // thread -> (head hh, 8 consecutive dims) in the final merge; its gate
+    // values are read now, so that the merging split does not wait for them
+    const int hh = tid >> 4, d0 = (tid & 15) * 8;
+    float gsig[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) gsig[x] = sigmoid(to_f32(gate[hh * D + d0 + x]));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
         unsigned long long* word = a.arrivals + (s * kKvHeads + g);
-        unsigned long long old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // first attempt assumes this split is the last to arrive: right for the
+        // split whose merge ends the call, one round trip saved
+        unsigned long long old = ((unsigned long long)a.tag << 32) | (unsigned int)(n_live - 1);
         unsigned int arrived = 0;
         for (;;) {                                     // retries only on contention
             const unsigned int cnt = ((unsigned int)(old >> 32) == a.tag) ? (unsigned int)old : 0u;
@@ -418,26 +426,45 @@ void decode_kernel(DecodeArgs a) {
     __syncthreads();
     if (!last_flag) return;
 
-    // thread -> (head hh, 8 consecutive dims)
-    const int hh = tid >> 4, d0 = (tid & 15) * 8;
+    // online merge of the splits' partials, four per round of loads
     const int64_t hb = ((int64_t)s * kHeads + g * HG + hh) * a.nsplit;
-    float M = kNegInf;
-    for (int cc = 0; cc < n_live; ++cc) M = fmaxf(M, observe(a.part_m + hb + cc));
+    float M = kNegInf, den = 0.0f;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    float den = 0.0f;
-    for (int cc = 0; cc < n_live; ++cc) {
-        const float e = fast_exp2(observe(a.part_m + hb + cc) - M);
-        den += observe(a.part_l + hb + cc) * e;
-        const float* po = a.part_o + (hb + cc) * D + d0;
+    for (int c0 = 0; c0 < n_live; c0 += 4) {
+        float pm[4], pl[4], po[4][8];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) acc[x] += observe(po + x) * e;
+        for (int j = 0; j < 4; ++j) {
+            const int cc = c0 + j;
+            pm[j] = kNegInf;
+            pl[j] = 0.0f;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) po[j][x] = 0.0f;
+            if (cc < n_live) {
+                pm[j] = observe(a.part_m + hb + cc);
+                pl[j] = observe(a.part_l + hb + cc);
+#pragma unroll
+                for (int x = 0; x < 8; ++x) po[j][x] = observe(a.part_o + (hb + cc) * D + d0 + x);
+            }
+        }
+        float Mn = M;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Mn = fmaxf(Mn, pm[j]);   // finite: split c0 has rows
+        const float rs = fast_exp2(M - Mn);                   // 0 on the first round
+        den *= rs;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[x] *= rs;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float e = fast_exp2(pm[j] - Mn);            // 0 for the padding entries
+            den += pl[j] * e;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) acc[x] += po[j][x] * e;
+        }
+        M = Mn;
     }
     const float inv = 1.0f / den;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-        const int i = hh * D + d0 + x;
-        out[i] = from_f32<T>(acc[x] * inv * sigmoid(to_f32(gate[i])));
-    }
+    for (int x = 0; x < 8; ++x) out[hh * D + d0 + x] = from_f32<T>(acc[x] * inv * gsig[x]);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream) {
