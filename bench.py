@@ -151,6 +151,8 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--eager", action="store_true",
+                    help="time decode steps as eager calls only (no HIP graph), e.g. under counter collection")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device copy first (scale for HBM byte counters)")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT", "COMMAND"),
@@ -239,7 +241,7 @@ def bench_decode(w, args, fa, synth, torch):
     runs = [LayerRun(w, spec, copies, True, fa, synth) for spec in w.layers]
     torch.cuda.synchronize()
     wall_eager, per_launch = run_timed(runs, args.steps, args.warmup, copies, fa, torch)
-    wall = run_graphs(runs, args.steps, args.warmup, copies, fa, torch)
+    wall = wall_eager if args.eager else run_graphs(runs, args.steps, args.warmup, copies, fa, torch)
     kv_per_step = per_step_unique
     ms_per_step = wall * 1e3 / args.steps
     launches = len(per_launch)
@@ -376,7 +378,7 @@ def main():
         "data": "synthetic: seeded N(0,1) inputs and cache prefixes, resident in HBM",
         "config": res["config"], "roofline": res["roofline"],
         "frac_hbm_peak": round(res["value"] / HBM_PEAK_GBS, 4),
-        "launch": "each step replayed from a HIP graph of its kernel launches",
+        "launch": "eager calls" if args.eager else "each step replayed from a HIP graph of its kernel launches",
         "eager": res["eager"],
     }
     if not args.no_cpu_baseline:

@@ -10,10 +10,12 @@
 //   attn_scale (Ch 9, 9.5); out = softmax-weighted V times sigma(gate)
 //   (Ch 9, 9.8).
 //
-// Shape of the work: one workgroup = 128 query rows of one head (4 waves x
-// 32 rows).  KV tiles of 64 keys are double-buffered in LDS: while the waves
-// compute on one buffer, the next tile's loads are in flight in registers,
-// and land in the other buffer after the compute (one barrier per tile).
+// Two kernels share the scheme below.  prefill_kernel (f32 layers): one
+// workgroup = 128 query rows of one head (4 waves x 32 rows), 64-key tiles,
+// online softmax whose reference moves lazily.  prefill_group_kernel (bf16
+// layers, further down): one workgroup = 4 heads of one KV group over the same
+// 32 query rows, 32-key tiles, a fixed per-row softmax reference.
+//
 // Each wave computes S^T = K Q^T on 32x32 MFMA tiles (fp16 32x32x16 on bf16
 // layers, reading the fp16 key copy the prep kernel made; f32 32x32x2 on f32
 // layers), so a lane holds one query's scores: the row max and sum need one
@@ -21,13 +23,13 @@
 // score registers are the B operand as they are (the key order inside a
 // K-step is permuted identically in P and V), and the V^T A operand comes
 // from the transposing LDS load (ds_read_b64_tr_b16), two per MFMA.
-// Window-aware tile skipping: only tiles intersecting [p_lo - W + 1, p_hi]
-// are visited; masks are applied only on tiles that straddle a boundary; the
-// O rescale is skipped when no running maximum of the wave changed.
-// Workgroups are numbered so that the 16 heads sharing one KV head and one
-// query block land on the same XCD (round-robin dispatch over 8 XCDs), so
-// their K/V tiles are served by that XCD's L2; heavy (late) query blocks are
-// dispatched first.
+// K/V tiles are double-buffered in LDS with the next tile's loads in flight
+// during the compute (one barrier per tile).  Window-aware tile skipping:
+// only tiles intersecting [p_lo - W + 1, p_hi] are visited; masks are applied
+// only on tiles that straddle a boundary.  Workgroups are numbered so that the
+// 16 heads sharing one KV head and one query block land on the same XCD
+// (round-robin dispatch over 8 XCDs), so their K/V tiles are served by that
+// XCD's L2; heavy (late) query blocks are dispatched first.
 #include <type_traits>
 
 #include "device_common.h"
@@ -38,6 +40,12 @@
 #endif
 #ifndef MUSE_PREFILL_WPB
 #define MUSE_PREFILL_WPB 4   // waves (heads of one KV group) per workgroup on bf16 layers
+#endif
+#ifndef MUSE_PREFILL_KT
+#define MUSE_PREFILL_KT 1    // 32-key halves per K/V tile on bf16 layers
+#endif
+#ifndef MUSE_PREFILL_PIPE
+#define MUSE_PREFILL_PIPE 0  // software-pipelined tile loop on bf16 layers
 #endif
 
 namespace muse {
@@ -330,17 +338,16 @@ void prefill_kernel(AttnArgs a) {
     }
 }
 
-// ---- bf16 layers: four heads of one GQA group per workgroup, one head per
-// wave, 64 query rows per wave.  Each K/V fragment read from LDS feeds two
-// MFMAs (query rows 0-31 and 32-63 of the wave), which halves the LDS bytes
-// per flop of the 32-row layout above (with 32 rows per wave the LDS read
-// rate, not the matrix cores, bounds the loop).  A one-wave-per-SIMD launch
-// gives each wave the 512-entry register file: Q (64 rows), a tile's scores
-// and the O accumulators stay in registers.  The four waves share one row
-// range, so tile ranges and masks are uniform across the workgroup.
+// ---- bf16 layers: heads of one KV group per workgroup, one head per wave,
+// all waves over the same query rows, so tile ranges and masks are uniform
+// across the workgroup and each K/V tile staged in LDS serves every wave.
+// The build uses 4 heads x 32 rows per workgroup with 32-key tiles (QG = 1,
+// WPB = 4, KT = 1, no software pipelining): two waves per SIMD.  64 rows per
+// wave (QG = 2) halves the LDS reads per flop but needs one wave per SIMD,
+// and measured slower, as did 8 heads per workgroup and the pipelined loop.
 //
 // Softmax reference.  Each row's reference is fixed at the maximum of the
-// first 32-key half in which it sees a key, and never moves: later
+// first 32-key half-tile in which it sees a key, and never moves: later
 // exponentials are exp2(s - ref) with s - ref possibly > 0.  Softmax is
 // invariant to the reference (O and l carry the same factor), the maximum
 // key has P >= 1 so nothing underflows that matters, and the only failure is
@@ -362,7 +369,10 @@ int prefill_grid_group(int n_seq, int n_new, int rows_per_wave, int heads_per_bl
     return ((units + 7) / 8) * 8 * (kHeadsPerKv / heads_per_block);
 }
 
-template <int QG, int WPB>                             // 32-row query groups per wave, waves (heads) per block
+// QG: 32-row query groups per wave; WPB: waves (= heads of one KV group) per
+// workgroup; KT: 32-key halves per K/V tile; PIPE: issue the Q.K of the next
+// tile next to the softmax and P.V of the current one
+template <int QG, int WPB, int KT, bool PIPE>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(GroupTraits<QG>::WAVES)))
 void prefill_group_kernel(AttnArgs a) {
     typedef bf16_t T;
@@ -372,7 +382,7 @@ void prefill_group_kernel(AttnArgs a) {
     using FragQ = MQ::Frag;
     using FragP = MP::Frag;
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    constexpr int BMW = 32 * QG, BN = kPrefillBN, D = kHeadDim;
+    constexpr int BMW = 32 * QG, BN = 32 * KT, D = kHeadDim;
     constexpr int LDK = D + 8, LDV = D + 32;           // conflict-free b128 / transposing reads
     constexpr int NST = D / (2 * MQ::KPL);             // K-steps of Q.K (8)
     constexpr int ES = 2;
@@ -464,10 +474,33 @@ void prefill_group_kernel(AttnArgs a) {
         }
     };
 
-    // S^T halves (keys 32kt..32kt+31 x the wave's two row groups), started at c0
-    auto qk = [&](floatx16 (&sc)[2][QG], const TQ* Kc, const floatx16 (&c0)[QG]) __attribute__((always_inline)) {
+    auto load_k = [&](int tile) __attribute__((always_inline)) {
+        const int j0 = tile * BN;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int u = 0; u < NCH; ++u)
+            kreg[u] = *(const u32x4*)(kbase + (int64_t)min(j0 + r_t + u * RSTEP, kv_end - 1) * ROW);
+    };
+    auto load_v = [&](int tile) __attribute__((always_inline)) {
+        const int j0 = tile * BN;
+#pragma unroll
+        for (int u = 0; u < NCH; ++u)
+            vreg[u] = *(const u32x4*)(vbase + (int64_t)min(j0 + r_t + u * RSTEP, kv_end - 1) * ROW);
+    };
+    auto store_k = [&](int bufi) __attribute__((always_inline)) {
+        char* kd = (char*)Ks[bufi] + r_t * LDK * ES + c_t * 16;
+#pragma unroll
+        for (int u = 0; u < NCH; ++u) *(u32x4*)(kd + u * RSTEP * LDK * ES) = kreg[u];
+    };
+    auto store_v = [&](int bufi) __attribute__((always_inline)) {
+        char* vd = (char*)Vs[bufi] + r_t * LDV * ES + c_t * 16;
+#pragma unroll
+        for (int u = 0; u < NCH; ++u) *(u32x4*)(vd + u * RSTEP * LDV * ES) = vreg[u];
+    };
+
+    // S^T halves (keys 32kt..32kt+31 x the wave's row groups), started at c0
+    auto qk = [&](floatx16 (&sc)[KT][QG], const TQ* Kc, const floatx16 (&c0)[QG]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
             for (int qg = 0; qg < QG; ++qg) sc[kt][qg] = c0[qg];
 #pragma unroll
@@ -480,10 +513,10 @@ void prefill_group_kernel(AttnArgs a) {
     };
     // key 32kt + 8(i/4) + 4gl + i%4 of the tile at j0 is visible to row (qg, l32)
     // iff 0 <= p - key < W (W = infinity on full layers)
-    auto apply_mask = [&](floatx16 (&sc)[2][QG], int j0) __attribute__((always_inline)) {
+    auto apply_mask = [&](floatx16 (&sc)[KT][QG], int j0) __attribute__((always_inline)) {
         const unsigned wlim = W > 0 ? (unsigned)W : 0x7fffffffu;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int qg = 0; qg < QG; ++qg)
 #pragma unroll
@@ -517,6 +550,76 @@ void prefill_group_kernel(AttnArgs a) {
         }
     };
 
+    auto record_unset = [&](bool (&unset)[QG]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) unset[qg] = ref[qg] == kNegInf;
+    };
+    // mask of a boundary tile; rows still without a reference take the maximum
+    // of their first visible half (their scores were computed from 0, not -ref)
+    auto fix_tile = [&](floatx16 (&sc)[KT][QG], int j0, const bool (&unset)[QG]) __attribute__((always_inline)) {
+        const bool masked = (j0 + BN - 1 > P0) || (W > 0 && P1 - j0 >= W);
+        if (masked) {
+            asm volatile("");                              // keep this a branch
+            apply_mask(sc, j0);
+        }
+        bool any_unset = false;
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) any_unset = any_unset || unset[qg];
+        if (__ballot(any_unset) != 0) {
+            asm volatile("");                              // keep this a branch
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int qg = 0; qg < QG; ++qg) {
+                    const float m = row_max(sc[kt][qg]);
+                    if (ref[qg] == kNegInf && m > kNegInf) ref[qg] = m;
+                    const float r = (unset[qg] && ref[qg] != kNegInf) ? ref[qg] : 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sc[kt][qg][i] -= r;
+                }
+            set_nref();
+        }
+    };
+    // P = exp2(S - ref) in bf16; l += sum of those P; O^T += V^T P^T
+    auto softmax_pv = [&](floatx16 (&sc)[KT][QG], const T* Vc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int st = 0; st < 2 * KT; ++st) {              // 16 keys per K-step
+            FragP pf[QG];
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) {
+#pragma unroll
+                for (int t = 0; t < MP::KPL; ++t) frag_set(pf[qg], t, fast_exp2(sc[st / 2][qg][8 * (st % 2) + t]));
+                const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+                float acc = l_run[qg];
+                acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[qg], pf[qg], 0, 1), one, acc, false);
+                acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[qg], pf[qg], 2, 3), one, acc, false);
+                acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[qg], pf[qg], 4, 5), one, acc, false);
+                acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[qg], pf[qg], 6, 7), one, acc, false);
+                l_run[qg] = acc;
+            }
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                // item t of lane group gl is key kb + 8*(t/4) + t%4 with
+                // kb = 32(st/2) + 16(st%2) + 4gl; each run of 4 keys is one
+                // transposing read: source lane i of a 16-lane group points at
+                // row kb + 8r + i/4, columns 32dt + 16*(group%2) + 4*(i%4)..+3
+                typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+                const int kb = 32 * (st / 2) + 16 * (st % 2) + 4 * gl;
+                const int i16 = lane & 15;
+                const int col = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+                const T* src0 = Vc + (kb + (i16 >> 2)) * LDV + col;
+                const T* src1 = src0 + 8 * LDV;
+                const shortx4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_shortx4*)(__attribute__((address_space(3))) void*)src0);
+                const shortx4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_shortx4*)(__attribute__((address_space(3))) void*)src1);
+                const FragP vf = __builtin_bit_cast(FragP, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                for (int qg = 0; qg < QG; ++qg) o[dt][qg] = MP::mma(vf, pf[qg], o[dt][qg]);
+            }
+        }
+    };
+
     for (int pass = 0; pass < 2; ++pass) {
         if (pass == 1) {
             // exact row maxima from a Q.K-only sweep over the same tiles
@@ -534,11 +637,13 @@ void prefill_group_kernel(AttnArgs a) {
                 const int cur = it & 1;
                 const int j0 = (tile_lo + it) * BN;
                 load_tile(min(tile_lo + it + 1, tile_hi), false);   // the last one is a harmless repeat
-                floatx16 sc[2][QG];
+                floatx16 sc[KT][QG];
                 qk(sc, Ks[cur], zero);
                 apply_mask(sc, j0);
 #pragma unroll
-                for (int qg = 0; qg < QG; ++qg) mx[qg] = fmaxf(mx[qg], fmaxf(row_max(sc[0][qg]), row_max(sc[1][qg])));
+                for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+                    for (int kt = 0; kt < KT; ++kt) mx[qg] = fmaxf(mx[qg], row_max(sc[kt][qg]));
                 store_tile(cur ^ 1, false);
                 __syncthreads();
             }
@@ -553,84 +658,62 @@ void prefill_group_kernel(AttnArgs a) {
             l_run[qg] = 0.0f;
         }
 
-        load_tile(tile_lo, true);
-        store_tile(0, true);
-        __syncthreads();
-        for (int it = 0; it < ntiles; ++it) {
-            const int cur = it & 1;
-            const int j0 = (tile_lo + it) * BN;
-            load_tile(min(tile_lo + it + 1, tile_hi), true);   // in flight during the compute (last: a repeat)
-            const bool masked = (j0 + BN - 1 > P0) || (W > 0 && P1 - j0 >= W);
-            bool unset[QG], any_unset = false;
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg) {
-                unset[qg] = ref[qg] == kNegInf;
-                any_unset = any_unset || unset[qg];
-            }
-
-            floatx16 sc[2][QG];
-            qk(sc, Ks[cur], nref);
-            store_tile(cur ^ 1, true);                     // that buffer is free since the last barrier
-            if (masked) {
-                asm volatile("");                          // keep this a branch
-                apply_mask(sc, j0);
-            }
-            if (__ballot(any_unset) != 0) {
-                // rows still without a reference take the maximum of their first
-                // visible half; their scores were computed from 0, not -ref
-                asm volatile("");                          // keep this a branch
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int qg = 0; qg < QG; ++qg) {
-                        const float m = row_max(sc[kt][qg]);
-                        if (ref[qg] == kNegInf && m > kNegInf) ref[qg] = m;
-                        const float r = (unset[qg] && ref[qg] != kNegInf) ? ref[qg] : 0.0f;
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) sc[kt][qg][i] -= r;
-                    }
-                set_nref();
-            }
-
-            // P = exp2(S - ref) in bf16; l += sum of those P; O^T += V^T P^T
-            const T* Vc = Vs[cur];
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {               // 16 keys per K-step
-                FragP pf[QG];
-#pragma unroll
-                for (int qg = 0; qg < QG; ++qg) {
-#pragma unroll
-                    for (int t = 0; t < MP::KPL; ++t) frag_set(pf[qg], t, fast_exp2(sc[st / 2][qg][8 * (st % 2) + t]));
-                    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-                    float acc = l_run[qg];
-                    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[qg], pf[qg], 0, 1), one, acc, false);
-                    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[qg], pf[qg], 2, 3), one, acc, false);
-                    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[qg], pf[qg], 4, 5), one, acc, false);
-                    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[qg], pf[qg], 6, 7), one, acc, false);
-                    l_run[qg] = acc;
-                }
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    // item t of lane group gl is key kb + 8*(t/4) + t%4 with
-                    // kb = 32(st/2) + 16(st%2) + 4gl; each run of 4 keys is one
-                    // transposing read: source lane i of a 16-lane group points at
-                    // row kb + 8r + i/4, columns 32dt + 16*(group%2) + 4*(i%4)..+3
-                    typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
-                    const int kb = 32 * (st / 2) + 16 * (st % 2) + 4 * gl;
-                    const int i16 = lane & 15;
-                    const int col = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
-                    const T* src0 = Vc + (kb + (i16 >> 2)) * LDV + col;
-                    const T* src1 = src0 + 8 * LDV;
-                    const shortx4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_shortx4*)(__attribute__((address_space(3))) void*)src0);
-                    const shortx4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_shortx4*)(__attribute__((address_space(3))) void*)src1);
-                    const FragP vf = __builtin_bit_cast(FragP, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-                    for (int qg = 0; qg < QG; ++qg) o[dt][qg] = MP::mma(vf, pf[qg], o[dt][qg]);
-                }
-            }
+        if constexpr (!PIPE) {
+            load_tile(tile_lo, true);
+            store_tile(0, true);
             __syncthreads();
+            for (int it = 0; it < ntiles; ++it) {
+                const int cur = it & 1;
+                load_tile(min(tile_lo + it + 1, tile_hi), true);   // in flight during the compute (last: a repeat)
+                __builtin_amdgcn_sched_barrier(0);         // keep the loads ahead of the compute
+                bool unset[QG];
+                record_unset(unset);
+                floatx16 sc[KT][QG];
+                qk(sc, Ks[cur], nref);
+                store_tile(cur ^ 1, true);                 // that buffer is free since the last barrier
+                fix_tile(sc, (tile_lo + it) * BN, unset);
+                softmax_pv(sc, Vs[cur]);
+                __syncthreads();
+            }
+        } else {
+            // K runs one tile ahead of V: iteration it issues the Q.K of tile it+1
+            // (K slot (it+1)&1) next to the softmax and P.V of tile it (V slot
+            // it&1), while the loads of K[it+2] and V[it+1] are in flight; those
+            // land in K slot it&1 and V slot (it+1)&1, both last read before the
+            // previous barrier.  The mask and references of tile it+1 are applied
+            // after that barrier, so the loop body has no branch between the
+            // MFMAs of one tile and the VALU work of the other.
+            load_k(tile_lo);
+            load_v(tile_lo);
+            store_k(0);
+            store_v(0);
+            load_k(min(tile_lo + 1, tile_hi));
+            store_k(1);
+            __syncthreads();
+            floatx16 s0[KT][QG], s1[KT][QG];
+            bool un0[QG], un1[QG];
+            record_unset(un0);
+            qk(s0, Ks[0], nref);
+            fix_tile(s0, tile_lo * BN, un0);
+            __syncthreads();                               // K slot 0 is refilled in iteration 0
+            auto step = [&](int it, floatx16 (&sc)[KT][QG], floatx16 (&sn)[KT][QG], bool (&un_n)[QG])
+                __attribute__((always_inline)) {
+                load_k(min(tile_lo + it + 2, tile_hi));    // past the end: harmless repeats
+                load_v(min(tile_lo + it + 1, tile_hi));
+                __builtin_amdgcn_sched_barrier(0);         // keep the loads ahead of the compute
+                record_unset(un_n);
+                qk(sn, Ks[(it + 1) & 1], nref);            // the last iteration's is unused
+                softmax_pv(sc, Vs[it & 1]);
+                __builtin_amdgcn_sched_barrier(0);         // stores after the compute
+                store_k(it & 1);
+                store_v((it + 1) & 1);
+                __syncthreads();
+                if (it + 1 < ntiles) fix_tile(sn, (tile_lo + it + 1) * BN, un_n);
+            };
+            for (int it = 0; it < ntiles; it += 2) {
+                step(it, s0, s1, un1);
+                if (it + 1 < ntiles) step(it + 1, s1, s0, un0);
+            }
         }
 
         // an overflow anywhere shows up as a non-finite l or O
@@ -673,7 +756,7 @@ void prefill_group_kernel(AttnArgs a) {
 
 hipError_t launch_prefill(const AttnArgs& a, int dtype, hipStream_t stream) {
     if (dtype == 1)
-        hipLaunchKernelGGL((prefill_group_kernel<MUSE_PREFILL_QG, MUSE_PREFILL_WPB>),
+        hipLaunchKernelGGL((prefill_group_kernel<MUSE_PREFILL_QG, MUSE_PREFILL_WPB, MUSE_PREFILL_KT, MUSE_PREFILL_PIPE != 0>),
                            dim3((unsigned)prefill_grid_group(a.n_seq, a.n_new, 32 * MUSE_PREFILL_QG, MUSE_PREFILL_WPB)),
                            dim3(64 * MUSE_PREFILL_WPB), 0, stream, a);
     else
