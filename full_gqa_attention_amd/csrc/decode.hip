@@ -9,7 +9,7 @@
 // workgroup owns one (sequence, KV head, split) and computes all 16 heads in
 // a single pass over its rows.
 //
-// Streaming: each wave owns every fourth 16-row sub-tile of the split and
+// Streaming: each of the 8 waves owns every eighth 16-row sub-tile of the split and
 // keeps DEPTH sub-tiles of loads in flight in registers; there is no
 // workgroup barrier inside the loop, so the waves of a CU overlap freely.
 //   * K rows go through a wave-private LDS buffer into the A-operand layout of
@@ -29,7 +29,7 @@
 // rotates the new K, stores K-hat and V to cache row p (Ch 14, 14.7) and
 // substitutes that row in its registers.
 //
-// After the loop the 4 waves merge in LDS; each split writes a partial (max,
+// After the loop the waves merge in LDS; each split writes a partial (max,
 // sum, O); the last split of a (sequence, KV head) to arrive merges all of
 // them and applies the gate (Ch 9, 9.8).  Arrivals are counted in a 64-bit
 // word holding (call tag, count): a word carrying another call's tag counts
@@ -81,7 +81,7 @@ struct SubTile {
 };
 
 template <typename T, int DEPTH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MUSE_DECODE_WAVES, MUSE_DECODE_WAVES)))
+__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(MUSE_DECODE_WAVES, MUSE_DECODE_WAVES)))
 void decode_kernel(DecodeArgs a) {
     using Tr = DecodeTraits<T>;
     constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
@@ -89,8 +89,9 @@ void decode_kernel(DecodeArgs a) {
     constexpr int LDV = Tr::LDV, LDKW = Tr::LDKW, LDQ = D + 4;
     constexpr int ES = (int)sizeof(T);
     constexpr int WAVE_V = SUB * LDV * ES, WAVE_K = SUB * LDKW * ES;
-    constexpr int LOOP_BYTES = 4 * (WAVE_V + WAVE_K) + HG * LDQ * 4;
-    constexpr int MERGE_BYTES = 4 * HG * (D + 2) * 4;
+    constexpr int NW = kDecodeWaves, NT = 64 * NW;
+    constexpr int LOOP_BYTES = NW * (WAVE_V + WAVE_K) + HG * LDQ * 4;
+    constexpr int MERGE_BYTES = NW * HG * (D + 2) * 4;
     constexpr int LDS_BYTES = LOOP_BYTES > MERGE_BYTES ? LOOP_BYTES : MERGE_BYTES;
     // per-wave V (and f32 K) buffers and the f32 Q-hat; the 4-wave merge after the loop
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
@@ -110,7 +111,7 @@ void decode_kernel(DecodeArgs a) {
 
     if (L < 0 || L > a.max_seq_len) {                  // refused on the device
         if (c == 0)
-            for (int i = tid; i < HG * D; i += 256) ((T*)a.out)[obase + i] = from_f32<T>(__builtin_nanf(""));
+            for (int i = tid; i < HG * D; i += NT) ((T*)a.out)[obase + i] = from_f32<T>(__builtin_nanf(""));
         return;
     }
     const int64_t p = L;
@@ -121,12 +122,12 @@ void decode_kernel(DecodeArgs a) {
     const int n_live = (int)((p - lo) / a.chunk) + 1;       // splits with rows
     const bool owns_p = (ce == p + 1);
     const int n_sub = (int)((ce - cs + SUB - 1) / SUB);
-    const int my_cnt = n_sub > wave ? (n_sub - wave + 3) / 4 : 0;  // sub-tiles wave, wave+4, ...
+    const int my_cnt = n_sub > wave ? (n_sub - wave + NW - 1) / NW : 0;  // sub-tiles wave, wave+NW, ...
 
     char* wave_lds = lds + wave * (WAVE_V + WAVE_K);
     T* Vw = (T*)wave_lds;
     T* Kw = (T*)(wave_lds + WAVE_V);
-    float* Qf = (float*)(lds + 4 * (WAVE_V + WAVE_K));
+    float* Qf = (float*)(lds + NW * (WAVE_V + WAVE_K));
 
     // ---- loads of one 16-row sub-tile.  Every lane always loads (a load
     // skipped by some waves would make the compiler wait for all of them):
@@ -138,7 +139,7 @@ void decode_kernel(DecodeArgs a) {
     const char* gv = (const char*)a.cache_v + ((int64_t)s * a.capacity * kKvHeads + g) * D * ES;
     auto clamp_row = [&](int64_t j) __attribute__((always_inline)) { return j < ce ? j : ce - 1; };
     auto issue = [&](SubTile<T>& t, int k) __attribute__((always_inline)) {
-        const int64_t j0 = cs + (int64_t)SUB * (wave + 4 * k);
+        const int64_t j0 = cs + (int64_t)SUB * (wave + NW * k);
         if constexpr (kBf16) {
             // K and V: rows 4u + lane/16, 16-B chunk lane%16 (whole 256-B rows per
             // 16 lanes; loading K straight into the MFMA layout, 64 B from each of
@@ -179,8 +180,8 @@ void decode_kernel(DecodeArgs a) {
         if (a.rope) rope_sincos(a.theta, lane, p, sn, cs_);
         const T* q = (const T*)a.q + obase;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int hh = wave * 4 + i;
+        for (int i = 0; i < HG / NW; ++i) {
+            const int hh = wave * (HG / NW) + i;
             float y0, y1;
             norm_rope_pair(to_f32(q[hh * D + 2 * lane]), to_f32(q[hh * D + 2 * lane + 1]), a.eps,
                            a.q_gain, a.rope, sn, cs_, y0, y1);
@@ -241,7 +242,7 @@ void decode_kernel(DecodeArgs a) {
     float m_run = kNegInf, l_run = 0.0f;
 
     auto process = [&](SubTile<T>& t, int k) __attribute__((always_inline)) {
-        const int64_t j0 = cs + (int64_t)SUB * (wave + 4 * k);
+        const int64_t j0 = cs + (int64_t)SUB * (wave + NW * k);
         // ---- scores S^T[key j0 + 4*q4 + i][head l16]
         floatx4 sc = floatx4{};
         if constexpr (kBf16) {
@@ -345,7 +346,7 @@ void decode_kernel(DecodeArgs a) {
         if constexpr (DEPTH > 7) stage(b7, k0 + 7);
     }
 
-    // ---- merge the 4 waves: LDS holds per wave [16 heads][128 + 2] floats
+    // ---- merge the waves: LDS holds per wave [16 heads][128 + 2] floats
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
     __syncthreads();
@@ -363,14 +364,14 @@ void decode_kernel(DecodeArgs a) {
     const T* gate = (const T*)a.gate + obase;
     T* out = (T*)a.out + obase;
     const int64_t pbase = ((int64_t)s * kHeads + g * HG) * a.nsplit + c;   // head 16g, split c
-    for (int i = tid; i < HG * D; i += 256) {
+    for (int i = tid; i < HG * D; i += NT) {
         const int hh = i / D, d = i % D;
         float M = kNegInf;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, mg[(w * HG + hh) * (D + 2) + D]);
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, mg[(w * HG + hh) * (D + 2) + D]);
         float acc = 0.0f, den = 0.0f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < NW; ++w) {
             const float* row = mg + (w * HG + hh) * (D + 2);
             const float e = (row[D] == kNegInf) ? 0.0f : fast_exp2(row[D] - M);
             acc += row[d] * e;
@@ -395,12 +396,13 @@ void decode_kernel(DecodeArgs a) {
     // count, and the merging split reads them with agent-coherent loads.  No
     // agent-scope fence is used: on this GPU one writes back / invalidates
     // the whole L2 of an XCD, which costs more than the attention itself.
-    // thread -> (head hh, 8 consecutive dims) in the final merge; its gate
+    // thread -> (head hh, DPT consecutive dims) in the final merge; its gate
     // values are read now, so that the merging split does not wait for them
-    const int hh = tid >> 4, d0 = (tid & 15) * 8;
-    float gsig[8];
+    constexpr int TPH = NT / HG, DPT = D / TPH;        // threads per head, dims per thread
+    const int hh = tid / TPH, d0 = (tid % TPH) * DPT;
+    float gsig[DPT];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) gsig[x] = sigmoid(to_f32(gate[hh * D + d0 + x]));
+    for (int x = 0; x < DPT; ++x) gsig[x] = sigmoid(to_f32(gate[hh * D + d0 + x]));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
@@ -429,21 +431,23 @@ void decode_kernel(DecodeArgs a) {
     // online merge of the splits' partials, four per round of loads
     const int64_t hb = ((int64_t)s * kHeads + g * HG + hh) * a.nsplit;
     float M = kNegInf, den = 0.0f;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float acc[DPT];
+#pragma unroll
+    for (int x = 0; x < DPT; ++x) acc[x] = 0.0f;
     for (int c0 = 0; c0 < n_live; c0 += 4) {
-        float pm[4], pl[4], po[4][8];
+        float pm[4], pl[4], po[4][DPT];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int cc = c0 + j;
             pm[j] = kNegInf;
             pl[j] = 0.0f;
 #pragma unroll
-            for (int x = 0; x < 8; ++x) po[j][x] = 0.0f;
+            for (int x = 0; x < DPT; ++x) po[j][x] = 0.0f;
             if (cc < n_live) {
                 pm[j] = observe(a.part_m + hb + cc);
                 pl[j] = observe(a.part_l + hb + cc);
 #pragma unroll
-                for (int x = 0; x < 8; ++x) po[j][x] = observe(a.part_o + (hb + cc) * D + d0 + x);
+                for (int x = 0; x < DPT; ++x) po[j][x] = observe(a.part_o + (hb + cc) * D + d0 + x);
             }
         }
         float Mn = M;
@@ -452,23 +456,23 @@ void decode_kernel(DecodeArgs a) {
         const float rs = fast_exp2(M - Mn);                   // 0 on the first round
         den *= rs;
 #pragma unroll
-        for (int x = 0; x < 8; ++x) acc[x] *= rs;
+        for (int x = 0; x < DPT; ++x) acc[x] *= rs;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float e = fast_exp2(pm[j] - Mn);            // 0 for the padding entries
             den += pl[j] * e;
 #pragma unroll
-            for (int x = 0; x < 8; ++x) acc[x] += po[j][x] * e;
+            for (int x = 0; x < DPT; ++x) acc[x] += po[j][x] * e;
         }
         M = Mn;
     }
     const float inv = 1.0f / den;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) out[hh * D + d0 + x] = from_f32<T>(acc[x] * inv * gsig[x]);
+    for (int x = 0; x < DPT; ++x) out[hh * D + d0 + x] = from_f32<T>(acc[x] * inv * gsig[x]);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.n_seq * kKvHeads * a.nsplit)), block(256);
+    const dim3 grid((unsigned)(a.n_seq * kKvHeads * a.nsplit)), block(64 * kDecodeWaves);
     if (dtype == 1)
         hipLaunchKernelGGL((decode_kernel<bf16_t, MUSE_DECODE_DEPTH>), grid, block, 0, stream, a);
     else

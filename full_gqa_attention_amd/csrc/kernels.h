@@ -84,7 +84,8 @@ struct DecodeArgs {
 // Launch geometry shared by the host code and the kernels.
 constexpr int kPrefillBM = 128;  // query rows per prefill workgroup (4 waves x 32)
 constexpr int kPrefillBN = 64;   // keys per prefill tile
-constexpr int kDecodeTile = 64;  // keys per decode tile (4 waves x 16)
+constexpr int kDecodeTile = 64;  // split granularity of the decode (keys)
+constexpr int kDecodeWaves = 8;  // waves per decode workgroup (two per SIMD)
 
 int prefill_grid(int n_seq, int n_new);
 

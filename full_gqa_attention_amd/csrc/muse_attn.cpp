@@ -61,7 +61,7 @@ muse_status check_sizes(int32_t n_seq, int32_t n_new, int32_t max_seq_len) {
 int64_t decode_target_blocks() {
     const char* e = std::getenv("MUSE_DECODE_TARGET_BLOCKS");
     const long v = e ? std::strtol(e, nullptr, 10) : 0;
-    return v > 0 ? v : 256;
+    return v > 0 ? v : 256;                            // one workgroup per CU
 }
 
 // Decode split: about decode_target_blocks() workgroups in total, chunks a
