@@ -363,13 +363,13 @@ void decode_kernel(DecodeArgs a) {
     __syncthreads();
     const T* gate = (const T*)a.gate + obase;
     T* out = (T*)a.out + obase;
-    const int64_t pbase = ((int64_t)s * kHeads + g * HG) * a.nsplit + c;   // head 16g, split c
-    for (int i = tid; i < HG * D; i += NT) {
-        const int hh = i / D, d = i % D;
-        float M = kNegInf;
+    // this split's partial for (head hh, dim d) from the waves' rows in LDS
+    auto split_partial = [&](int hh, int d, float& M, float& den) __attribute__((always_inline)) {
+        M = kNegInf;
 #pragma unroll
         for (int w = 0; w < NW; ++w) M = fmaxf(M, mg[(w * HG + hh) * (D + 2) + D]);
-        float acc = 0.0f, den = 0.0f;
+        float acc = 0.0f;
+        den = 0.0f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             const float* row = mg + (w * HG + hh) * (D + 2);
@@ -377,34 +377,32 @@ void decode_kernel(DecodeArgs a) {
             acc += row[d] * e;
             den += row[D + 1] * e;
         }
-        if (n_live == 1) {                             // the only split: finish here
+        return acc;
+    };
+    if (n_live == 1) {                                 // the only split: finish here
+        for (int i = tid; i < HG * D; i += NT) {
+            float M, den;
+            const float acc = split_partial(i / D, i % D, M, den);
             out[i] = from_f32<T>(acc / den * sigmoid(to_f32(gate[i])));
-        } else {
-            const int64_t pi = pbase + (int64_t)hh * a.nsplit;
-            publish(a.part_o + pi * D + d, acc);
-            if (d == 0) {
-                publish(a.part_m + pi, M);
-                publish(a.part_l + pi, den);
-            }
         }
+        return;
     }
-    if (n_live == 1) return;
 
-    // ---- arrival; the last split merges every split's partial.  The
-    // partials were written with agent-coherent stores (see publish); waiting
-    // for them to complete before the barrier orders them before the arrival
-    // count, and the merging split reads them with agent-coherent loads.  No
+    // ---- several splits.  Each split first counts its arrival: the last one
+    // merges, and it does not publish its own partial.  The others publish
+    // (m, l, O) with agent-coherent stores, wait for them to complete, then
+    // set their ready word to this call's tag; the merging split waits for
+    // those words (every other split has already arrived, so they are
+    // running) and reads the partials with agent-coherent loads.  No
     // agent-scope fence is used: on this GPU one writes back / invalidates
     // the whole L2 of an XCD, which costs more than the attention itself.
-    // thread -> (head hh, DPT consecutive dims) in the final merge; its gate
-    // values are read now, so that the merging split does not wait for them
+    // Thread -> (head hh, DPT consecutive dims) in the final merge; its gate
+    // values are read now, so that the merging split does not wait for them.
     constexpr int TPH = NT / HG, DPT = D / TPH;        // threads per head, dims per thread
     const int hh = tid / TPH, d0 = (tid % TPH) * DPT;
     float gsig[DPT];
 #pragma unroll
     for (int x = 0; x < DPT; ++x) gsig[x] = sigmoid(to_f32(gate[hh * D + d0 + x]));
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
     if (tid == 0) {
         unsigned long long* word = a.arrivals + (s * kKvHeads + g);
         // first attempt assumes this split is the last to arrive: right for the
@@ -426,10 +424,55 @@ void decode_kernel(DecodeArgs a) {
                                __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    if (!last_flag) return;
+    unsigned int* ready = a.ready + (int64_t)(s * kKvHeads + g) * a.nsplit;
+    const int64_t pbase = ((int64_t)s * kHeads + g * HG) * a.nsplit + c;   // head 16g, split c
+    if (!last_flag) {
+        for (int i = tid; i < HG * D; i += NT) {
+            const int h2 = i / D, d = i % D;
+            float M, den;
+            const float acc = split_partial(h2, d, M, den);
+            const int64_t pi = pbase + (int64_t)h2 * a.nsplit;
+            publish(a.part_o + pi * D + d, acc);
+            if (d == 0) {
+                publish(a.part_m + pi, M);
+                publish(a.part_l + pi, den);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);                 // the partial is stored before it is marked ready
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(ready + c, a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
 
-    // online merge of the splits' partials, four per round of loads
+    // ---- the merging split: wait (bounded) for the other splits' partials
+    if (tid == 0) last_flag = 1;                       // reused below as "all ready"
+    __syncthreads();
+    for (int cc = tid; cc < n_live; cc += NT) {
+        if (cc == c) continue;
+        int spins = 0;
+        while (__hip_atomic_load(ready + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.tag) {
+            if (++spins > kDecodeReadySpins) {
+                last_flag = 0;                         // give up: the output becomes NaN
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        // consumed: cleared for the next call or graph replay
+        __hip_atomic_store(ready + cc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!last_flag) {
+#pragma unroll
+        for (int x = 0; x < DPT; ++x) out[hh * D + d0 + x] = from_f32<T>(__builtin_nanf(""));
+        return;
+    }
+
+    // online merge in split order (the result does not depend on which split
+    // merges): this split's partial from LDS, the others four per round of loads
     const int64_t hb = ((int64_t)s * kHeads + g * HG + hh) * a.nsplit;
+    float own_m, own_l, own_o[DPT];
+#pragma unroll
+    for (int x = 0; x < DPT; ++x) own_o[x] = split_partial(hh, d0 + x, own_m, own_l);
     float M = kNegInf, den = 0.0f;
     float acc[DPT];
 #pragma unroll
@@ -443,7 +486,12 @@ void decode_kernel(DecodeArgs a) {
             pl[j] = 0.0f;
 #pragma unroll
             for (int x = 0; x < DPT; ++x) po[j][x] = 0.0f;
-            if (cc < n_live) {
+            if (cc == c) {
+                pm[j] = own_m;
+                pl[j] = own_l;
+#pragma unroll
+                for (int x = 0; x < DPT; ++x) po[j][x] = own_o[x];
+            } else if (cc < n_live) {
                 pm[j] = observe(a.part_m + hb + cc);
                 pl[j] = observe(a.part_l + hb + cc);
 #pragma unroll

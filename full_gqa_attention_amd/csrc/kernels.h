@@ -78,6 +78,7 @@ struct DecodeArgs {
     float* part_m;          // [S][32][nsplit] partial maxima (log2 domain)
     float* part_l;          // [S][32][nsplit] partial softmax denominators
     unsigned long long* arrivals;  // [S][2] (tag << 32 | splits arrived)
+    unsigned int* ready;    // [S][2][nsplit] tag of the call whose partial is stored, 0 once merged
     float theta[64];        // f32 RoPE frequency table
 };
 
@@ -86,6 +87,7 @@ constexpr int kPrefillBM = 128;  // query rows per prefill workgroup (4 waves x 
 constexpr int kPrefillBN = 64;   // keys per prefill tile
 constexpr int kDecodeTile = 64;  // split granularity of the decode (keys)
 constexpr int kDecodeWaves = 8;  // waves per decode workgroup (two per SIMD)
+constexpr int kDecodeReadySpins = 1 << 20;  // polls of a ready word before the merge gives up
 
 int prefill_grid(int n_seq, int n_new);
 

@@ -85,9 +85,10 @@ void decode_split(const muse_attn_layer* l, int32_t n_seq, int32_t max_seq_len,
 
 // Prefill: Q-hat [S][N][32][128] (score type, same element size as the layer
 // dtype), then on bf16 layers the fp16 key copy [S][max_seq_len + N][2][128].
-// Decode: arrival words [S][2] (u64), then the split partials.
+// Decode: arrival words [S][2] (u64), ready words [S][2][nsplit] (u32), then the
+// split partials.
 struct WorkspaceLayout {
-    size_t qhat = 0, kq = 0, arrivals = 0, part_o = 0, part_m = 0, part_l = 0, total = 0;
+    size_t qhat = 0, kq = 0, arrivals = 0, ready = 0, part_o = 0, part_m = 0, part_l = 0, total = 0;
     int64_t kq_capacity = 0;
     int32_t chunk = 0, nsplit = 0;
 };
@@ -109,6 +110,8 @@ WorkspaceLayout layout_for(const muse_attn_layer* l, int32_t n_seq, int32_t n_ne
         w.arrivals = 0;
         off = round_up((size_t)n_seq * kKvHeads * sizeof(unsigned long long), kAlign);
         decode_split(l, n_seq, max_seq_len, &w.chunk, &w.nsplit);
+        w.ready = off;
+        off += round_up((size_t)n_seq * kKvHeads * w.nsplit * sizeof(unsigned int), kAlign);
         const size_t parts = (size_t)n_seq * kHeads * w.nsplit;
         w.part_o = off;
         off += round_up(parts * kHeadDim * sizeof(float), kAlign);
@@ -216,6 +219,7 @@ muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, cons
         da.part_m = (float*)(ws + wl.part_m);
         da.part_l = (float*)(ws + wl.part_l);
         da.arrivals = (unsigned long long*)(ws + wl.arrivals);
+        da.ready = (unsigned int*)(ws + wl.ready);
         if (rope) rope_table(layer->rope_theta, da.theta);
         if (timer && hipEventRecord(timer->start, stream) != hipSuccess) return MUSE_ERR_HIP;
         if (muse::launch_decode(da, dt, stream) != hipSuccess) return MUSE_ERR_HIP;
