@@ -151,6 +151,8 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--schedule", action="store_true",
+                    help="also time the 52-layer schedule workload (chunked prefill phase + 256 decode steps)")
     ap.add_argument("--eager", action="store_true",
                     help="time decode steps as eager calls only (no HIP graph), e.g. under counter collection")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -160,6 +162,12 @@ def parse():
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT", "COMMAND"),
                     help="write the decode kernel's HBM-traffic summary from two --pmc runs and exit")
     return ap.parse_args()
+
+
+def percentiles(xs):
+    """p10, p50, p90 (nearest rank) of a list of launch times."""
+    v = sorted(xs)
+    return [v[min(len(v) - 1, int(q * len(v)))] for q in (0.1, 0.5, 0.9)]
 
 
 def log(msg):
@@ -254,7 +262,8 @@ def bench_decode(w, args, fa, synth, torch):
         b = kv_row_bytes(w.dtype) * w.n_seq * visible_rows(r.spec, w.prefix)
         per_layer[r.spec.name] = {"kernel_us": round(1e3 * sum(lt) / len(lt), 2),
                                   "kv_MB": round(b / 1e6, 3),
-                                  "kernel_GBps": round(b / (sum(lt) / len(lt) * 1e-3) / 1e9, 1)}
+                                  "kernel_GBps": round(b / (sum(lt) / len(lt) * 1e-3) / 1e9, 1),
+                                  "p10_p50_p90_us": [round(1e3 * x, 2) for x in percentiles(lt)]}
     res = {
         "value": kv_per_step / (ms_per_step * 1e-3) / 1e9,
         "ms_per_step": ms_per_step,
@@ -290,7 +299,8 @@ def bench_prefill(w, steps, warmup, fa, synth, torch):
         f = FLOP_PER_PAIR * w.n_seq * prefill_pairs(r.spec, w.prefix, w.n_new)
         avg = sum(lt) / len(lt)
         per_layer[r.spec.name] = {"kernel_ms": round(avg, 4), "tflop": round(f / 1e12, 4),
-                                  "kernel_TFLOPs": round(f / (avg * 1e-3) / 1e12, 1)}
+                                  "kernel_TFLOPs": round(f / (avg * 1e-3) / 1e12, 1),
+                                  "p10_p50_p90_ms": [round(x, 4) for x in percentiles(lt)]}
     kern = sum(per_launch) / len(per_launch)
     achieved = flops_step / len(runs) / (kern * 1e-3) / 1e12
     return {
@@ -304,6 +314,74 @@ def bench_prefill(w, steps, warmup, fa, synth, torch):
                      "per_layer": per_layer},
         "flop_per_step": flops_step, "steps": steps, "warmup": warmup,
     }
+
+
+def bench_schedule(w, fa, synth, torch):
+    """The 52-layer schedule workload: 4 sequences with 32,768 cached rows per
+    layer, a 4,096-token chunked prefill through all 52 layers (timed as one
+    phase, eager calls), then 256 decode steps of all 52 layers (one step =
+    52 decode calls and the seq_len increment, replayed from a HIP graph)."""
+    S, L0, N, steps = w.n_seq, w.prefix, w.n_new, w.decode_steps
+    extra = 4                                          # warm-up decode steps, rows overwritten later
+    cap = L0 + N + steps + extra
+    max_dec = L0 + N + steps + extra - 1
+    log(f"schedule {w.name}: {len(w.layers)} layers, capacity {cap}")
+    layers, inputs, outs, dec_in = [], [], [], []
+    for spec in w.layers:
+        inp = synth.layer_inputs(w, spec, device="cuda", backend="torch", capacity=cap)
+        layers.append(fa.make_layer(spec.kind, window=spec.window, rope_theta=spec.rope_theta,
+                                    rms_eps=spec.rms_eps, q_norm_gain=spec.q_gain,
+                                    k_norm_gain=spec.k_gain, attn_scale=spec.scale, dtype=w.dtype))
+        inputs.append(inp)
+        outs.append(torch.empty_like(inp.gate))
+        d = synth.layer_inputs(w, spec, device="cuda", backend="torch", n_new=1, prefix=0,
+                               step=1, with_cache=False)
+        dec_in.append((d.q, d.k, d.v, d.gate, torch.empty_like(d.gate)))
+    seq_len = torch.full((S,), L0, dtype=torch.int32, device="cuda")
+    ws_p = fa.workspace(layers[0], S, N, L0, False)
+    ws_d = torch.empty(max(fa.workspace_size(lay, S, 1, max_dec, True) for lay in layers),
+                       dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for lay, inp, out in zip(layers, inputs, outs):
+        fa.prefill(lay, inp.q, inp.k, inp.v, inp.gate, inp.cache_k, inp.cache_v, seq_len, out,
+                   max_seq_len=L0, workspace=ws_p)
+    torch.cuda.synchronize()
+    t_prefill = time.perf_counter() - t0
+    flops = sum(FLOP_PER_PAIR * S * prefill_pairs(spec, L0, N) for spec in w.layers)
+    seq_len.fill_(L0 + N)
+
+    def one_step():
+        for lay, inp, (q, k, v, g, o) in zip(layers, inputs, dec_in):
+            fa.decode(lay, q, k, v, g, inp.cache_k, inp.cache_v, seq_len, o, max_seq_len=max_dec,
+                      workspace=ws_d)
+        seq_len.add_(1)
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_step()
+    for _ in range(extra):
+        graph.replay()
+    torch.cuda.synchronize()
+    seq_len.fill_(L0 + N)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    t_decode = time.perf_counter() - t0
+    kv = sum(kv_row_bytes(w.dtype) * S * visible_rows(spec, L0 + N + i)
+             for i in range(steps) for spec in w.layers)
+    del graph
+    return {"workload": w.name, "layers": len(w.layers), "n_seq": S,
+            "prefill": {"tokens_per_seq": N, "at_position": L0, "ms": round(t_prefill * 1e3, 2),
+                        "tflop": round(flops / 1e12, 3), "TFLOPs": round(flops / t_prefill / 1e12, 1),
+                        "frac_mfma_peak": round(flops / t_prefill / 1e12 / MFMA_PEAK_TFLOPS, 4),
+                        "launch": "eager"},
+            "decode": {"steps": steps, "ms": round(t_decode * 1e3, 2), "kv_GB": round(kv / 1e9, 2),
+                       "GBps": round(kv / t_decode / 1e9, 1),
+                       "frac_hbm_peak": round(kv / t_decode / 1e9 / HBM_PEAK_GBS, 4),
+                       "launch": "each step (52 decode calls + seq_len increment) replayed from a HIP graph"}}
 
 
 def cpu_baseline_decode(w, runs, synth, torch):
@@ -391,6 +469,9 @@ def main():
     if not args.no_prefill:
         pw = synth.WORKLOADS[args.prefill_workload]
         line["prefill"] = bench_prefill(pw, args.prefill_steps, 2, fa, synth, torch)
+    if args.schedule:
+        torch.cuda.empty_cache()
+        line["schedule"] = bench_schedule(synth.WORKLOADS["schedule_52x4_32768p4096_256d"], fa, synth, torch)
     print(json.dumps(line), flush=True)
 
 

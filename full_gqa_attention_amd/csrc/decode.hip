@@ -91,7 +91,7 @@ void decode_kernel(DecodeArgs a) {
     constexpr int WAVE_V = SUB * LDV * ES, WAVE_K = SUB * LDKW * ES;
     constexpr int NW = kDecodeWaves, NT = 64 * NW;
     constexpr int LOOP_BYTES = NW * (WAVE_V + WAVE_K) + HG * LDQ * 4;
-    constexpr int MERGE_BYTES = NW * HG * (D + 2) * 4;
+    constexpr int MERGE_BYTES = NW * HG * (D + 2) * 4 + HG * kMaxSplits * 4;
     constexpr int LDS_BYTES = LOOP_BYTES > MERGE_BYTES ? LOOP_BYTES : MERGE_BYTES;
     // per-wave V (and f32 K) buffers and the f32 Q-hat; the 4-wave merge after the loop
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
@@ -404,24 +404,40 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int x = 0; x < DPT; ++x) gsig[x] = sigmoid(to_f32(gate[hh * D + d0 + x]));
     if (tid == 0) {
-        unsigned long long* word = a.arrivals + (s * kKvHeads + g);
-        // first attempt assumes this split is the last to arrive: right for the
-        // split whose merge ends the call, one round trip saved
-        unsigned long long old = ((unsigned long long)a.tag << 32) | (unsigned int)(n_live - 1);
-        unsigned int arrived = 0;
-        for (;;) {                                     // retries only on contention
-            const unsigned int cnt = ((unsigned int)(old >> 32) == a.tag) ? (unsigned int)old : 0u;
-            const unsigned long long want = ((unsigned long long)a.tag << 32) | (cnt + 1);
-            if (__hip_atomic_compare_exchange_strong(word, &old, want, __ATOMIC_RELAXED,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-                arrived = cnt + 1;
-                break;
+        // count this split's arrival on a tagged word (tag << 32 | count); true
+        // for the arrival that completes n, which resets the word for a replay
+        // with the same tag.  The first attempt assumes it completes n: right
+        // for the split whose merge ends the call, one round trip saved.
+        auto arrive = [&](unsigned long long* word, int n) {
+            unsigned long long old = ((unsigned long long)a.tag << 32) | (unsigned int)(n - 1);
+            unsigned int arrived = 0;
+            for (;;) {                                 // retries only on contention
+                const unsigned int cnt = ((unsigned int)(old >> 32) == a.tag) ? (unsigned int)old : 0u;
+                const unsigned long long want = ((unsigned long long)a.tag << 32) | (cnt + 1);
+                if (__hip_atomic_compare_exchange_strong(word, &old, want, __ATOMIC_RELAXED,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                    arrived = cnt + 1;
+                    break;
+                }
             }
+            const bool done = arrived == (unsigned int)n;
+            if (done)
+                __hip_atomic_store(word, (unsigned long long)a.tag << 32, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            return done;
+        };
+        // Many splits arriving on one word serialise on its compare-and-swap, so
+        // they count in groups of kArriveGroup first; the last of each group then
+        // arrives on the (sequence, KV head) word.
+        unsigned long long* words = a.arrivals + (int64_t)(s * kKvHeads + g) * kArriveWords;
+        const int n_grps = (n_live + kArriveGroup - 1) / kArriveGroup;
+        bool last = true;
+        if (n_grps > 1) {
+            const int grp = c / kArriveGroup;
+            last = arrive(words + 1 + grp, min(kArriveGroup, n_live - grp * kArriveGroup));
         }
-        last_flag = (arrived == (unsigned int)n_live);
-        if (last_flag)                                 // ready for a replay with the same tag
-            __hip_atomic_store(word, (unsigned long long)a.tag << 32, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+        if (last) last = arrive(words, n_grps > 1 ? n_grps : n_live);
+        last_flag = last;
     }
     __syncthreads();
     unsigned int* ready = a.ready + (int64_t)(s * kKvHeads + g) * a.nsplit;
@@ -467,52 +483,73 @@ void decode_kernel(DecodeArgs a) {
         return;
     }
 
-    // online merge in split order (the result does not depend on which split
-    // merges): this split's partial from LDS, the others four per round of loads
+    // ---- merge (the result does not depend on which split merges).
+    // Phase 1: thread (head hh, lane k of the head's TPH threads) reads (m, l)
+    // of splits k, k + TPH, ... in one round of loads; the head's maximum and
+    // denominator come from a reduction over those TPH lanes (one wave half),
+    // and each split's weight exp2(m_c - M) goes to LDS.
+    static_assert(TPH == 32, "one head per half wave in the merge");
+    float* wts = (float*)lds + NW * HG * (D + 2);      // [16 heads][kMaxSplits] after the wave rows
+    const int k = tid % TPH;
     const int64_t hb = ((int64_t)s * kHeads + g * HG + hh) * a.nsplit;
     float own_m, own_l, own_o[DPT];
 #pragma unroll
     for (int x = 0; x < DPT; ++x) own_o[x] = split_partial(hh, d0 + x, own_m, own_l);
-    float M = kNegInf, den = 0.0f;
+    float pm[kMaxSplits / TPH], pl[kMaxSplits / TPH];
+    float M = kNegInf;
+#pragma unroll
+    for (int j = 0; j < kMaxSplits / TPH; ++j) {
+        const int cc = k + TPH * j;
+        pm[j] = kNegInf;
+        pl[j] = 0.0f;
+        if (cc == c) {
+            pm[j] = own_m;
+            pl[j] = own_l;
+        } else if (cc < n_live) {
+            pm[j] = observe(a.part_m + hb + cc);
+            pl[j] = observe(a.part_l + hb + cc);
+        }
+        M = fmaxf(M, pm[j]);
+    }
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));   // within the half wave
+    float den = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxSplits / TPH; ++j) {
+        const int cc = k + TPH * j;
+        const float e = fast_exp2(pm[j] - M);          // 0 past n_live
+        if (cc < n_live) wts[hh * kMaxSplits + cc] = e;
+        den += pl[j] * e;
+    }
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) den += __shfl_xor(den, o, 64);
+    __syncthreads();
+    // Phase 2: O = sum_c w_c O_c over the splits, eight splits per round of loads
     float acc[DPT];
 #pragma unroll
     for (int x = 0; x < DPT; ++x) acc[x] = 0.0f;
-    for (int c0 = 0; c0 < n_live; c0 += 4) {
-        float pm[4], pl[4], po[4][DPT];
+    for (int c0 = 0; c0 < n_live; c0 += 8) {
+        float po[8][DPT];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 8; ++j) {
             const int cc = c0 + j;
-            pm[j] = kNegInf;
-            pl[j] = 0.0f;
 #pragma unroll
             for (int x = 0; x < DPT; ++x) po[j][x] = 0.0f;
             if (cc == c) {
-                pm[j] = own_m;
-                pl[j] = own_l;
 #pragma unroll
                 for (int x = 0; x < DPT; ++x) po[j][x] = own_o[x];
             } else if (cc < n_live) {
-                pm[j] = observe(a.part_m + hb + cc);
-                pl[j] = observe(a.part_l + hb + cc);
 #pragma unroll
                 for (int x = 0; x < DPT; ++x) po[j][x] = observe(a.part_o + (hb + cc) * D + d0 + x);
             }
         }
-        float Mn = M;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Mn = fmaxf(Mn, pm[j]);   // finite: split c0 has rows
-        const float rs = fast_exp2(M - Mn);                   // 0 on the first round
-        den *= rs;
-#pragma unroll
-        for (int x = 0; x < DPT; ++x) acc[x] *= rs;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float e = fast_exp2(pm[j] - Mn);            // 0 for the padding entries
-            den += pl[j] * e;
+        for (int j = 0; j < 8; ++j) {
+            const int cc = c0 + j;
+            const float e = cc < n_live ? wts[hh * kMaxSplits + cc] : 0.0f;
 #pragma unroll
             for (int x = 0; x < DPT; ++x) acc[x] += po[j][x] * e;
         }
-        M = Mn;
     }
     const float inv = 1.0f / den;
 #pragma unroll

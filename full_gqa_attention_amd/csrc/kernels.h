@@ -77,7 +77,7 @@ struct DecodeArgs {
     float* part_o;          // [S][32][nsplit][128] unnormalised partial outputs
     float* part_m;          // [S][32][nsplit] partial maxima (log2 domain)
     float* part_l;          // [S][32][nsplit] partial softmax denominators
-    unsigned long long* arrivals;  // [S][2] (tag << 32 | splits arrived)
+    unsigned long long* arrivals;  // [S][2][kArriveWords] (tag << 32 | arrivals): the pair, then groups
     unsigned int* ready;    // [S][2][nsplit] tag of the call whose partial is stored, 0 once merged
     float theta[64];        // f32 RoPE frequency table
 };
@@ -88,6 +88,9 @@ constexpr int kPrefillBN = 64;   // keys per prefill tile
 constexpr int kDecodeTile = 64;  // split granularity of the decode (keys)
 constexpr int kDecodeWaves = 8;  // waves per decode workgroup (two per SIMD)
 constexpr int kDecodeReadySpins = 1 << 20;  // polls of a ready word before the merge gives up
+constexpr int kMaxSplits = 128;  // decode splits per (sequence, KV head), at most
+constexpr int kArriveGroup = 8;   // decode splits counted per group word
+constexpr int kArriveWords = 1 + kMaxSplits / kArriveGroup;  // arrival words per (sequence, KV head)
 
 int prefill_grid(int n_seq, int n_new);
 

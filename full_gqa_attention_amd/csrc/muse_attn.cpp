@@ -64,9 +64,18 @@ int64_t decode_target_blocks() {
     return v > 0 ? v : 256;                            // one workgroup per CU
 }
 
+int64_t decode_min_split_rows() {
+    const char* e = std::getenv("MUSE_DECODE_MIN_SPLIT_ROWS");
+    const long v = e ? std::strtol(e, nullptr, 10) : 0;
+    return v > 0 ? v : 512;
+}
+
 // Decode split: about decode_target_blocks() workgroups in total, chunks a
-// multiple of the 64-row tile.  The span of visible rows is at most window
-// (sliding) or max_seq_len + 1 (full).
+// multiple of the 64-row tile and (when the span allows) of at least
+// decode_min_split_rows() rows: a split costs a fixed few microseconds (its
+// first loads, its partial and the merge), which short splits do not repay.
+// The span of visible rows is at most window (sliding) or max_seq_len + 1
+// (full).
 void decode_split(const muse_attn_layer* l, int32_t n_seq, int32_t max_seq_len,
                   int32_t* chunk, int32_t* nsplit) {
     int64_t span = (int64_t)max_seq_len + 1;
@@ -75,7 +84,10 @@ void decode_split(const muse_attn_layer* l, int32_t n_seq, int32_t max_seq_len,
     const int64_t target = decode_target_blocks();
     int64_t want = (target + pairs - 1) / pairs;
     const int64_t tiles = (span + muse::kDecodeTile - 1) / muse::kDecodeTile;
+    const int64_t by_rows = span / decode_min_split_rows();
+    if (want > by_rows) want = by_rows;
     if (want > tiles) want = tiles;
+    if (want > muse::kMaxSplits) want = muse::kMaxSplits;
     if (want < 1) want = 1;
     int64_t ch = (span + want - 1) / want;
     ch = (ch + muse::kDecodeTile - 1) / muse::kDecodeTile * muse::kDecodeTile;
@@ -85,8 +97,8 @@ void decode_split(const muse_attn_layer* l, int32_t n_seq, int32_t max_seq_len,
 
 // Prefill: Q-hat [S][N][32][128] (score type, same element size as the layer
 // dtype), then on bf16 layers the fp16 key copy [S][max_seq_len + N][2][128].
-// Decode: arrival words [S][2] (u64), ready words [S][2][nsplit] (u32), then the
-// split partials.
+// Decode: arrival words [S][2][kArriveWords] (u64), ready words [S][2][nsplit]
+// (u32), then the split partials.
 struct WorkspaceLayout {
     size_t qhat = 0, kq = 0, arrivals = 0, ready = 0, part_o = 0, part_m = 0, part_l = 0, total = 0;
     int64_t kq_capacity = 0;
@@ -108,7 +120,7 @@ WorkspaceLayout layout_for(const muse_attn_layer* l, int32_t n_seq, int32_t n_ne
         }
     } else {
         w.arrivals = 0;
-        off = round_up((size_t)n_seq * kKvHeads * sizeof(unsigned long long), kAlign);
+        off = round_up((size_t)n_seq * kKvHeads * muse::kArriveWords * sizeof(unsigned long long), kAlign);
         decode_split(l, n_seq, max_seq_len, &w.chunk, &w.nsplit);
         w.ready = off;
         off += round_up((size_t)n_seq * kKvHeads * w.nsplit * sizeof(unsigned int), kAlign);
