@@ -659,21 +659,48 @@ void prefill_group_kernel(AttnArgs a) {
         }
 
         if constexpr (!PIPE) {
-            load_tile(tile_lo, true);
-            store_tile(0, true);
+            // loads run two tiles ahead, alternating between two register sets
+            u32x4 ka[NCH], va[NCH], kb2[NCH], vb2[NCH];
+            auto ld2 = [&](u32x4 (&kr)[NCH], u32x4 (&vr)[NCH], int tile) __attribute__((always_inline)) {
+                const int j0 = tile * BN;
+#pragma unroll
+                for (int u = 0; u < NCH; ++u) {
+                    const int64_t off = (int64_t)min(j0 + r_t + u * RSTEP, kv_end - 1) * ROW;
+                    kr[u] = *(const u32x4*)(kbase + off);
+                    vr[u] = *(const u32x4*)(vbase + off);
+                }
+            };
+            auto st2 = [&](const u32x4 (&kr)[NCH], const u32x4 (&vr)[NCH], int bufi) __attribute__((always_inline)) {
+                char* kd = (char*)Ks[bufi] + r_t * LDK * ES + c_t * 16;
+                char* vd = (char*)Vs[bufi] + r_t * LDV * ES + c_t * 16;
+#pragma unroll
+                for (int u = 0; u < NCH; ++u) {
+                    *(u32x4*)(kd + u * RSTEP * LDK * ES) = kr[u];
+                    *(u32x4*)(vd + u * RSTEP * LDV * ES) = vr[u];
+                }
+            };
+            ld2(ka, va, tile_lo);
+            st2(ka, va, 0);
+            ld2(kb2, vb2, min(tile_lo + 1, tile_hi));
             __syncthreads();
-            for (int it = 0; it < ntiles; ++it) {
+            auto step = [&](int it, u32x4 (&kn)[NCH], u32x4 (&vn)[NCH], u32x4 (&kf)[NCH], u32x4 (&vf)[NCH])
+                __attribute__((always_inline)) {
+                // kn/vn hold tile it+1 (loaded one iteration ago); kf/vf take tile it+2
                 const int cur = it & 1;
-                load_tile(min(tile_lo + it + 1, tile_hi), true);   // in flight during the compute (last: a repeat)
-                __builtin_amdgcn_sched_barrier(0);         // keep the loads ahead of the compute
+                ld2(kf, vf, min(tile_lo + it + 2, tile_hi));
+                __builtin_amdgcn_sched_barrier(0);
                 bool unset[QG];
                 record_unset(unset);
                 floatx16 sc[KT][QG];
                 qk(sc, Ks[cur], nref);
-                store_tile(cur ^ 1, true);                 // that buffer is free since the last barrier
+                st2(kn, vn, cur ^ 1);                      // that buffer is free since the last barrier
                 fix_tile(sc, (tile_lo + it) * BN, unset);
                 softmax_pv(sc, Vs[cur]);
                 __syncthreads();
+            };
+            for (int it = 0; it < ntiles; it += 2) {
+                step(it, kb2, vb2, ka, va);
+                if (it + 1 < ntiles) step(it + 1, ka, va, kb2, vb2);
             }
         } else {
             // K runs one tile ahead of V: iteration it issues the Q.K of tile it+1
