@@ -21,6 +21,7 @@ struct PrepArgs {
     int32_t n_seq;
     int32_t n_new;
     int32_t rope;           // 1: sliding layer (rotate), 0: NoPE
+    int32_t skip_q;         // 1: Q-hat is made by the attention kernel (bf16 layers)
     float eps;
     float q_gain;
     float k_gain;
@@ -36,7 +37,13 @@ struct PrepArgs {
 
 // Kernel (b): prefill attention over the cache with the gate epilogue.
 struct AttnArgs {
-    const void* qhat;       // workspace Q-hat [S][N][32][128], scaled by attn_scale * log2(e)
+    const void* qhat;       // f32 layers: workspace Q-hat [S][N][32][128], scaled by attn_scale * log2(e)
+    const void* q;          // bf16 layers: raw Q [S][N][32][128] (Q-hat is made in the kernel)
+    int32_t rope;           // bf16 layers: 1 on sliding layers (rotate Q)
+    float eps;
+    float q_gain;
+    float q_scale;          // attn_scale * log2(e)
+    float theta[64];        // f32 RoPE frequency table
     const void* gate;       // [S][N][4096]
     void* out;              // [S][N][4096]
     const void* kq;         // keys in the score type [S][kq_capacity][2][128]

@@ -95,8 +95,8 @@ void decode_split(const muse_attn_layer* l, int32_t n_seq, int32_t max_seq_len,
     *nsplit = (int32_t)((span + ch - 1) / ch);
 }
 
-// Prefill: Q-hat [S][N][32][128] (score type, same element size as the layer
-// dtype), then on bf16 layers the fp16 key copy [S][max_seq_len + N][2][128].
+// Prefill: on f32 layers Q-hat [S][N][32][128]; on bf16 layers (where the
+// attention kernel makes Q-hat itself) the fp16 key copy [S][max_seq_len + N][2][128].
 // Decode: arrival words [S][2][kArriveWords] (u64), ready words [S][2][nsplit]
 // (u32), then the split partials.
 struct WorkspaceLayout {
@@ -111,8 +111,9 @@ WorkspaceLayout layout_for(const muse_attn_layer* l, int32_t n_seq, int32_t n_ne
     const size_t es = elem_bytes(l->dtype);
     size_t off = 0;
     if (!decode) {
+        // bf16 layers make Q-hat inside the attention kernel; f32 layers stage it
         w.qhat = 0;
-        off = round_up((size_t)n_seq * n_new * kHeads * kHeadDim * es, kAlign);
+        if (l->dtype != MUSE_BF16) off = round_up((size_t)n_seq * n_new * kHeads * kHeadDim * es, kAlign);
         if (l->dtype == MUSE_BF16) {
             w.kq = off;
             w.kq_capacity = (int64_t)max_seq_len + n_new;
@@ -257,6 +258,7 @@ muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, cons
     pa.q_gain = layer->q_norm_gain;
     pa.k_gain = layer->k_norm_gain;
     pa.q_scale = scale_log2;
+    pa.skip_q = layer->dtype == MUSE_BF16 ? 1 : 0;
     pa.window = rope ? layer->window : 0;
     if (layer->dtype == MUSE_BF16) {
         // prefix rows the chunk can see: [0, L) on full layers, at most
@@ -272,6 +274,12 @@ muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, cons
     AttnArgs aa;
     std::memset(&aa, 0, sizeof aa);
     aa.qhat = pa.qhat;
+    aa.q = q;
+    aa.rope = pa.rope;
+    aa.eps = pa.eps;
+    aa.q_gain = pa.q_gain;
+    aa.q_scale = pa.q_scale;
+    std::memcpy(aa.theta, pa.theta, sizeof aa.theta);
     aa.gate = gate;
     aa.out = out;
     aa.kq = layer->dtype == MUSE_BF16 ? (const void*)(ws + wl.kq) : cache->k;

@@ -423,15 +423,61 @@ void prefill_group_kernel(AttnArgs a) {
         return;
     }
 
-    // ---- Q-hat fragments of the wave's two 32-row groups (B operand of S^T = K Q^T)
+    // ---- Q-hat of the wave's rows (B operand of S^T = K Q^T), made here from the
+    // raw Q: QK-norm with gain ("Chapter 9 - The Muse Glimmer architecture" 9.5;
+    // "Chapter 14 - QK-norm and RoPE" 14.3), RoPE on sliding layers (Ch 14,
+    // 14.4-14.5: angle f32(p) * theta_i in f32, accurate sincosf), then
+    // attn_scale * log2(e), rounded to fp16.  Each (row, head) is made by
+    // exactly one wave, so this costs no more than a separate pass and saves
+    // writing Q-hat to HBM and reading it back.  The workgroup's rows share one
+    // (cos, sin) table in LDS.
+    __shared__ float2 rot[BMW][kHeadDim / 2];
+    if (a.rope) {
+        float th = 0.0f;                               // theta[lane] without indexing the argument block
+#pragma unroll
+        for (int i = 0; i < 64; ++i) th = (lane == i) ? a.theta[i] : th;
+        for (int row = wave; row < BMW; row += WPB) {
+            float sn, cs;
+            sincosf((float)((int64_t)L + q0 + row) * th, &sn, &cs);
+            rot[row][lane] = make_float2(cs, sn);
+        }
+        __syncthreads();
+    }
     FragQ qf[QG][NST];
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
         const int tq = q0 + 32 * qg + l32;
-        const TQ* qrow = (const TQ*)a.qhat + (((int64_t)s * N + tq) * kHeads + h) * D;
+        const bf16_t* qrow = (const bf16_t*)a.q + (((int64_t)s * N + min(tq, N - 1)) * kHeads + h) * D;
+        float x[NST][8];
+        float ss = 0.0f;
 #pragma unroll
-        for (int st = 0; st < NST; ++st)
-            qf[qg][st] = tq < N ? *(const FragQ*)(qrow + 2 * MQ::KPL * st + MQ::KPL * gl) : FragQ{};
+        for (int st = 0; st < NST; ++st) {
+            const bf16x8 raw = *(const bf16x8*)(qrow + 2 * MQ::KPL * st + MQ::KPL * gl);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                x[st][t] = (float)raw[t];
+                ss += x[st][t] * x[st][t];
+            }
+        }
+        ss = sum_halves(ss);                           // the row's other 64 values sit in lane l ^ 32
+        const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+            float y[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) y[t] = (x[st][t] * r) * a.q_gain;
+            if (a.rope) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {          // pair (dims 2i, 2i+1), i = 8 st + 4 gl + j
+                    const float2 c = rot[32 * qg + l32][8 * st + 4 * gl + j];
+                    const float y0 = y[2 * j], y1 = y[2 * j + 1];
+                    y[2 * j] = y0 * c.x - y1 * c.y;
+                    y[2 * j + 1] = y0 * c.y + y1 * c.x;
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) qf[qg][st][t] = (TQ)(tq < N ? y[t] * a.q_scale : 0.0f);
+        }
     }
 
     // ---- keys the workgroup can see (positions fit in int32: bounded by 2^24)

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     __syncthreads();
 
     const int sub = tid & 15;                      // 8 values: dims 8*sub .. 8*sub+7
-    for (int vec = tid >> 4; vec < kHeads + 2 * kKvHeads; vec += 16) {
+    for (int vec = (tid >> 4) + (a.skip_q ? kHeads : 0); vec < kHeads + 2 * kKvHeads; vec += 16) {
         float x[8];
         if (vec >= kHeads + kKvHeads) {            // V: exact copy
             const int g = vec - kHeads - kKvHeads;

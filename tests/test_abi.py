@@ -206,9 +206,10 @@ def test_empty_batches_are_valid_noops(lib):
 
 def test_workspace_sizes():
     lay = fa.make_layer(fa.FULL_NOPE, dtype=fa.BF16)
-    # bf16 prefill: fp16 Q-hat plus an fp16 copy of the keys the chunk can see
-    assert fa.workspace_size(lay, 8, 8192, 0, False) == 8 * 8192 * 4096 * 2 + 8 * 8192 * 256 * 2
-    assert fa.workspace_size(lay, 4, 4096, 32768, False) == 4 * 4096 * 4096 * 2 + 4 * 36864 * 256 * 2
+    # bf16 prefill: an fp16 copy of the keys the chunk can see (Q-hat is made in
+    # the attention kernel); f32 prefill: Q-hat
+    assert fa.workspace_size(lay, 8, 8192, 0, False) == 8 * 8192 * 256 * 2
+    assert fa.workspace_size(lay, 4, 4096, 32768, False) == 4 * 36864 * 256 * 2
     f32 = fa.make_layer(fa.FULL_NOPE, dtype=fa.F32)
     assert fa.workspace_size(f32, 1, 512, 0, False) == 512 * 4096 * 4
     d1 = fa.workspace_size(lay, 64, 1, 8192, True)
