@@ -30,11 +30,13 @@
 // substitutes that row in its registers.
 //
 // After the loop the waves merge in LDS; each split writes a partial (max,
-// sum, O); the last split of a (sequence, KV head) to arrive merges all of
-// them and applies the gate (Ch 9, 9.8).  Arrivals are counted in a 64-bit
-// word holding (call tag, count): a word carrying another call's tag counts
-// as zero, so the workspace needs no clearing; the merging split resets the
-// count.  Splits that would cover no row of a shorter sequence exit at once.
+// sum, O); the splits' partials are merged in two levels (groups of
+// consecutive splits, then the groups) by the last split to arrive at each,
+// and the final merge applies the gate (Ch 9, 9.8).  Arrivals are counted in
+// 64-bit words holding (call tag, count): a word carrying another call's tag
+// counts as zero, so the workspace needs no clearing; the merging split
+// resets the count.  Splits that would cover no row of a shorter sequence
+// exit at once.
 #include <type_traits>
 
 #include "device_common.h"
@@ -80,6 +82,14 @@ struct SubTile {
     u32x4 v[DecodeTraits<T>::VREG];
 };
 
+// Vector accesses to the split partials with the same per-dword coherence as
+// the agent-scope atomics above (the sc1 cache policy).  The buffer resource
+// spans one (sequence, KV head)'s partials; an access beyond it reads zeros.
+constexpr int kCoherent = 16;                          // sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
 template <typename T, int DEPTH>
 __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(MUSE_DECODE_WAVES, MUSE_DECODE_WAVES)))
 void decode_kernel(DecodeArgs a) {
@@ -91,7 +101,7 @@ void decode_kernel(DecodeArgs a) {
     constexpr int WAVE_V = SUB * LDV * ES, WAVE_K = SUB * LDKW * ES;
     constexpr int NW = kDecodeWaves, NT = 64 * NW;
     constexpr int LOOP_BYTES = NW * (WAVE_V + WAVE_K) + HG * LDQ * 4;
-    constexpr int MERGE_BYTES = NW * HG * (D + 2) * 4 + HG * kMaxSplits * 4;
+    constexpr int MERGE_BYTES = NW * HG * (D + 2) * 4;
     constexpr int LDS_BYTES = LOOP_BYTES > MERGE_BYTES ? LOOP_BYTES : MERGE_BYTES;
     // per-wave V (and f32 K) buffers and the f32 Q-hat; the 4-wave merge after the loop
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
@@ -128,6 +138,50 @@ void decode_kernel(DecodeArgs a) {
     T* Vw = (T*)wave_lds;
     T* Kw = (T*)(wave_lds + WAVE_V);
     float* Qf = (float*)(lds + NW * (WAVE_V + WAVE_K));
+
+    // ---- the raw Q of this wave's heads, on the owner of p the new K (wave
+    // 0) or V (wave 1) row, and the gate values this thread applies at the
+    // end: loaded before the cache prefetch so that they do not wait behind it
+    constexpr int QPW = HG / NW;                       // query heads each wave normalises
+    T qraw[QPW][2];
+    {
+        const T* q = (const T*)a.q + obase;
+#pragma unroll
+        for (int i = 0; i < QPW; ++i) {
+            const int hh = wave * QPW + i;
+            qraw[i][0] = q[hh * D + 2 * lane];
+            qraw[i][1] = q[hh * D + 2 * lane + 1];
+        }
+    }
+    T nraw[2] = {from_f32<T>(0.0f), from_f32<T>(0.0f)};
+    const bool new_row = owns_p && wave < 2;
+    if (new_row) {
+        const T* src = (const T*)(wave == 0 ? a.k : a.v) + ((int64_t)s * kKvHeads + g) * D;
+        nraw[0] = src[2 * lane];
+        nraw[1] = src[2 * lane + 1];
+    }
+    // thread -> (head hh, DPT consecutive dims) after the loop
+    constexpr int TPH = NT / HG, DPT = D / TPH;        // threads per head, dims per thread
+    static_assert(TPH == 32 && DPT == 4, "a head per half wave, 4 dims per thread");
+    const int hh = tid / TPH, d0 = (tid % TPH) * DPT;
+    constexpr int GREG = DPT * ES / 16 > 0 ? DPT * ES / 16 : 1;   // 16-B loads of gate values
+    u32x4 graw[GREG];
+    if constexpr (kBf16) {
+        const uint2 g2 = *(const uint2*)((const char*)a.gate + (obase + hh * D + d0) * ES);
+        graw[0] = u32x4{g2.x, g2.y, 0u, 0u};
+    } else {
+        graw[0] = *(const u32x4*)((const char*)a.gate + (obase + hh * D + d0) * ES);
+    }
+    auto gate_sig = [&](int x) __attribute__((always_inline)) {     // sigmoid of gate value d0 + x
+        float gv;
+        if constexpr (kBf16) {
+            const unsigned w = graw[0][x / 2];
+            gv = __uint_as_float((x % 2) ? (w & 0xffff0000u) : (w << 16));
+        } else {
+            gv = __uint_as_float(graw[0][x]);
+        }
+        return sigmoid(gv);
+    };
 
     // ---- loads of one 16-row sub-tile.  Every lane always loads (a load
     // skipped by some waves would make the compiler wait for all of them):
@@ -178,36 +232,32 @@ void decode_kernel(DecodeArgs a) {
     {
         float sn = 0.0f, cs_ = 1.0f;
         if (a.rope) rope_sincos(a.theta, lane, p, sn, cs_);
-        const T* q = (const T*)a.q + obase;
 #pragma unroll
-        for (int i = 0; i < HG / NW; ++i) {
-            const int hh = wave * (HG / NW) + i;
+        for (int i = 0; i < QPW; ++i) {
+            const int h2 = wave * QPW + i;
             float y0, y1;
-            norm_rope_pair(to_f32(q[hh * D + 2 * lane]), to_f32(q[hh * D + 2 * lane + 1]), a.eps,
-                           a.q_gain, a.rope, sn, cs_, y0, y1);
-            Qf[hh * LDQ + 2 * lane] = y0;
-            Qf[hh * LDQ + 2 * lane + 1] = y1;
+            norm_rope_pair(to_f32(qraw[i][0]), to_f32(qraw[i][1]), a.eps, a.q_gain, a.rope, sn, cs_, y0, y1);
+            Qf[h2 * LDQ + 2 * lane] = y0;
+            Qf[h2 * LDQ + 2 * lane + 1] = y1;
         }
-        if (owns_p && wave == 0) {
-            const T* kr = (const T*)a.k + ((int64_t)s * kKvHeads + g) * D;
-            float y0, y1;
-            norm_rope_pair(to_f32(kr[2 * lane]), to_f32(kr[2 * lane + 1]), a.eps, a.k_gain, a.rope,
-                           sn, cs_, y0, y1);
-            const T k0 = from_f32<T>(y0), k1 = from_f32<T>(y1);
-            T* dst = (T*)a.cache_k + (((int64_t)s * a.capacity + p) * kKvHeads + g) * D;
-            dst[2 * lane] = k0;
-            dst[2 * lane + 1] = k1;
-            knew[2 * lane] = k0;
-            knew[2 * lane + 1] = k1;
-        }
-        if (owns_p && wave == 1) {
-            const T* vr = (const T*)a.v + ((int64_t)s * kKvHeads + g) * D;
-            T* dst = (T*)a.cache_v + (((int64_t)s * a.capacity + p) * kKvHeads + g) * D;
-            const T v0 = vr[2 * lane], v1 = vr[2 * lane + 1];
-            dst[2 * lane] = v0;
-            dst[2 * lane + 1] = v1;
-            vnew[2 * lane] = v0;
-            vnew[2 * lane + 1] = v1;
+        if (new_row) {
+            T r0 = nraw[0], r1 = nraw[1];
+            T* dst;
+            if (wave == 0) {                           // K-hat
+                float y0, y1;
+                norm_rope_pair(to_f32(r0), to_f32(r1), a.eps, a.k_gain, a.rope, sn, cs_, y0, y1);
+                r0 = from_f32<T>(y0);
+                r1 = from_f32<T>(y1);
+                dst = (T*)a.cache_k + (((int64_t)s * a.capacity + p) * kKvHeads + g) * D;
+                knew[2 * lane] = r0;
+                knew[2 * lane + 1] = r1;
+            } else {                                   // V as it is
+                dst = (T*)a.cache_v + (((int64_t)s * a.capacity + p) * kKvHeads + g) * D;
+                vnew[2 * lane] = r0;
+                vnew[2 * lane + 1] = r1;
+            }
+            dst[2 * lane] = r0;
+            dst[2 * lane + 1] = r1;
         }
     }
     __syncthreads();
@@ -361,48 +411,53 @@ void decode_kernel(DecodeArgs a) {
         mw[D + 1] = l_run;
     }
     __syncthreads();
-    const T* gate = (const T*)a.gate + obase;
     T* out = (T*)a.out + obase;
-    // this split's partial for (head hh, dim d) from the waves' rows in LDS
-    auto split_partial = [&](int hh, int d, float& M, float& den) __attribute__((always_inline)) {
+    // this split's partial for (head h2, dim d) from the waves' rows in LDS
+    auto split_partial = [&](int h2, int d, float& M, float& den) __attribute__((always_inline)) {
         M = kNegInf;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, mg[(w * HG + hh) * (D + 2) + D]);
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, mg[(w * HG + h2) * (D + 2) + D]);
         float acc = 0.0f;
         den = 0.0f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            const float* row = mg + (w * HG + hh) * (D + 2);
+            const float* row = mg + (w * HG + h2) * (D + 2);
             const float e = (row[D] == kNegInf) ? 0.0f : fast_exp2(row[D] - M);
             acc += row[d] * e;
             den += row[D + 1] * e;
         }
         return acc;
     };
+    float own_m, own_l, own_o[DPT];
+#pragma unroll
+    for (int x = 0; x < DPT; ++x) own_o[x] = split_partial(hh, d0 + x, own_m, own_l);
     if (n_live == 1) {                                 // the only split: finish here
-        for (int i = tid; i < HG * D; i += NT) {
-            float M, den;
-            const float acc = split_partial(i / D, i % D, M, den);
-            out[i] = from_f32<T>(acc / den * sigmoid(to_f32(gate[i])));
-        }
+        const float inv = 1.0f / own_l;
+#pragma unroll
+        for (int x = 0; x < DPT; ++x) out[hh * D + d0 + x] = from_f32<T>(own_o[x] * inv * gate_sig(x));
         return;
     }
 
-    // ---- several splits.  Each split first counts its arrival: the last one
-    // merges, and it does not publish its own partial.  The others publish
-    // (m, l, O) with agent-coherent stores, wait for them to complete, then
-    // set their ready word to this call's tag; the merging split waits for
-    // those words (every other split has already arrived, so they are
-    // running) and reads the partials with agent-coherent loads.  No
-    // agent-scope fence is used: on this GPU one writes back / invalidates
-    // the whole L2 of an XCD, which costs more than the attention itself.
-    // Thread -> (head hh, DPT consecutive dims) in the final merge; its gate
-    // values are read now, so that the merging split does not wait for them.
-    constexpr int TPH = NT / HG, DPT = D / TPH;        // threads per head, dims per thread
-    const int hh = tid / TPH, d0 = (tid % TPH) * DPT;
-    float gsig[DPT];
-#pragma unroll
-    for (int x = 0; x < DPT; ++x) gsig[x] = sigmoid(to_f32(gate[hh * D + d0 + x]));
+    // ---- several splits, merged in two levels: the splits of a (sequence,
+    // KV head) form groups of kArriveGroup consecutive splits.  Each split
+    // first counts its arrival on its group's word; the last of a group (the
+    // group merger) then counts on the (sequence, KV head) word, and the last
+    // there is the final merger.  A split that merges does not publish its
+    // own partial.  The others
+    // publish (m, l, O) with agent-coherent stores, wait for them to
+    // complete, then set their ready word to this call's tag; a merger waits
+    // for those words (every split it waits for has already arrived, so it is
+    // running) and reads the partials with agent-coherent loads.  A group
+    // merger that is not final publishes its group's merged partial in the
+    // slot of the group's first split (already consumed) and sets the group's
+    // ready word.  No agent-scope fence is used: on this GPU one writes back /
+    // invalidates the whole L2 of an XCD, which costs more than the attention
+    // itself.  Every merge runs in fixed order with a merger's own partial
+    // taken from registers (bit-equal to what it would have published), so
+    // the output does not depend on which splits merge.
+    constexpr int G = kArriveGroup;
+    const int n_grps = (n_live + G - 1) / G;
+    const int grp = c / G, c0 = grp * G, gsize = min(G, n_live - c0);
     if (tid == 0) {
         // count this split's arrival on a tagged word (tag << 32 | count); true
         // for the arrival that completes n, which resets the word for a replay
@@ -426,134 +481,135 @@ void decode_kernel(DecodeArgs a) {
                                    __HIP_MEMORY_SCOPE_AGENT);
             return done;
         };
-        // Many splits arriving on one word serialise on its compare-and-swap, so
-        // they count in groups of kArriveGroup first; the last of each group then
-        // arrives on the (sequence, KV head) word.
-        unsigned long long* words = a.arrivals + (int64_t)(s * kKvHeads + g) * kArriveWords;
-        const int n_grps = (n_live + kArriveGroup - 1) / kArriveGroup;
-        bool last = true;
-        if (n_grps > 1) {
-            const int grp = c / kArriveGroup;
-            last = arrive(words + 1 + grp, min(kArriveGroup, n_live - grp * kArriveGroup));
-        }
-        if (last) last = arrive(words, n_grps > 1 ? n_grps : n_live);
-        last_flag = last;
+        unsigned long long* words = a.arrivals + (int64_t)(s * kKvHeads + g) * kArriveWords;   // pair, then groups
+        int role = 0;                                  // 0 publish, 1 group merger, 2 final merger
+        if (n_grps == 1) role = arrive(words, n_live) ? 2 : 0;
+        else if (arrive(words + 1 + grp, gsize)) role = arrive(words, n_grps) ? 2 : 1;
+        last_flag = role;
     }
     __syncthreads();
-    unsigned int* ready = a.ready + (int64_t)(s * kKvHeads + g) * a.nsplit;
-    const int64_t pbase = ((int64_t)s * kHeads + g * HG) * a.nsplit + c;   // head 16g, split c
-    if (!last_flag) {
-        for (int i = tid; i < HG * D; i += NT) {
-            const int h2 = i / D, d = i % D;
-            float M, den;
-            const float acc = split_partial(h2, d, M, den);
-            const int64_t pi = pbase + (int64_t)h2 * a.nsplit;
-            publish(a.part_o + pi * D + d, acc);
-            if (d == 0) {
-                publish(a.part_m + pi, M);
-                publish(a.part_l + pi, den);
-            }
+    const int role = last_flag;
+    unsigned int* ready = a.ready + (int64_t)(s * kKvHeads + g) * kReadyWords;   // splits, then groups
+    // the partials of this KV head's 16 query heads: O [16][nsplit][128], (m, l) [16][nsplit]
+    float* po = a.part_o + ((int64_t)s * kHeads + g * HG) * a.nsplit * D;
+    const __amdgpu_buffer_rsrc_t rs_o = partial_rsrc(po, (uint32_t)(HG * a.nsplit * D * 4));
+    const int64_t ml_head = ((int64_t)s * kHeads + g * HG + hh) * a.nsplit;   // (m, l) of head hh, slot 0
+    auto publish_partial = [&](int slot, float m, float l, const float (&o)[DPT]) __attribute__((always_inline)) {
+        const int off = ((hh * a.nsplit + slot) * D + d0) * 4;            // bytes
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])},
+            rs_o, off, 0, kCoherent);
+        if (d0 == 0) {
+            publish(a.part_m + ml_head + slot, m);
+            publish(a.part_l + ml_head + slot, l);
         }
         __builtin_amdgcn_s_waitcnt(0);                 // the partial is stored before it is marked ready
         __syncthreads();
+    };
+    if (role == 0) {
+        publish_partial(c, own_m, own_l, own_o);
         if (tid == 0) __hip_atomic_store(ready + c, a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
 
-    // ---- the merging split: wait (bounded) for the other splits' partials
-    if (tid == 0) last_flag = 1;                       // reused below as "all ready"
-    __syncthreads();
-    for (int cc = tid; cc < n_live; cc += NT) {
-        if (cc == c) continue;
-        int spins = 0;
-        while (__hip_atomic_load(ready + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.tag) {
-            if (++spins > kDecodeReadySpins) {
-                last_flag = 0;                         // give up: the output becomes NaN
-                break;
+    // wait (bounded) for ready words first .. first + n - 1 except entry own,
+    // clearing each for the next call or graph replay; false on a time-out
+    __shared__ int ready_ok[2];
+    auto wait_ready = [&](int first, int n, int own, int flag) __attribute__((always_inline)) {
+        if (tid == 0) ready_ok[flag] = 1;
+        __syncthreads();
+        for (int j = tid; j < n; j += NT) {
+            if (j == own) continue;
+            int spins = 0;
+            while (__hip_atomic_load(ready + first + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.tag) {
+                if (++spins > kDecodeReadySpins) {
+                    ready_ok[flag] = 0;                // give up: the output becomes NaN
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
             }
-            __builtin_amdgcn_s_sleep(2);
+            __hip_atomic_store(ready + first + j, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        // consumed: cleared for the next call or graph replay
-        __hip_atomic_store(ready + cc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!last_flag) {
+        __syncthreads();
+        return ready_ok[flag] != 0;
+    };
+    // Merge n <= 16 partials in slot order first, first + stride, ...; entry
+    // own comes from (om, ol, oo).  Lane k of the head's TPH reads entry k's
+    // (m, l); the maximum and the denominator are reductions over those
+    // lanes; then every thread sums its DPT dims of the n O rows, all loads
+    // of one merge in flight together.
+    constexpr int ME = 16;                             // merge entries at most
+    static_assert(G <= ME && kMaxSplits / G <= ME && ME <= TPH, "one merge entry per lane");
+    auto merge = [&](int first, int stride, int n, int own, float om, float ol, const float (&oo)[DPT],
+                     float& m_out, float& l_out, float (&acc)[DPT]) __attribute__((always_inline)) {
+        // the O rows first, so that one round trip covers these loads and the (m, l) below
+        u32x4 raw[ME];
 #pragma unroll
-        for (int x = 0; x < DPT; ++x) out[hh * D + d0 + x] = from_f32<T>(__builtin_nanf(""));
+        for (int j = 0; j < ME; ++j) {
+            if (j < n) {                               // n is uniform over the workgroup
+                const int off = ((hh * a.nsplit + first + stride * j) * D + d0) * 4;
+                raw[j] = __builtin_amdgcn_raw_buffer_load_b128(rs_o, off, 0, kCoherent);
+            }
+        }
+        const int k = tid % TPH;
+        float mk = kNegInf, lk = 0.0f;
+        if (k == own) {
+            mk = om;
+            lk = ol;
+        } else if (k < n) {
+            mk = observe(a.part_m + ml_head + first + stride * k);
+            lk = observe(a.part_l + ml_head + first + stride * k);
+        }
+        float M = mk;
+#pragma unroll
+        for (int o2 = TPH / 2; o2 >= 1; o2 >>= 1) M = fmaxf(M, __shfl_xor(M, o2, 64));
+        const float e = k < n ? fast_exp2(mk - M) : 0.0f;
+        float den = lk * e;
+#pragma unroll
+        for (int o2 = TPH / 2; o2 >= 1; o2 >>= 1) den += __shfl_xor(den, o2, 64);
+#pragma unroll
+        for (int x = 0; x < DPT; ++x) acc[x] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < ME; ++j) {
+            const float w = __shfl(e, (lane & ~(TPH - 1)) | j, 64);    // entry j's weight (0 past n)
+            if (j < n) {
+#pragma unroll
+                for (int x = 0; x < DPT; ++x) {
+                    const float v = (j == own) ? oo[x] : __uint_as_float(raw[j][x]);
+                    acc[x] += v * w;
+                }
+            }
+        }
+        m_out = M;
+        l_out = den;
+    };
+
+    // ---- a merger: first its group
+    float gm, gl, go[DPT];
+    const bool ok = wait_ready(c0, gsize, c - c0, 0);
+    merge(c0, 1, gsize, c - c0, own_m, own_l, own_o, gm, gl, go);
+    if (!ok) {
+        gm = gl = __builtin_nanf("");
+#pragma unroll
+        for (int x = 0; x < DPT; ++x) go[x] = __builtin_nanf("");
+    }
+    if (role == 1) {                                   // publish the group's partial
+        publish_partial(c0, gm, gl, go);
+        if (tid == 0) __hip_atomic_store(ready + kMaxSplits + grp, a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-
-    // ---- merge (the result does not depend on which split merges).
-    // Phase 1: thread (head hh, lane k of the head's TPH threads) reads (m, l)
-    // of splits k, k + TPH, ... in one round of loads; the head's maximum and
-    // denominator come from a reduction over those TPH lanes (one wave half),
-    // and each split's weight exp2(m_c - M) goes to LDS.
-    static_assert(TPH == 32, "one head per half wave in the merge");
-    float* wts = (float*)lds + NW * HG * (D + 2);      // [16 heads][kMaxSplits] after the wave rows
-    const int k = tid % TPH;
-    const int64_t hb = ((int64_t)s * kHeads + g * HG + hh) * a.nsplit;
-    float own_m, own_l, own_o[DPT];
+    float fl = gl, fo[DPT];
 #pragma unroll
-    for (int x = 0; x < DPT; ++x) own_o[x] = split_partial(hh, d0 + x, own_m, own_l);
-    float pm[kMaxSplits / TPH], pl[kMaxSplits / TPH];
-    float M = kNegInf;
-#pragma unroll
-    for (int j = 0; j < kMaxSplits / TPH; ++j) {
-        const int cc = k + TPH * j;
-        pm[j] = kNegInf;
-        pl[j] = 0.0f;
-        if (cc == c) {
-            pm[j] = own_m;
-            pl[j] = own_l;
-        } else if (cc < n_live) {
-            pm[j] = observe(a.part_m + hb + cc);
-            pl[j] = observe(a.part_l + hb + cc);
-        }
-        M = fmaxf(M, pm[j]);
+    for (int x = 0; x < DPT; ++x) fo[x] = go[x];
+    if (n_grps > 1) {                                  // the final merger: then the groups' partials
+        const bool ok2 = wait_ready(kMaxSplits, n_grps, grp, 1);
+        float fm;
+        merge(0, G, n_grps, grp, gm, gl, go, fm, fl, fo);
+        if (!ok2) fl = __builtin_nanf("");
     }
+    const float inv = 1.0f / fl;
 #pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));   // within the half wave
-    float den = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kMaxSplits / TPH; ++j) {
-        const int cc = k + TPH * j;
-        const float e = fast_exp2(pm[j] - M);          // 0 past n_live
-        if (cc < n_live) wts[hh * kMaxSplits + cc] = e;
-        den += pl[j] * e;
-    }
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) den += __shfl_xor(den, o, 64);
-    __syncthreads();
-    // Phase 2: O = sum_c w_c O_c over the splits, eight splits per round of loads
-    float acc[DPT];
-#pragma unroll
-    for (int x = 0; x < DPT; ++x) acc[x] = 0.0f;
-    for (int c0 = 0; c0 < n_live; c0 += 8) {
-        float po[8][DPT];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int cc = c0 + j;
-#pragma unroll
-            for (int x = 0; x < DPT; ++x) po[j][x] = 0.0f;
-            if (cc == c) {
-#pragma unroll
-                for (int x = 0; x < DPT; ++x) po[j][x] = own_o[x];
-            } else if (cc < n_live) {
-#pragma unroll
-                for (int x = 0; x < DPT; ++x) po[j][x] = observe(a.part_o + (hb + cc) * D + d0 + x);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int cc = c0 + j;
-            const float e = cc < n_live ? wts[hh * kMaxSplits + cc] : 0.0f;
-#pragma unroll
-            for (int x = 0; x < DPT; ++x) acc[x] += po[j][x] * e;
-        }
-    }
-    const float inv = 1.0f / den;
-#pragma unroll
-    for (int x = 0; x < DPT; ++x) out[hh * D + d0 + x] = from_f32<T>(acc[x] * inv * gsig[x]);
+    for (int x = 0; x < DPT; ++x) out[hh * D + d0 + x] = from_f32<T>(fo[x] * inv * gate_sig(x));
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream) {

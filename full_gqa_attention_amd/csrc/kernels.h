@@ -85,7 +85,7 @@ struct DecodeArgs {
     float* part_m;          // [S][32][nsplit] partial maxima (log2 domain)
     float* part_l;          // [S][32][nsplit] partial softmax denominators
     unsigned long long* arrivals;  // [S][2][kArriveWords] (tag << 32 | arrivals): the pair, then groups
-    unsigned int* ready;    // [S][2][nsplit] tag of the call whose partial is stored, 0 once merged
+    unsigned int* ready;    // [S][2][kReadyWords] tag of the call whose split (then group) partial is stored, 0 once merged
     float theta[64];        // f32 RoPE frequency table
 };
 
@@ -96,8 +96,9 @@ constexpr int kDecodeTile = 64;  // split granularity of the decode (keys)
 constexpr int kDecodeWaves = 8;  // waves per decode workgroup (two per SIMD)
 constexpr int kDecodeReadySpins = 1 << 20;  // polls of a ready word before the merge gives up
 constexpr int kMaxSplits = 128;  // decode splits per (sequence, KV head), at most
-constexpr int kArriveGroup = 8;   // decode splits counted per group word
+constexpr int kArriveGroup = 8;   // decode splits per merge group (and group arrival word)
 constexpr int kArriveWords = 1 + kMaxSplits / kArriveGroup;  // arrival words per (sequence, KV head)
+constexpr int kReadyWords = kMaxSplits + kMaxSplits / kArriveGroup;  // ready words per (sequence, KV head): splits, groups
 
 int prefill_grid(int n_seq, int n_new);
 

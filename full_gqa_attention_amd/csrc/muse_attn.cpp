@@ -97,8 +97,8 @@ void decode_split(const muse_attn_layer* l, int32_t n_seq, int32_t max_seq_len,
 
 // Prefill: on f32 layers Q-hat [S][N][32][128]; on bf16 layers (where the
 // attention kernel makes Q-hat itself) the fp16 key copy [S][max_seq_len + N][2][128].
-// Decode: arrival words [S][2][kArriveWords] (u64), ready words [S][2][nsplit]
-// (u32), then the split partials.
+// Decode: arrival words [S][2][kArriveWords] (u64), ready words [S][2][kReadyWords]
+// (u32), then the split partials O [S][32][nsplit][128], m and l [S][32][nsplit].
 struct WorkspaceLayout {
     size_t qhat = 0, kq = 0, arrivals = 0, ready = 0, part_o = 0, part_m = 0, part_l = 0, total = 0;
     int64_t kq_capacity = 0;
@@ -124,7 +124,7 @@ WorkspaceLayout layout_for(const muse_attn_layer* l, int32_t n_seq, int32_t n_ne
         off = round_up((size_t)n_seq * kKvHeads * muse::kArriveWords * sizeof(unsigned long long), kAlign);
         decode_split(l, n_seq, max_seq_len, &w.chunk, &w.nsplit);
         w.ready = off;
-        off += round_up((size_t)n_seq * kKvHeads * w.nsplit * sizeof(unsigned int), kAlign);
+        off += round_up((size_t)n_seq * kKvHeads * muse::kReadyWords * sizeof(unsigned int), kAlign);
         const size_t parts = (size_t)n_seq * kHeads * w.nsplit;
         w.part_o = off;
         off += round_up(parts * kHeadDim * sizeof(float), kAlign);

@@ -111,6 +111,18 @@ def test_decode_ragged(spec, dtype):
     _check_layer(w, spec, inp, decode=True)
 
 
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F32], ids=["bf16", "f32"])
+def test_decode_long_context_two_level_merge(dtype):
+    """Long contexts make many splits per (sequence, KV head), merged in
+    groups and then across groups: 40,000 cached rows (six groups, the last
+    partial), 9,000 (two) and 7,680 (a full group and a group of one split)."""
+    spec = synth.full()
+    lens = [40000, 9000, 7680]
+    w = _custom("long_decode", dtype, len(lens), max(lens), 1, [spec])
+    inp = _ragged_inputs(w, spec, lens, 1)
+    _check_layer(w, spec, inp, decode=True)
+
+
 @pytest.mark.parametrize("spec", [synth.sliding(100, 500000.0), synth.full()], ids=["w100", "full"])
 def test_decode_equals_last_prefill_row(spec):
     """Cross-entry: decode at p reproduces row p of a (p+1)-token prefill."""
