@@ -23,11 +23,13 @@
 //   * Online softmax in the log2 domain; the row max over 16 keys needs two
 //     lane exchanges (xor 16, 32).
 //
-// Before the loop each workgroup computes Q-hat of its 16 heads from the raw
-// Q (norm, gain, RoPE on sliding layers: "Chapter 14 - QK-norm and RoPE"
-// 14.3-14.5).  The workgroup whose split holds position p also normalises and
-// rotates the new K, stores K-hat and V to cache row p (Ch 14, 14.7) and
-// substitutes that row in its registers.
+// Before the loop each wave computes Q-hat of the 16 heads from the raw Q
+// itself, in the B-operand layout it needs (norm, gain, RoPE on sliding
+// layers: "Chapter 14 - QK-norm and RoPE" 14.3-14.5), with no workgroup
+// barrier; it also makes the new K row (K-hat, rounded as stored) in the
+// chunk layout of its sub-tiles, for the lanes whose row is position p.  The
+// workgroup whose split holds p stores K-hat and V to cache row p (Ch 14,
+// 14.7).
 //
 // After the loop the waves merge in LDS; each split writes a partial (max,
 // sum, O); the splits' partials are merged in two levels (groups of
@@ -96,17 +98,15 @@ void decode_kernel(DecodeArgs a) {
     using Tr = DecodeTraits<T>;
     constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
     constexpr int D = kHeadDim, HG = kHeadsPerKv, SUB = 16;
-    constexpr int LDV = Tr::LDV, LDKW = Tr::LDKW, LDQ = D + 4;
+    constexpr int LDV = Tr::LDV, LDKW = Tr::LDKW;
     constexpr int ES = (int)sizeof(T);
     constexpr int WAVE_V = SUB * LDV * ES, WAVE_K = SUB * LDKW * ES;
     constexpr int NW = kDecodeWaves, NT = 64 * NW;
-    constexpr int LOOP_BYTES = NW * (WAVE_V + WAVE_K) + HG * LDQ * 4;
+    constexpr int LOOP_BYTES = NW * (WAVE_V + WAVE_K);
     constexpr int MERGE_BYTES = NW * HG * (D + 2) * 4;
     constexpr int LDS_BYTES = LOOP_BYTES > MERGE_BYTES ? LOOP_BYTES : MERGE_BYTES;
-    // per-wave V (and f32 K) buffers and the f32 Q-hat; the 4-wave merge after the loop
+    // per-wave K and V buffers; the waves' partials after the loop
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
-    __shared__ __attribute__((aligned(16))) T knew[D];    // new key row p (stored values)
-    __shared__ __attribute__((aligned(16))) T vnew[D];    // new value row p
     __shared__ int last_flag;
 
     const int b = blockIdx.x;
@@ -137,29 +137,28 @@ void decode_kernel(DecodeArgs a) {
     char* wave_lds = lds + wave * (WAVE_V + WAVE_K);
     T* Vw = (T*)wave_lds;
     T* Kw = (T*)(wave_lds + WAVE_V);
-    float* Qf = (float*)(lds + NW * (WAVE_V + WAVE_K));
 
-    // ---- the raw Q of this wave's heads, on the owner of p the new K (wave
-    // 0) or V (wave 1) row, and the gate values this thread applies at the
-    // end: loaded before the cache prefetch so that they do not wait behind it
-    constexpr int QPW = HG / NW;                       // query heads each wave normalises
-    T qraw[QPW][2];
+    // ---- first the small loads, so that they do not queue behind the cache
+    // stream: the raw Q of the 16 heads in the B-operand layout of
+    // S^T = K Q^T (lane: head l16, k-group q4), the new K and V rows in the
+    // chunk layout of a cache sub-tile (every wave loads them; rows equal to
+    // p take them), and the gate values this thread applies at the end.
+    u32x4 qv[4];                                       // bf16: dims 32 st + 8 q4 .. + 7
+    float qf32[kBf16 ? 1 : 32];                        // f32: dims 4 st + q4
     {
-        const T* q = (const T*)a.q + obase;
+        const T* qh = (const T*)a.q + obase + (int64_t)l16 * D;
+        if constexpr (kBf16) {
 #pragma unroll
-        for (int i = 0; i < QPW; ++i) {
-            const int hh = wave * QPW + i;
-            qraw[i][0] = q[hh * D + 2 * lane];
-            qraw[i][1] = q[hh * D + 2 * lane + 1];
+            for (int st = 0; st < 4; ++st) qv[st] = *(const u32x4*)(qh + 32 * st + 8 * q4);
+        } else {
+#pragma unroll
+            for (int st = 0; st < 32; ++st) qf32[st] = to_f32(qh[4 * st + q4]);
         }
     }
-    T nraw[2] = {from_f32<T>(0.0f), from_f32<T>(0.0f)};
-    const bool new_row = owns_p && wave < 2;
-    if (new_row) {
-        const T* src = (const T*)(wave == 0 ? a.k : a.v) + ((int64_t)s * kKvHeads + g) * D;
-        nraw[0] = src[2 * lane];
-        nraw[1] = src[2 * lane + 1];
-    }
+    const int nch = kBf16 ? l16 : (lane & 31);         // 16-B chunk of a row this lane holds
+    const int64_t new_off = ((int64_t)s * kKvHeads + g) * D * ES + 16 * nch;
+    const u32x4 kn_raw = *(const u32x4*)((const char*)a.k + new_off);
+    u32x4 vnew_c = *(const u32x4*)((const char*)a.v + new_off);
     // thread -> (head hh, DPT consecutive dims) after the loop
     constexpr int TPH = NT / HG, DPT = D / TPH;        // threads per head, dims per thread
     static_assert(TPH == 32 && DPT == 4, "a head per half wave, 4 dims per thread");
@@ -217,8 +216,112 @@ void decode_kernel(DecodeArgs a) {
     // pipeline stages as named variables (an indexed array of them ends up in scratch)
     static_assert(DEPTH >= 1 && DEPTH <= 8, "pipeline depth 1..8");
     SubTile<T> b0, b1, b2, b3, b4, b5, b6, b7;
-    // (sub-tiles past the wave's share load clamped rows and are never processed)
+    // (sub-tiles past the wave's share load clamped rows and are never
+    // processed).  The first sub-tile's loads go out now; the others after
+    // Q-hat, so that computing it does not wait behind a full queue of loads.
     issue(b0, 0);
+
+    // ---- Q-hat and the new K row, wave by wave (no workgroup barrier): RMS
+    // norm with gain, then RoPE on sliding layers ("Chapter 14 - QK-norm and
+    // RoPE" 14.3-14.5).  Lane i computes (cos, sin) of pair i; lanes fetch
+    // the pairs they hold with cross-lane reads.
+    float sn = 0.0f, cs_ = 1.0f;
+    if (a.rope) rope_sincos(a.theta, lane, p, sn, cs_);
+    auto rotate = [&](float& y0, float& y1, int pair) __attribute__((always_inline)) {
+        const float c2 = __shfl(cs_, pair, 64), s2 = __shfl(sn, pair, 64);
+        const float z0 = y0 * c2 - y1 * s2;
+        const float z1 = y0 * s2 + y1 * c2;
+        y0 = z0;
+        y1 = z1;
+    };
+    auto bf16_at = [](const u32x4& v, int t) __attribute__((always_inline)) {
+        const unsigned w = v[t / 2];
+        return __uint_as_float((t % 2) ? (w & 0xffff0000u) : (w << 16));
+    };
+    constexpr int NSTQ = kBf16 ? 4 : 32;               // 16x16x32 bf16 / 16x16x4 f32 steps
+    using MW = Mma16Wide<T>;
+    using MN = Mma16Narrow<T>;
+    typename MW::Frag qhi[NSTQ], qlo[kBf16 ? NSTQ : 1];
+    {
+        float x[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) x[i] = kBf16 ? bf16_at(qv[i / 8], i % 8) : qf32[kBf16 ? 0 : i];
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) ss += x[i] * x[i];
+        ss += __shfl_xor(ss, 16, 64);                  // the head's other k-groups
+        ss += __shfl_xor(ss, 32, 64);
+        const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) x[i] = (x[i] * r) * a.q_gain;
+        if constexpr (kBf16) {
+            if (a.rope) {
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) rotate(x[8 * st + 2 * j], x[8 * st + 2 * j + 1], 16 * st + 4 * q4 + j);
+            }
+#pragma unroll
+            for (int st = 0; st < NSTQ; ++st) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const float xv = x[8 * st + t];
+                    const bf16_t hi = (bf16_t)xv;
+                    qhi[st][t] = hi;
+                    qlo[st][t] = (bf16_t)(xv - (float)hi);
+                }
+            }
+        } else {
+            if (a.rope) {                              // dim 4 st + q4; its pair partner sits in lane ^ 16
+#pragma unroll
+                for (int st = 0; st < 32; ++st) {
+                    const float other = __shfl_xor(x[st], 16, 64);
+                    float y0 = (q4 & 1) ? other : x[st], y1 = (q4 & 1) ? x[st] : other;
+                    rotate(y0, y1, 2 * st + (q4 >> 1));
+                    x[st] = (q4 & 1) ? y1 : y0;
+                }
+            }
+#pragma unroll
+            for (int st = 0; st < NSTQ; ++st) qhi[st] = x[st];
+        }
+    }
+    // the new K row as it is stored (K-hat rounded to the cache type), in the
+    // lane's chunk; the owner of p writes both rows to the cache
+    u32x4 knew_c;
+    {
+        constexpr int NV = 16 / ES;                    // values per chunk
+        float x[NV];
+#pragma unroll
+        for (int t = 0; t < NV; ++t) x[t] = kBf16 ? bf16_at(kn_raw, t) : __uint_as_float(kn_raw[t % 4]);
+        float ss = 0.0f;
+#pragma unroll
+        for (int t = 0; t < NV; ++t) ss += x[t] * x[t];
+#pragma unroll
+        for (int o2 = 1; o2 < (kBf16 ? 16 : 32); o2 <<= 1) ss += __shfl_xor(ss, o2, 64);   // the row's chunks
+        const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
+#pragma unroll
+        for (int t = 0; t < NV; ++t) x[t] = (x[t] * r) * a.k_gain;
+        if (a.rope) {
+#pragma unroll
+            for (int j = 0; j < NV / 2; ++j) rotate(x[2 * j], x[2 * j + 1], (NV / 2) * nch + j);
+        }
+        if constexpr (kBf16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const unsigned lo16 = __builtin_bit_cast(unsigned short, from_f32<bf16_t>(x[2 * j]));
+                const unsigned hi16 = __builtin_bit_cast(unsigned short, from_f32<bf16_t>(x[2 * j + 1]));
+                knew_c[j] = lo16 | (hi16 << 16);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) knew_c[j] = __float_as_uint(x[kBf16 ? 0 : j]);
+        }
+    }
+    if (owns_p && wave == 0 && (kBf16 ? q4 == 0 : lane < 32)) {
+        const int64_t row_off = (((int64_t)s * a.capacity + p) * kKvHeads + g) * D * ES + 16 * nch;
+        *(u32x4*)((char*)a.cache_k + row_off) = knew_c;
+        *(u32x4*)((char*)a.cache_v + row_off) = vnew_c;
+    }
     if constexpr (DEPTH > 1) issue(b1, 1);
     if constexpr (DEPTH > 2) issue(b2, 2);
     if constexpr (DEPTH > 3) issue(b3, 3);
@@ -226,65 +329,6 @@ void decode_kernel(DecodeArgs a) {
     if constexpr (DEPTH > 5) issue(b5, 5);
     if constexpr (DEPTH > 6) issue(b6, 6);
     if constexpr (DEPTH > 7) issue(b7, 7);
-
-    // ---- prologue: Q-hat of the 16 heads (f32 in LDS); the owner of p also
-    // makes the new K/V row
-    {
-        float sn = 0.0f, cs_ = 1.0f;
-        if (a.rope) rope_sincos(a.theta, lane, p, sn, cs_);
-#pragma unroll
-        for (int i = 0; i < QPW; ++i) {
-            const int h2 = wave * QPW + i;
-            float y0, y1;
-            norm_rope_pair(to_f32(qraw[i][0]), to_f32(qraw[i][1]), a.eps, a.q_gain, a.rope, sn, cs_, y0, y1);
-            Qf[h2 * LDQ + 2 * lane] = y0;
-            Qf[h2 * LDQ + 2 * lane + 1] = y1;
-        }
-        if (new_row) {
-            T r0 = nraw[0], r1 = nraw[1];
-            T* dst;
-            if (wave == 0) {                           // K-hat
-                float y0, y1;
-                norm_rope_pair(to_f32(r0), to_f32(r1), a.eps, a.k_gain, a.rope, sn, cs_, y0, y1);
-                r0 = from_f32<T>(y0);
-                r1 = from_f32<T>(y1);
-                dst = (T*)a.cache_k + (((int64_t)s * a.capacity + p) * kKvHeads + g) * D;
-                knew[2 * lane] = r0;
-                knew[2 * lane + 1] = r1;
-            } else {                                   // V as it is
-                dst = (T*)a.cache_v + (((int64_t)s * a.capacity + p) * kKvHeads + g) * D;
-                vnew[2 * lane] = r0;
-                vnew[2 * lane + 1] = r1;
-            }
-            dst[2 * lane] = r0;
-            dst[2 * lane + 1] = r1;
-        }
-    }
-    __syncthreads();
-
-    // Q-hat as the B operand of S^T = K Q^T: lane holds head l16, k-group q4
-    constexpr int NSTQ = kBf16 ? 4 : 32;               // 16x16x32 bf16 / 16x16x4 f32 steps
-    using MW = Mma16Wide<T>;
-    using MN = Mma16Narrow<T>;
-    typename MW::Frag qhi[NSTQ], qlo[kBf16 ? NSTQ : 1];
-    {
-        const float* qrow = Qf + l16 * LDQ;
-        if constexpr (kBf16) {
-#pragma unroll
-            for (int st = 0; st < NSTQ; ++st) {
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const float x = qrow[32 * st + 8 * q4 + t];
-                    const bf16_t hi = (bf16_t)x;
-                    qhi[st][t] = hi;
-                    qlo[st][t] = (bf16_t)(x - (float)hi);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int st = 0; st < NSTQ; ++st) qhi[st] = qrow[4 * st + q4];
-        }
-    }
 
     floatx4 o[D / 16];
 #pragma unroll
@@ -302,8 +346,8 @@ void decode_kernel(DecodeArgs a) {
                 const int r = 4 * u + q4;
                 u32x4 kraw = t.k[u], vraw = t.v[u];
                 if (clamp_row(j0 + r) == p) {
-                    kraw = *(const u32x4*)(knew + l16 * 8);
-                    vraw = *(const u32x4*)(vnew + l16 * 8);
+                    kraw = knew_c;
+                    vraw = vnew_c;
                 }
                 *(u32x4*)(Kw + r * LDKW + l16 * 8) = kraw;
                 *(u32x4*)(Vw + r * LDV + l16 * 8) = vraw;
@@ -320,8 +364,8 @@ void decode_kernel(DecodeArgs a) {
                 const int r = 2 * u + (lane >> 5);
                 u32x4 kraw = t.k[u], vraw = t.v[u];
                 if (clamp_row(j0 + r) == p) {
-                    kraw = *(const u32x4*)(knew + (lane & 31) * 4);
-                    vraw = *(const u32x4*)(vnew + (lane & 31) * 4);
+                    kraw = knew_c;
+                    vraw = vnew_c;
                 }
                 *(u32x4*)(Kw + r * LDKW + (lane & 31) * 4) = kraw;
                 *(u32x4*)(Vw + r * LDV + (lane & 31) * 4) = vraw;
