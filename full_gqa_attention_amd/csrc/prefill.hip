@@ -802,7 +802,10 @@ void prefill_group_kernel(AttnArgs a) {
         if (!__syncthreads_or(!__builtin_isfinite(chk))) break;
     }
 
-    // ---- epilogue: normalise, gate, store
+    // ---- epilogue: normalise, gate, store.  All of a row's gate values are
+    // loaded before any output is stored: interleaved, every load would wait
+    // for the stores before it (the two buffers may alias as far as the
+    // compiler knows), one memory round trip per value.
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
         const float l_tot = sum_halves(l_run[qg]);
@@ -812,16 +815,26 @@ void prefill_group_kernel(AttnArgs a) {
         const int64_t base = (((int64_t)s * N + tq) * kHeads + h) * D;
         const T* gate = (const T*)a.gate + base;
         T* dst = out + base;
+        uint2 graw[4][4];                              // dims 32 dt + 8 ig + 4 gl .. + 3
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int ig = 0; ig < 4; ++ig) graw[dt][ig] = *(const uint2*)(gate + 32 * dt + 8 * ig + 4 * gl);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
             for (int ig = 0; ig < 4; ++ig) {
-                const int d0 = 32 * dt + 8 * ig + 4 * gl;
+                unsigned packed[2];
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
-                    const float gv = to_f32(gate[d0 + x]);
-                    dst[d0 + x] = from_f32<T>(o[dt][qg][4 * ig + x] * inv * sigmoid(gv));
+                    const unsigned w = x < 2 ? graw[dt][ig].x : graw[dt][ig].y;
+                    const float gv = __uint_as_float((x & 1) ? (w & 0xffff0000u) : (w << 16));
+                    const T y = from_f32<T>(o[dt][qg][4 * ig + x] * inv * sigmoid(gv));
+                    const unsigned u = __builtin_bit_cast(unsigned short, y);
+                    if (x & 1) packed[x / 2] |= u << 16;
+                    else packed[x / 2] = u;
                 }
+                *(uint2*)(dst + 32 * dt + 8 * ig + 4 * gl) = make_uint2(packed[0], packed[1]);
             }
         }
     }
