@@ -431,7 +431,7 @@ void prefill_group_kernel(AttnArgs a) {
     // exactly one wave, so this costs no more than a separate pass and saves
     // writing Q-hat to HBM and reading it back.  The workgroup's rows share one
     // (cos, sin) table in LDS.
-    __shared__ float2 rot[BMW][kHeadDim / 2];
+    __shared__ float2 rot[BMW][kHeadDim / 2 + 1];       // padded: rows start 2 banks apart
     if (a.rope) {
         float th = 0.0f;                               // theta[lane] without indexing the argument block
 #pragma unroll

@@ -2,12 +2,14 @@
 // for a chunk of new tokens (the prefill path; decode does this inside its
 // own kernel).
 //
-// One workgroup (256 threads) per new token.  A head vector of 128 values is
-// handled by 16 lanes, 8 values (16 bytes, RoPE pairs 4i..4i+3) per lane, so
-// one wave covers four vectors and the 36 vectors of a token (32 Q heads, 2 K
-// heads, 2 V heads) take three passes of the workgroup.  The 64 sin/cos
-// pairs of the token's position are computed once, by the first 64 threads,
-// and shared through LDS.
+// f32 layers: one workgroup (256 threads) per new token.  A head vector of
+// 128 values is handled by 16 lanes, 8 values (16 bytes, RoPE pairs
+// 4i..4i+3) per lane, so one wave covers four vectors and the 36 vectors of a
+// token (32 Q heads, 2 K heads, 2 V heads) take three passes of the
+// workgroup.  The 64 sin/cos pairs of the token's position are computed
+// once, by the first 64 threads, and shared through LDS.  bf16 layers only
+// need K-hat and V here (the attention kernel makes Q-hat): one wave takes
+// the four K/V vectors of four tokens in turn.
 //   * QK-norm: RMS over the 128 values of one head, then the constant gain
 //     ("Chapter 9 - The Muse Glimmer architecture" 9.5 RMSNorm formula;
 //     "Chapter 14 - QK-norm and RoPE" 14.3: Q gain about 3.87, K gain 1).
@@ -81,14 +83,99 @@ __device__ __forceinline__ void convert_prefix(const PrepArgs& a, int idx) {
     }
 }
 
+// bf16 layers (Q-hat is made by the attention kernel): K-hat and V of
+// kKvTokensPerWave tokens per wave, 16 tokens per workgroup.  Lane l holds
+// the 16-byte chunk l % 16 (dims 8 (l % 16) .. + 7) of vector l / 16: K head
+// 0, K head 1, V head 0, V head 1.  All of a wave's loads are issued before
+// its first store (a load after a store to a buffer the compiler cannot tell
+// apart would wait for it), and lane i computes (cos, sin) of RoPE pair i
+// for each token, which the K lanes fetch with cross-lane reads.
+constexpr int kKvTokensPerWave = 4;
+__device__ __forceinline__ void prep_kv_bf16(const PrepArgs& a, int blk) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int vec = lane >> 4, sub = lane & 15;
+    const int hk = vec & 1;
+    const bool is_k = vec < kKvHeads;
+    const int n_tok = a.n_seq * a.n_new;
+    const int tok0 = (blk * 4 + wave) * kKvTokensPerWave;
+    u32x4 raw[kKvTokensPerWave];
+    int Ls[kKvTokensPerWave];
+#pragma unroll
+    for (int i = 0; i < kKvTokensPerWave; ++i) {
+        const int tok = min(tok0 + i, n_tok - 1);
+        const bf16_t* src = (const bf16_t*)(is_k ? a.k : a.v) + ((int64_t)tok * kKvHeads + hk) * kHeadDim + 8 * sub;
+        raw[i] = *(const u32x4*)src;
+        Ls[i] = a.seq_len[tok / a.n_new];
+    }
+    float th = 0.0f;                               // theta[lane] without indexing the argument block
+#pragma unroll
+    for (int i = 0; i < 64; ++i) th = (lane == i) ? a.theta[i] : th;
+#pragma unroll
+    for (int i = 0; i < kKvTokensPerWave; ++i) {
+        const int tok = tok0 + i;
+        if (tok >= n_tok) break;                   // uniform over the wave
+        const int s = tok / a.n_new, t = tok - s * a.n_new;
+        const int L = Ls[i];
+        if (L < 0 || L > a.max_seq_len) continue;  // refused (the attention kernel writes NaN)
+        const int64_t p = (int64_t)L + t;
+        const int64_t row = ((int64_t)s * a.capacity + p) * kKvHeads + hk;
+        if (!is_k) {                               // V: exact copy
+            *(u32x4*)((bf16_t*)a.cache_v + row * kHeadDim + 8 * sub) = raw[i];
+        }
+        const bf16x8 kx = __builtin_bit_cast(bf16x8, raw[i]);
+        float y[8];
+        float ss = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            y[j] = (float)kx[j];
+            ss += y[j] * y[j];
+        }
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);   // the 16 lanes of this head
+        const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = (y[j] * r) * a.k_gain;
+        if (a.rope) {
+            float sn, cs;
+            sincosf((float)p * th, &sn, &cs);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float c2 = __shfl(cs, 4 * sub + j, 64), s2 = __shfl(sn, 4 * sub + j, 64);
+                const float y0 = y[2 * j], y1 = y[2 * j + 1];
+                y[2 * j] = y0 * c2 - y1 * s2;
+                y[2 * j + 1] = y0 * s2 + y1 * c2;
+            }
+        }
+        if (is_k) {
+            bf16x8 kv;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kv[j] = from_f32<bf16_t>(y[j]);
+            const u32x4 kr = __builtin_bit_cast(u32x4, kv);
+            *(u32x4*)((bf16_t*)a.cache_k + row * kHeadDim + 8 * sub) = kr;
+            // the score copy holds the stored values
+            const int64_t qrow = ((int64_t)s * a.kq_capacity + p) * kKvHeads + hk;
+            *(u32x4*)((f16_t*)a.kq + qrow * kHeadDim + 8 * sub) = k_chunk_to_score(kr, bf16_t{});
+        }
+    }
+}
+
+__host__ __device__ inline int prep_kv_blocks(int n_tok) { return (n_tok + 4 * kKvTokensPerWave - 1) / (4 * kKvTokensPerWave); }
+
 template <typename T>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     typedef typename ScoreType<T>::type TQ;
     __shared__ float2 rot[64];                     // (cos, sin) of pair i at this token's position
     const int n_tok = a.n_seq * a.n_new;
-    if ((int)blockIdx.x >= n_tok) {                // fp16 copy of visible prefix keys
-        if constexpr (sizeof(T) == 2) convert_prefix(a, (int)blockIdx.x - n_tok);
+    const int n_main = a.skip_q ? prep_kv_blocks(n_tok) : n_tok;
+    if ((int)blockIdx.x >= n_main) {               // fp16 copy of visible prefix keys
+        if constexpr (sizeof(T) == 2) convert_prefix(a, (int)blockIdx.x - n_main);
         return;
+    }
+    if constexpr (sizeof(T) == 2) {
+        if (a.skip_q) {
+            prep_kv_bf16(a, blockIdx.x);
+            return;
+        }
     }
     const int tok = blockIdx.x;                    // s * n_new + t
     const int s = tok / a.n_new;
@@ -164,7 +251,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 }
 
 hipError_t launch_prep(const PrepArgs& a, int dtype, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.n_seq * a.n_new + a.n_seq * a.conv_blocks)), block(256);
+    const int n_tok = a.n_seq * a.n_new;
+    const int n_main = a.skip_q ? prep_kv_blocks(n_tok) : n_tok;
+    const dim3 grid((unsigned)(n_main + a.n_seq * a.conv_blocks)), block(256);
     if (dtype == 1)
         hipLaunchKernelGGL(prep_kernel<bf16_t>, grid, block, 0, stream, a);
     else
