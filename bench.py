@@ -310,7 +310,7 @@ def bench_prefill(w, steps, warmup, fa, synth, torch):
         "frac_mfma_peak": round(flops_step / (ms_per_step * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "muse::prefill_group_kernel<1, 4, 1, false> (bf16)", "avg_launch_ms": round(kern, 4),
+                     "kernel": "muse::prefill_group_kernel<1, 8, 1, false> (bf16)", "avg_launch_ms": round(kern, 4),
                      "per_layer": per_layer},
         "flop_per_step": flops_step, "steps": steps, "warmup": warmup,
     }
