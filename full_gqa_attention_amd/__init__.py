@@ -47,7 +47,7 @@ class Layer(ctypes.Structure):
                 ("window", ctypes.c_int32), ("rope_theta", ctypes.c_float),
                 ("rms_eps", ctypes.c_float), ("q_norm_gain", ctypes.c_float),
                 ("k_norm_gain", ctypes.c_float), ("attn_scale", ctypes.c_float),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("kv_ring", ctypes.c_int32)]
 
 
 class KvCache(ctypes.Structure):
@@ -104,9 +104,11 @@ def _check(code: int, where: str):
 
 def make_layer(kind: int, *, window: int = 0, rope_theta: float = 0.0, rms_eps: float = 1e-5,
                q_norm_gain: float = 3.87, k_norm_gain: float = 1.0,
-               attn_scale: float = 1.0 / math.sqrt(128.0), dtype: int = BF16) -> Layer:
+               attn_scale: float = 1.0 / math.sqrt(128.0), dtype: int = BF16,
+               kv_ring: int = 0) -> Layer:
+    """kv_ring=1 (sliding bf16 layers): the cache is a ring, position p in row p % capacity."""
     return Layer(N_HEADS, N_KV_HEADS, HEAD_DIM, kind, window, rope_theta, rms_eps,
-                 q_norm_gain, k_norm_gain, attn_scale, dtype)
+                 q_norm_gain, k_norm_gain, attn_scale, dtype, kv_ring)
 
 
 def layer_init(layer_index: int, dtype: int = BF16) -> Layer:
@@ -212,10 +214,12 @@ def prefill(layer: Layer, q, k, v, gate, cache_k, cache_v, seq_len, out=None, *,
     """muse_attn_prefill on torch tensors (see include/muse_attn.h).
 
     max_seq_len defaults to capacity - n_new (an upper bound of seq_len that
-    needs no device read)."""
+    needs no device read); a kv_ring layer must pass it."""
     if out is None:
         out = torch.empty(gate.shape, dtype=gate.dtype, device=gate.device)
     if max_seq_len is None:
+        if layer.kv_ring:
+            raise ValueError("a kv_ring layer needs max_seq_len (positions outgrow the ring)")
         max_seq_len = cache_k.shape[1] - q.shape[1]
     return _call(False, layer, q, k, v, gate, cache_k, cache_v, seq_len, out, max_seq_len,
                  workspace, stream, timer)
@@ -228,6 +232,8 @@ def decode(layer: Layer, q, k, v, gate, cache_k, cache_v, seq_len, out=None, *,
     if out is None:
         out = torch.empty(gate.shape, dtype=gate.dtype, device=gate.device)
     if max_seq_len is None:
+        if layer.kv_ring:
+            raise ValueError("a kv_ring layer needs max_seq_len (positions outgrow the ring)")
         max_seq_len = cache_k.shape[1] - 1
     return _call(True, layer, q, k, v, gate, cache_k, cache_v, seq_len, out, max_seq_len,
                  workspace, stream, timer)

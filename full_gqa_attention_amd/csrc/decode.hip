@@ -191,6 +191,14 @@ void decode_kernel(DecodeArgs a) {
     const char* gk = (const char*)a.cache_k + ((int64_t)s * a.capacity * kKvHeads + g) * D * ES;
     const char* gv = (const char*)a.cache_v + ((int64_t)s * a.capacity * kKvHeads + g) * D * ES;
     auto clamp_row = [&](int64_t j) __attribute__((always_inline)) { return j < ce ? j : ce - 1; };
+    // cache row of position j: j, or j % ring on a ring layer, where the
+    // split's positions [cs, ce) (at most `ring` of them) wrap at most once
+    const int64_t row_cs = a.ring ? cs % a.ring : cs;
+    const int64_t wrap = a.ring ? a.ring : INT64_MAX;
+    auto cache_row = [&](int64_t j) __attribute__((always_inline)) {
+        const int64_t r = row_cs + (j - cs);
+        return r >= wrap ? r - wrap : r;
+    };
     auto issue = [&](SubTile<T>& t, int k) __attribute__((always_inline)) {
         const int64_t j0 = cs + (int64_t)SUB * (wave + NW * k);
         if constexpr (kBf16) {
@@ -199,14 +207,14 @@ void decode_kernel(DecodeArgs a) {
             // 16 rows per instruction, streams far slower)
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int64_t jv = clamp_row(j0 + 4 * u + q4);
+                const int64_t jv = cache_row(clamp_row(j0 + 4 * u + q4));
                 t.k[u] = __builtin_nontemporal_load((const u32x4*)(gk + jv * row_stride + l16 * 16));
                 t.v[u] = __builtin_nontemporal_load((const u32x4*)(gv + jv * row_stride + l16 * 16));
             }
         } else {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {              // rows 2u + lane/32, 16-B chunk lane%32
-                const int64_t jj = clamp_row(j0 + 2 * u + (lane >> 5));
+                const int64_t jj = cache_row(clamp_row(j0 + 2 * u + (lane >> 5)));
                 t.k[u] = __builtin_nontemporal_load((const u32x4*)(gk + jj * row_stride + (lane & 31) * 16));
                 t.v[u] = __builtin_nontemporal_load((const u32x4*)(gv + jj * row_stride + (lane & 31) * 16));
             }
@@ -318,7 +326,7 @@ void decode_kernel(DecodeArgs a) {
         }
     }
     if (owns_p && wave == 0 && (kBf16 ? q4 == 0 : lane < 32)) {
-        const int64_t row_off = (((int64_t)s * a.capacity + p) * kKvHeads + g) * D * ES + 16 * nch;
+        const int64_t row_off = (((int64_t)s * a.capacity + cache_row(p)) * kKvHeads + g) * D * ES + 16 * nch;
         *(u32x4*)((char*)a.cache_k + row_off) = knew_c;
         *(u32x4*)((char*)a.cache_v + row_off) = vnew_c;
     }

@@ -32,6 +32,10 @@ struct PrepArgs {
     int64_t kq_capacity;
     int32_t window;         // 0: full; else only rows > p_first - window are copied
     int32_t conv_blocks;    // prefix-conversion workgroups per sequence
+    int32_t kq_windowed;    // 1: kq (and vq) row = position - max(0, seq_len - window + 1)
+    int64_t ring;           // 0: cache row = position; else cache row = position % ring
+    void* vq;               // ring layers: copy of the V rows the chunk sees, laid out as kq
+    int32_t phase;          // 0: prefix copy and new rows; 1: prefix copy only; 2: new rows only
     float theta[64];        // f32 RoPE frequency table
 };
 
@@ -55,6 +59,8 @@ struct AttnArgs {
     int32_t n_seq;
     int32_t n_new;
     int32_t window;         // 0: full causal; else keys with p - j < window
+    int32_t kq_windowed;    // 1: kq row = position - max(0, seq_len - window + 1)
+    int32_t v_windowed;     // 1: cache_v row likewise (cache_v is then the V copy)
 };
 
 // Kernel (c): the whole decode step for one new token per sequence in one
@@ -73,6 +79,7 @@ struct DecodeArgs {
     int32_t max_seq_len;
     int32_t n_seq;
     int32_t window;         // 0: full causal; else keys with p - j < window
+    int64_t ring;           // 0: cache row = position; else cache row = position % ring
     int32_t rope;           // 1: sliding layer (rotate), 0: NoPE
     float eps;
     float q_gain;
@@ -93,6 +100,11 @@ struct DecodeArgs {
 constexpr int kPrefillBM = 128;  // query rows per prefill workgroup (4 waves x 32)
 constexpr int kPrefillBN = 64;   // keys per prefill tile
 constexpr int kDecodeTile = 64;  // split granularity of the decode (keys)
+// The windowed key (and ring-layer V) copies of the prefill start at the
+// window's first visible position rounded down to a multiple of this, so
+// that every key tile the attention kernel loads (tiles start at multiples of
+// their size, at most this) lies inside the copy.
+constexpr int kWindowAlign = 64;
 constexpr int kDecodeWaves = 8;  // waves per decode workgroup (two per SIMD)
 constexpr int kDecodeReadySpins = 1 << 20;  // polls of a ready word before the merge gives up
 constexpr int kMaxSplits = 128;  // decode splits per (sequence, KV head), at most

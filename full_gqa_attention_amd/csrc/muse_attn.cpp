@@ -48,7 +48,27 @@ muse_status check_layer(const muse_attn_layer* l) {
     // |gain| * sqrt(128), which must stay inside fp16's range.
     if (!(std::fabs(l->q_norm_gain) <= kMaxGain) || !(std::fabs(l->k_norm_gain) <= kMaxGain))
         return MUSE_ERR_LAYER;
+    // a ring cache holds a sliding layer's window ("Chapter 9" 9.7); bf16 only
+    if (l->kv_ring != 0 && (l->kv_ring != 1 || l->kind != MUSE_SLIDING_ROPE || l->dtype != MUSE_BF16))
+        return MUSE_ERR_LAYER;
     return MUSE_OK;
+}
+
+// Prefix positions the prefill's key copy holds per sequence: all of them on
+// full layers; on sliding layers those from the window's first visible one
+// rounded down to kWindowAlign.
+int64_t copied_prefix(const muse_attn_layer* l, int32_t max_seq_len) {
+    int64_t prefix = max_seq_len;
+    const int64_t win = (int64_t)l->window - 1 + (muse::kWindowAlign - 1);
+    if (l->kind == MUSE_SLIDING_ROPE && win < prefix) prefix = win;
+    return prefix;
+}
+
+// Rows the cache must hold: every position of the call, or on a ring layer
+// the last min(window, positions) of them.
+int64_t rows_needed(const muse_attn_layer* l, int32_t max_seq_len, int32_t n_new) {
+    const int64_t need = (int64_t)max_seq_len + n_new;
+    return l->kv_ring ? (need < l->window ? need : (int64_t)l->window) : need;
 }
 
 muse_status check_sizes(int32_t n_seq, int32_t n_new, int32_t max_seq_len) {
@@ -96,11 +116,16 @@ void decode_split(const muse_attn_layer* l, int32_t n_seq, int32_t max_seq_len,
 }
 
 // Prefill: on f32 layers Q-hat [S][N][32][128]; on bf16 layers (where the
-// attention kernel makes Q-hat itself) the fp16 key copy [S][max_seq_len + N][2][128].
+// attention kernel makes Q-hat itself) the fp16 copy of the keys the chunk can
+// see, [S][kq_capacity][2][128]: on full layers row = position (kq_capacity =
+// max_seq_len + N), on sliding layers row = position - base with base =
+// max(0, seq_len - window + 1) rounded down to kWindowAlign (kq_capacity =
+// min(max_seq_len, window - 1 + kWindowAlign - 1) + N); on ring layers then a
+// copy of the same rows of V, laid out alike.
 // Decode: arrival words [S][2][kArriveWords] (u64), ready words [S][2][kReadyWords]
 // (u32), then the split partials O [S][32][nsplit][128], m and l [S][32][nsplit].
 struct WorkspaceLayout {
-    size_t qhat = 0, kq = 0, arrivals = 0, ready = 0, part_o = 0, part_m = 0, part_l = 0, total = 0;
+    size_t qhat = 0, kq = 0, vq = 0, arrivals = 0, ready = 0, part_o = 0, part_m = 0, part_l = 0, total = 0;
     int64_t kq_capacity = 0;
     int32_t chunk = 0, nsplit = 0;
 };
@@ -116,8 +141,13 @@ WorkspaceLayout layout_for(const muse_attn_layer* l, int32_t n_seq, int32_t n_ne
         if (l->dtype != MUSE_BF16) off = round_up((size_t)n_seq * n_new * kHeads * kHeadDim * es, kAlign);
         if (l->dtype == MUSE_BF16) {
             w.kq = off;
-            w.kq_capacity = (int64_t)max_seq_len + n_new;
-            off += round_up((size_t)n_seq * (size_t)w.kq_capacity * kKvHeads * kHeadDim * 2, kAlign);
+            w.kq_capacity = copied_prefix(l, max_seq_len) + n_new;
+            const size_t rows_bytes = round_up((size_t)n_seq * (size_t)w.kq_capacity * kKvHeads * kHeadDim * 2, kAlign);
+            off += rows_bytes;
+            if (l->kv_ring) {                          // V rows the chunk can see, out of the ring
+                w.vq = off;
+                off += rows_bytes;
+            }
         }
     } else {
         w.arrivals = 0;
@@ -169,7 +199,7 @@ muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, cons
     if ((st = check_sizes(n_seq, n_new, max_seq_len)) != MUSE_OK) return st;
     if (!cache) return MUSE_ERR_NULL;
     if (cache->capacity < 0) return MUSE_ERR_CAPACITY;
-    if ((int64_t)max_seq_len + n_new > cache->capacity) return MUSE_ERR_CAPACITY;
+    if (rows_needed(layer, max_seq_len, n_new) > cache->capacity) return MUSE_ERR_CAPACITY;
     if (n_seq == 0 || n_new == 0) return MUSE_OK;    // nothing to do
     if (!seq_len || !q || !k || !v || !gate || !out || !cache->k || !cache->v || !workspace)
         return MUSE_ERR_NULL;
@@ -220,6 +250,7 @@ muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, cons
         da.max_seq_len = max_seq_len;
         da.n_seq = n_seq;
         da.window = rope ? layer->window : 0;
+        da.ring = layer->kv_ring ? cache->capacity : 0;
         da.rope = rope ? 1 : 0;
         da.eps = layer->rms_eps;
         da.q_gain = layer->q_norm_gain;
@@ -261,13 +292,13 @@ muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, cons
     pa.skip_q = layer->dtype == MUSE_BF16 ? 1 : 0;
     pa.window = rope ? layer->window : 0;
     if (layer->dtype == MUSE_BF16) {
-        // prefix rows the chunk can see: [0, L) on full layers, at most
-        // window - 1 rows below L on sliding layers
-        int64_t prefix = max_seq_len;
-        if (rope && (int64_t)layer->window - 1 < prefix) prefix = (int64_t)layer->window - 1;
+        // prefix rows the key copy holds (see copied_prefix), 64 per workgroup
         pa.kq = ws + wl.kq;
         pa.kq_capacity = wl.kq_capacity;
-        pa.conv_blocks = (int32_t)((prefix + 63) / 64);
+        pa.conv_blocks = (int32_t)((copied_prefix(layer, max_seq_len) + 63) / 64);
+        pa.kq_windowed = rope ? 1 : 0;
+        pa.ring = layer->kv_ring ? cache->capacity : 0;
+        pa.vq = layer->kv_ring ? (void*)(ws + wl.vq) : nullptr;
     }
     if (rope) rope_table(layer->rope_theta, pa.theta);
 
@@ -284,14 +315,23 @@ muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, cons
     aa.out = out;
     aa.kq = layer->dtype == MUSE_BF16 ? (const void*)(ws + wl.kq) : cache->k;
     aa.kq_capacity = layer->dtype == MUSE_BF16 ? wl.kq_capacity : cache->capacity;
-    aa.cache_v = cache->v;
-    aa.capacity = cache->capacity;
+    aa.cache_v = layer->kv_ring ? (const void*)(ws + wl.vq) : cache->v;
+    aa.capacity = layer->kv_ring ? wl.kq_capacity : cache->capacity;
+    aa.kq_windowed = pa.kq_windowed;
+    aa.v_windowed = layer->kv_ring ? 1 : 0;
     aa.seq_len = seq_len;
     aa.max_seq_len = max_seq_len;
     aa.n_seq = n_seq;
     aa.n_new = n_new;
     aa.window = rope ? layer->window : 0;
 
+    if (layer->kv_ring) {
+        // the visible prefix is copied out of the ring before any new row
+        // overwrites a slot it reads
+        pa.phase = 1;
+        if (muse::launch_prep(pa, dt, stream) != hipSuccess) return MUSE_ERR_HIP;
+        pa.phase = 2;
+    }
     if (muse::launch_prep(pa, dt, stream) != hipSuccess) return MUSE_ERR_HIP;
     if (timer && hipEventRecord(timer->start, stream) != hipSuccess) return MUSE_ERR_HIP;
     if (muse::launch_prefill(aa, dt, stream) != hipSuccess) return MUSE_ERR_HIP;
@@ -350,6 +390,7 @@ muse_status muse_attn_layer_init(muse_attn_layer* layer, int32_t layer_index, in
     l.k_norm_gain = 1.0f;
     l.attn_scale = (float)(1.0 / std::sqrt(128.0));
     l.dtype = dtype;
+    l.kv_ring = 0;
     *layer = l;
     return MUSE_OK;
 }

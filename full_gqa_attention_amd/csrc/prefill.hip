@@ -501,8 +501,14 @@ void prefill_group_kernel(AttnArgs a) {
     constexpr int64_t ROW = (int64_t)kKvHeads * D * ES;
     constexpr int RSTEP = NT / CPR;
     const int r_t = tid / CPR, c_t = tid % CPR;
-    const char* kbase = (const char*)a.kq + (((int64_t)s * a.kq_capacity) * kKvHeads + g) * D * ES + c_t * 16;
-    const char* vbase = (const char*)a.cache_v + (((int64_t)s * a.capacity) * kKvHeads + g) * D * ES + c_t * 16;
+    // rows of the K copy (and of V on ring layers) start on sliding layers at
+    // the window's first visible position rounded down to kWindowAlign; every
+    // tile read here starts at or past that (tiles start at multiples of BN,
+    // which divides kWindowAlign)
+    static_assert(kWindowAlign % BN == 0, "key tiles start inside the windowed copy");
+    const int64_t win0 = W > 0 ? max(0, L - W + 1) / kWindowAlign * kWindowAlign : 0;
+    const char* kbase = (const char*)a.kq + ((((int64_t)s * a.kq_capacity) - (a.kq_windowed ? win0 : 0)) * kKvHeads + g) * D * ES + c_t * 16;
+    const char* vbase = (const char*)a.cache_v + ((((int64_t)s * a.capacity) - (a.v_windowed ? win0 : 0)) * kKvHeads + g) * D * ES + c_t * 16;
     u32x4 kreg[NCH], vreg[NCH];
     // Tile rows into registers.  Rows past the last cached position are
     // clamped to it (in-bounds, finite data): every key there lies after

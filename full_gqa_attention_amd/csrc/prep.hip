@@ -66,20 +66,37 @@ __device__ __forceinline__ void store8(T* p, const float (&y)[8]) {
     }
 }
 
-// Rows [lo, L) of sequence s that the chunk's queries can see, 64 rows per
-// workgroup: bf16 cache -> fp16 score copy (exact for the normed keys).
+// First position held by the fp16 key copy (and the ring layers' V copy) of
+// a sequence with L cached rows: on sliding layers the window's first
+// visible position rounded down to kWindowAlign, else 0.
+__device__ __forceinline__ int copy_base(const PrepArgs& a, int L) {
+    return a.kq_windowed ? max(0, L - a.window + 1) / kWindowAlign * kWindowAlign : 0;
+}
+__device__ __forceinline__ int64_t copy_row(const PrepArgs& a, int L, int64_t j) {
+    return j - copy_base(a, L);
+}
+// Cache row of position j: j, or j % ring on a ring layer.
+__device__ __forceinline__ int64_t cache_row(const PrepArgs& a, int64_t j) {
+    return a.ring ? j % a.ring : j;
+}
+
+// Positions [copy_base, L) of sequence s (the ones the chunk's queries can
+// see, and up to kWindowAlign - 1 before them), 64 per workgroup: bf16 cache
+// -> fp16 score copy (exact for the normed keys); on ring layers V is copied
+// out of the ring as well.  (Positions before the window are masked; their
+// rows are copied so that every row the attention kernel loads is data.)
 __device__ __forceinline__ void convert_prefix(const PrepArgs& a, int idx) {
     const int s = idx / a.conv_blocks, blk = idx % a.conv_blocks;
     const int L = a.seq_len[s];
     if (L < 0 || L > a.max_seq_len) return;
-    const int lo = a.window > 0 ? max(0, L - a.window + 1) : 0;
-    const int r0 = lo + 64 * blk;
+    const int r0 = copy_base(a, L) + 64 * blk;
     for (int c = threadIdx.x; c < 64 * 32; c += 256) {   // 32 chunks of 16 B per position
-        const int row = r0 + c / 32, piece = c % 32;
-        if (row >= L) break;
-        const int64_t e = ((int64_t)s * a.capacity + row) * kKvHeads * kHeadDim + piece * 8;
-        const int64_t f = ((int64_t)s * a.kq_capacity + row) * kKvHeads * kHeadDim + piece * 8;
+        const int pos = r0 + c / 32, piece = c % 32;
+        if (pos >= L) break;
+        const int64_t e = ((int64_t)s * a.capacity + cache_row(a, pos)) * kKvHeads * kHeadDim + piece * 8;
+        const int64_t f = ((int64_t)s * a.kq_capacity + copy_row(a, L, pos)) * kKvHeads * kHeadDim + piece * 8;
         *(u32x4*)((f16_t*)a.kq + f) = k_chunk_to_score(*(const u32x4*)((const bf16_t*)a.cache_k + e), bf16_t{});
+        if (a.vq) *(u32x4*)((bf16_t*)a.vq + f) = *(const u32x4*)((const bf16_t*)a.cache_v + e);
     }
 }
 
@@ -118,9 +135,14 @@ __device__ __forceinline__ void prep_kv_bf16(const PrepArgs& a, int blk) {
         const int L = Ls[i];
         if (L < 0 || L > a.max_seq_len) continue;  // refused (the attention kernel writes NaN)
         const int64_t p = (int64_t)L + t;
-        const int64_t row = ((int64_t)s * a.capacity + p) * kKvHeads + hk;
+        // ring layers keep only the last `ring` positions of the chunk: an
+        // earlier one would share a row with a later one
+        const bool to_cache = !a.ring || t >= a.n_new - a.ring;
+        const int64_t row = ((int64_t)s * a.capacity + cache_row(a, p)) * kKvHeads + hk;
+        const int64_t qrow = ((int64_t)s * a.kq_capacity + copy_row(a, L, p)) * kKvHeads + hk;
         if (!is_k) {                               // V: exact copy
-            *(u32x4*)((bf16_t*)a.cache_v + row * kHeadDim + 8 * sub) = raw[i];
+            if (to_cache) *(u32x4*)((bf16_t*)a.cache_v + row * kHeadDim + 8 * sub) = raw[i];
+            if (a.vq) *(u32x4*)((bf16_t*)a.vq + qrow * kHeadDim + 8 * sub) = raw[i];
         }
         const bf16x8 kx = __builtin_bit_cast(bf16x8, raw[i]);
         float y[8];
@@ -151,9 +173,8 @@ __device__ __forceinline__ void prep_kv_bf16(const PrepArgs& a, int blk) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) kv[j] = from_f32<bf16_t>(y[j]);
             const u32x4 kr = __builtin_bit_cast(u32x4, kv);
-            *(u32x4*)((bf16_t*)a.cache_k + row * kHeadDim + 8 * sub) = kr;
+            if (to_cache) *(u32x4*)((bf16_t*)a.cache_k + row * kHeadDim + 8 * sub) = kr;
             // the score copy holds the stored values
-            const int64_t qrow = ((int64_t)s * a.kq_capacity + p) * kKvHeads + hk;
             *(u32x4*)((f16_t*)a.kq + qrow * kHeadDim + 8 * sub) = k_chunk_to_score(kr, bf16_t{});
         }
     }
@@ -166,7 +187,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     typedef typename ScoreType<T>::type TQ;
     __shared__ float2 rot[64];                     // (cos, sin) of pair i at this token's position
     const int n_tok = a.n_seq * a.n_new;
-    const int n_main = a.skip_q ? prep_kv_blocks(n_tok) : n_tok;
+    const int n_main = a.phase == 1 ? 0 : a.skip_q ? prep_kv_blocks(n_tok) : n_tok;
     if ((int)blockIdx.x >= n_main) {               // fp16 copy of visible prefix keys
         if constexpr (sizeof(T) == 2) convert_prefix(a, (int)blockIdx.x - n_main);
         return;
@@ -199,7 +220,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         if (vec >= kHeads + kKvHeads) {            // V: exact copy
             const int g = vec - kHeads - kKvHeads;
             const T* src = (const T*)a.v + ((int64_t)tok * kKvHeads + g) * kHeadDim + 8 * sub;
-            T* dst = (T*)a.cache_v + (((int64_t)s * a.capacity + p) * kKvHeads + g) * kHeadDim + 8 * sub;
+            T* dst = (T*)a.cache_v + (((int64_t)s * a.capacity + cache_row(a, p)) * kKvHeads + g) * kHeadDim + 8 * sub;
             *(u32x4*)dst = *(const u32x4*)src;
             if constexpr (sizeof(T) == 4) *(u32x4*)(dst + 4) = *(const u32x4*)(src + 4);
             continue;
@@ -233,7 +254,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
             store8((TQ*)a.qhat + ((int64_t)tok * kHeads + vec) * kHeadDim + 8 * sub, y);
         } else {
             const int g = vec - kHeads;
-            T* dst = (T*)a.cache_k + (((int64_t)s * a.capacity + p) * kKvHeads + g) * kHeadDim + 8 * sub;
+            T* dst = (T*)a.cache_k + (((int64_t)s * a.capacity + cache_row(a, p)) * kKvHeads + g) * kHeadDim + 8 * sub;
             if constexpr (sizeof(T) == 2) {
                 bf16x8 kv;
 #pragma unroll
@@ -241,7 +262,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
                 const u32x4 raw = __builtin_bit_cast(u32x4, kv);
                 *(u32x4*)dst = raw;
                 // the score copy holds the stored values
-                TQ* kq = (TQ*)a.kq + (((int64_t)s * a.kq_capacity + p) * kKvHeads + g) * kHeadDim + 8 * sub;
+                TQ* kq = (TQ*)a.kq + (((int64_t)s * a.kq_capacity + copy_row(a, L, p)) * kKvHeads + g) * kHeadDim + 8 * sub;
                 *(u32x4*)kq = k_chunk_to_score(raw, T{});
             } else {
                 store8(dst, y);
@@ -252,8 +273,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 
 hipError_t launch_prep(const PrepArgs& a, int dtype, hipStream_t stream) {
     const int n_tok = a.n_seq * a.n_new;
-    const int n_main = a.skip_q ? prep_kv_blocks(n_tok) : n_tok;
-    const dim3 grid((unsigned)(n_main + a.n_seq * a.conv_blocks)), block(256);
+    const int n_main = a.phase == 1 ? 0 : a.skip_q ? prep_kv_blocks(n_tok) : n_tok;
+    const int n_conv = a.phase == 2 ? 0 : a.n_seq * a.conv_blocks;
+    if (n_main + n_conv == 0) return hipSuccess;
+    const dim3 grid((unsigned)(n_main + n_conv)), block(256);
     if (dtype == 1)
         hipLaunchKernelGGL(prep_kernel<bf16_t>, grid, block, 0, stream, a);
     else

@@ -14,6 +14,9 @@
  *      14.4.2, 14.5; Ch 9, 9.7]
  *   3. KV append: cache row p of KV head g receives the normed (and rotated)
  *      K and the raw V.  [Ch 14, 14.7: keys are rotated before they are stored]
+ *      On a layer with kv_ring set the cache is a ring: position p lives in
+ *      row p % capacity.  ["Chapter 9 - The Muse Glimmer architecture" 9.7:
+ *      each sliding layer keeps a fixed 2,048-row ring, token-major]
  *   4. Causal GQA attention: query head h reads KV head h / 16; key j is
  *      visible iff j <= p and, on sliding layers, p - j < window; scores are
  *      (q . k) * attn_scale; softmax; weighted sum of V.  [Ch 9, 9.5, 9.6
@@ -32,11 +35,17 @@
  *       q          [n_seq][n_new][32][128]
  *       k, v       [n_seq][n_new][2][128]
  *       gate, out  [n_seq][n_new][4096]      (channel = head * 128 + dim)
- *       cache k, v [n_seq][capacity][2][128] (token-major; row = position)
+ *       cache k, v [n_seq][capacity][2][128] (token-major; row = position,
+ *                                             or position % capacity on a
+ *                                             kv_ring layer)
  *       seq_len    int32 [n_seq]             (rows already cached)
  *     Every pointer must be 16-byte aligned.
  *   - Inputs q, k, v, gate and seq_len are read-only.  Cache rows
  *     [seq_len[s], seq_len[s] + n_new) are written; other rows are only read.
+ *     On a kv_ring layer the rows written are those of the last
+ *     min(n_new, capacity) new positions (earlier ones would be overwritten
+ *     by later ones of the same call); the chunk's queries still see every
+ *     new key in their window.
  *     seq_len is not advanced: the caller does that after the call.
  *   - out must not overlap any other buffer; workspace must not overlap any
  *     other buffer.
@@ -65,7 +74,7 @@ typedef enum {
     MUSE_ERR_NULL = 1,      /* a required pointer is NULL                        */
     MUSE_ERR_SHAPE = 2,     /* head counts, head_dim or a size out of range      */
     MUSE_ERR_LAYER = 3,     /* kind/window/theta/eps/gain/scale inconsistent     */
-    MUSE_ERR_CAPACITY = 4,  /* max_seq_len + n_new > capacity                    */
+    MUSE_ERR_CAPACITY = 4,  /* capacity too small (see muse_kv_cache)            */
     MUSE_ERR_WORKSPACE = 5, /* workspace_bytes below muse_attn_workspace_size    */
     MUSE_ERR_DTYPE = 6,     /* dtype is not MUSE_F32 / MUSE_BF16                 */
     MUSE_ERR_HIP = 7,       /* a HIP launch or event call failed                 */
@@ -94,7 +103,11 @@ typedef enum { MUSE_SLIDING_ROPE = 0, MUSE_FULL_NOPE = 1 } muse_layer_kind;
  *               65504.  Cache K rows not written by this library must also
  *               stay below 65504 in magnitude.)
  *   attn_scale  finite and > 0 (1/sqrt(128); ["Chapter 9" 9.5])
- *   dtype       muse_dtype of activations, cache and output               */
+ *   dtype       muse_dtype of activations, cache and output
+ *   kv_ring     0: the cache row of position p is p.  1 (sliding bf16 layers
+ *               only, else MUSE_ERR_LAYER): the cache is a ring of capacity
+ *               rows and position p lives in row p % capacity, so a sliding
+ *               layer needs only window rows per sequence ["Chapter 9" 9.7] */
 typedef struct {
     int32_t n_heads;
     int32_t n_kv_heads;
@@ -107,10 +120,13 @@ typedef struct {
     float k_norm_gain;
     float attn_scale;
     int32_t dtype;
+    int32_t kv_ring;
 } muse_attn_layer;
 
 /* Contiguous per-sequence KV cache: k and v are DEVICE pointers to
- * [n_seq][capacity][2][128] arrays of the layer dtype; capacity is in rows. */
+ * [n_seq][capacity][2][128] arrays of the layer dtype; capacity is in rows.
+ * A call needs capacity >= max_seq_len + n_new, or on a kv_ring layer
+ * capacity >= min(window, max_seq_len + n_new) (else MUSE_ERR_CAPACITY). */
 typedef struct {
     void* k;
     void* v;
@@ -133,7 +149,7 @@ typedef struct {
  *   n_seq        >= 0 sequences;  n_new >= 0 new tokens per sequence
  *   seq_len      device int32[n_seq]: rows already cached
  *   max_seq_len  host upper bound of every seq_len[s]; sizes the grid and
- *                the capacity check (max_seq_len + n_new <= capacity)
+ *                the capacity check (see muse_kv_cache)
  *   q, k, v, gate, out   device, layouts above
  *   cache        host pointer to the cache descriptor
  *   workspace    device scratch of at least muse_attn_workspace_size(...)
@@ -175,7 +191,7 @@ muse_status muse_attn_workspace_size(const muse_attn_layer* layer, int32_t n_seq
 /* Fill *layer (host) with the model's parameters for layer `layer_index`
  * (0 <= layer_index < 52): kind by the l % 4 == 3 rule, window 2048 and
  * theta 500000 on sliding layers (0 and 0 on full layers), eps 1e-5, gains
- * 3.87 / 1.0, scale 1/sqrt(128), and the given dtype.
+ * 3.87 / 1.0, scale 1/sqrt(128), the given dtype, and kv_ring 0.
  * ["Chapter 9" 9.4, 9.7; "Chapter 14" 14.3] */
 muse_status muse_attn_layer_init(muse_attn_layer* layer, int32_t layer_index, int32_t dtype);
 

@@ -192,6 +192,36 @@ def test_validation_layer_kinds(lib, decode):
     assert f.call(lib) == NULL
 
 
+@pytest.mark.parametrize("decode", [False, True])
+def test_validation_ring(lib, decode):
+    """kv_ring: sliding bf16 layers only; the ring needs min(window,
+    max_seq_len + n_new) rows, a linear cache every position."""
+    for kind, dtype, ring in ((fa.FULL_NOPE, fa.BF16, 1), (fa.SLIDING_ROPE, fa.F32, 1),
+                              (fa.SLIDING_ROPE, fa.BF16, 2), (fa.SLIDING_ROPE, fa.BF16, -1)):
+        f = Fake(decode=decode, kind=kind, dtype=dtype)
+        f.layer.kv_ring = ring
+        assert f.call(lib) == LAYER, (kind, dtype, ring)
+    # a ring of window - 1 rows cannot hold the window once positions pass it
+    f = Fake(decode=decode)
+    f.layer.kv_ring = 1
+    f.cache.capacity = 2047
+    f.max_seq_len = 10000
+    f.ws = 0                         # would be NULL -- but the capacity check comes first
+    assert f.call(lib) == CAPACITY
+    # ... and the same cache without the ring cannot hold the positions either
+    f = Fake(decode=decode)
+    f.cache.capacity = 2048
+    f.max_seq_len = 10000
+    assert f.call(lib) == CAPACITY
+    # short sequences need only their positions, even on a ring layer
+    f = Fake(decode=decode)
+    f.layer.kv_ring = 1
+    f.cache.capacity = 200
+    f.max_seq_len = 100
+    f.ws = 0
+    assert f.call(lib) == NULL       # passes the capacity check, stops at the NULL workspace
+
+
 def test_empty_batches_are_valid_noops(lib):
     f = Fake()
     f.n_seq = 0
@@ -210,6 +240,13 @@ def test_workspace_sizes():
     # the attention kernel); f32 prefill: Q-hat
     assert fa.workspace_size(lay, 8, 8192, 0, False) == 8 * 8192 * 256 * 2
     assert fa.workspace_size(lay, 4, 4096, 32768, False) == 4 * 36864 * 256 * 2
+    # sliding bf16 layers copy only the window's keys (the window - 1 prefix rows, from a
+    # start rounded down to 64 rows, + the chunk); ring layers copy the same rows of V too
+    sl16 = fa.make_layer(fa.SLIDING_ROPE, window=2048, rope_theta=5e5, dtype=fa.BF16)
+    assert fa.workspace_size(sl16, 4, 4096, 32768, False) == 4 * (2047 + 63 + 4096) * 256 * 2
+    assert fa.workspace_size(sl16, 4, 4096, 100, False) == 4 * (100 + 4096) * 256 * 2
+    ring = fa.make_layer(fa.SLIDING_ROPE, window=2048, rope_theta=5e5, dtype=fa.BF16, kv_ring=1)
+    assert fa.workspace_size(ring, 4, 4096, 32768, False) == 2 * 4 * (2047 + 63 + 4096) * 256 * 2
     f32 = fa.make_layer(fa.FULL_NOPE, dtype=fa.F32)
     assert fa.workspace_size(f32, 1, 512, 0, False) == 512 * 4096 * 4
     d1 = fa.workspace_size(lay, 64, 1, 8192, True)
