@@ -153,6 +153,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--schedule", action="store_true",
                     help="also time the 52-layer schedule workload (chunked prefill phase + 256 decode steps)")
+    ap.add_argument("--ring", action="store_true",
+                    help="sliding layers keep their window in a ring cache (kv_ring) in the decode and schedule runs")
     ap.add_argument("--eager", action="store_true",
                     help="time decode steps as eager calls only (no HIP graph), e.g. under counter collection")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -174,17 +176,38 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def ring_of(cache, L: int, cap: int):
+    """A ring of `cap` rows holding positions [L - cap, L) of every sequence
+    at row p % cap (the same stored rows as the linear cache)."""
+    import torch
+    ring = torch.empty((cache.shape[0], cap) + tuple(cache.shape[2:]), dtype=cache.dtype, device=cache.device)
+    pos = torch.arange(max(0, L - cap), L, device=cache.device)
+    ring[:, pos % cap] = cache[:, pos]
+    if L < cap:
+        ring[:, L:] = 0
+    return ring
+
+
+def uses_ring(spec, ring: bool, synth) -> bool:
+    return ring and spec.kind == synth.SLIDING_ROPE
+
+
 class LayerRun:
-    def __init__(self, w, spec, copies, decode, fa, synth):
+    def __init__(self, w, spec, copies, decode, fa, synth, ring=False):
         import torch
         self.spec = spec
         self.inp = synth.layer_inputs(w, spec, device="cuda", backend="torch")
+        self.ring = uses_ring(spec, ring, synth) and decode
+        if self.ring:                                 # the window's rows only, as a ring
+            self.inp.cache_k = ring_of(self.inp.cache_k, w.prefix, spec.window)
+            self.inp.cache_v = ring_of(self.inp.cache_v, w.prefix, spec.window)
         self.caches = [(self.inp.cache_k, self.inp.cache_v)]
         for _ in range(1, copies):
             self.caches.append((self.inp.cache_k.clone(), self.inp.cache_v.clone()))
         self.layer = fa.make_layer(spec.kind, window=spec.window, rope_theta=spec.rope_theta,
                                    rms_eps=spec.rms_eps, q_norm_gain=spec.q_gain,
-                                   k_norm_gain=spec.k_gain, attn_scale=spec.scale, dtype=w.dtype)
+                                   k_norm_gain=spec.k_gain, attn_scale=spec.scale, dtype=w.dtype,
+                                   kv_ring=1 if self.ring else 0)
         self.decode = decode
         self.ws = fa.workspace(self.layer, w.n_seq, w.n_new, w.prefix, decode)
         self.out = torch.empty_like(self.inp.gate)
@@ -246,7 +269,7 @@ def bench_decode(w, args, fa, synth, torch):
     copies = min(copies, 8)
     log(f"decode {w.name}: {len(w.layers)} layers, {copies} cache copies, "
         f"{per_step_unique / 1e6:.1f} MB KV per step")
-    runs = [LayerRun(w, spec, copies, True, fa, synth) for spec in w.layers]
+    runs = [LayerRun(w, spec, copies, True, fa, synth, ring=args.ring) for spec in w.layers]
     torch.cuda.synchronize()
     wall_eager, per_launch = run_timed(runs, args.steps, args.warmup, copies, fa, torch)
     wall = wall_eager if args.eager else run_graphs(runs, args.steps, args.warmup, copies, fa, torch)
@@ -281,7 +304,7 @@ def bench_decode(w, args, fa, synth, torch):
                    "layers": [f"{s.name}" + (f"_w{s.window}_theta{int(s.rope_theta)}" if s.window else "_nope")
                               for s in w.layers],
                    "q_heads": 32, "kv_heads": 2, "head_dim": 128, "cache_copies": copies,
-                   "kv_bytes_per_step": kv_per_step},
+                   "kv_bytes_per_step": kv_per_step, "kv_ring_sliding": bool(args.ring)},
     }
     return res, runs
 
@@ -316,11 +339,12 @@ def bench_prefill(w, steps, warmup, fa, synth, torch):
     }
 
 
-def bench_schedule(w, fa, synth, torch):
+def bench_schedule(w, fa, synth, torch, ring=False):
     """The 52-layer schedule workload: 4 sequences with 32,768 cached rows per
     layer, a 4,096-token chunked prefill through all 52 layers (timed as one
     phase, eager calls), then 256 decode steps of all 52 layers (one step =
-    52 decode calls and the seq_len increment, replayed from a HIP graph)."""
+    52 decode calls and the seq_len increment, replayed from a HIP graph).
+    ring: the sliding layers keep their window in a ring of `window` rows."""
     S, L0, N, steps = w.n_seq, w.prefix, w.n_new, w.decode_steps
     extra = 4                                          # warm-up decode steps, rows overwritten later
     cap = L0 + N + steps + extra
@@ -328,17 +352,24 @@ def bench_schedule(w, fa, synth, torch):
     log(f"schedule {w.name}: {len(w.layers)} layers, capacity {cap}")
     layers, inputs, outs, dec_in = [], [], [], []
     for spec in w.layers:
-        inp = synth.layer_inputs(w, spec, device="cuda", backend="torch", capacity=cap)
+        r = uses_ring(spec, ring, synth)
+        inp = synth.layer_inputs(w, spec, device="cuda", backend="torch",
+                                 capacity=L0 if r else cap)
+        if r:
+            inp.cache_k = ring_of(inp.cache_k, L0, spec.window)
+            inp.cache_v = ring_of(inp.cache_v, L0, spec.window)
         layers.append(fa.make_layer(spec.kind, window=spec.window, rope_theta=spec.rope_theta,
                                     rms_eps=spec.rms_eps, q_norm_gain=spec.q_gain,
-                                    k_norm_gain=spec.k_gain, attn_scale=spec.scale, dtype=w.dtype))
+                                    k_norm_gain=spec.k_gain, attn_scale=spec.scale, dtype=w.dtype,
+                                    kv_ring=1 if r else 0))
         inputs.append(inp)
         outs.append(torch.empty_like(inp.gate))
         d = synth.layer_inputs(w, spec, device="cuda", backend="torch", n_new=1, prefix=0,
                                step=1, with_cache=False)
         dec_in.append((d.q, d.k, d.v, d.gate, torch.empty_like(d.gate)))
     seq_len = torch.full((S,), L0, dtype=torch.int32, device="cuda")
-    ws_p = fa.workspace(layers[0], S, N, L0, False)
+    ws_p = torch.empty(max(fa.workspace_size(lay, S, N, L0, False) for lay in layers),
+                       dtype=torch.uint8, device="cuda")
     ws_d = torch.empty(max(fa.workspace_size(lay, S, 1, max_dec, True) for lay in layers),
                        dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
@@ -373,7 +404,9 @@ def bench_schedule(w, fa, synth, torch):
     kv = sum(kv_row_bytes(w.dtype) * S * visible_rows(spec, L0 + N + i)
              for i in range(steps) for spec in w.layers)
     del graph
+    cache_bytes = sum(2 * inp.cache_k.numel() * inp.cache_k.element_size() for inp in inputs)
     return {"workload": w.name, "layers": len(w.layers), "n_seq": S,
+            "kv_ring_sliding": bool(ring), "kv_cache_GB": round(cache_bytes / 1e9, 3),
             "prefill": {"tokens_per_seq": N, "at_position": L0, "ms": round(t_prefill * 1e3, 2),
                         "tflop": round(flops / 1e12, 3), "TFLOPs": round(flops / t_prefill / 1e12, 1),
                         "frac_mfma_peak": round(flops / t_prefill / 1e12 / MFMA_PEAK_TFLOPS, 4),
@@ -471,7 +504,8 @@ def main():
         line["prefill"] = bench_prefill(pw, args.prefill_steps, 2, fa, synth, torch)
     if args.schedule:
         torch.cuda.empty_cache()
-        line["schedule"] = bench_schedule(synth.WORKLOADS["schedule_52x4_32768p4096_256d"], fa, synth, torch)
+        line["schedule"] = bench_schedule(synth.WORKLOADS["schedule_52x4_32768p4096_256d"], fa, synth, torch,
+                                          ring=args.ring)
     print(json.dumps(line), flush=True)
 
 
