@@ -155,6 +155,8 @@ def parse():
                     help="also time the 52-layer schedule workload (chunked prefill phase + 256 decode steps)")
     ap.add_argument("--ring", action="store_true",
                     help="sliding layers keep their window in a ring cache (kv_ring) in the decode and schedule runs")
+    ap.add_argument("--relocate", action="store_true",
+                    help="also time NoPE tile relocation (muse_kv_relocate) of a 64 x 8,192 full-layer cache")
     ap.add_argument("--eager", action="store_true",
                     help="time decode steps as eager calls only (no HIP graph), e.g. under counter collection")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -417,6 +419,43 @@ def bench_schedule(w, fa, synth, torch, ring=False):
                        "launch": "each step (52 decode calls + seq_len increment) replayed from a HIP graph"}}
 
 
+def bench_relocate(fa, synth, torch, steps=10):
+    """NoPE tile relocation ("Chapter 14 - QK-norm and RoPE" 14.6): the whole
+    cache of a full layer of the 64 x 8,192 decode workload, moved as 512-row
+    tiles from one cache to another (K and V; 1,024 tiles per pass)."""
+    S, L, T = 64, 8192, 512
+    spec = synth.full()
+    lay = fa.make_layer(spec.kind, dtype=synth.BF16)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    a_k = torch.randn((S, L, 2, 128), generator=g, device="cuda").to(torch.bfloat16)
+    a_v = torch.randn((S, L, 2, 128), generator=g, device="cuda").to(torch.bfloat16)
+    b_k, b_v = torch.empty_like(a_k), torch.empty_like(a_v)
+    # each sequence's tiles land reversed in another sequence, so no tile is a plain block copy of the whole cache
+    tiles = fa.kv_tiles([(s, i * T, (s + 1) % S, (L // T - 1 - i) * T, T) for s in range(S) for i in range(L // T)])
+    fa.kv_relocate(lay, a_k, a_v, b_k, b_v, tiles)
+    torch.cuda.synchronize()
+    # GPU time of one pass between events (the host builds and checks the
+    # tile list before enqueueing; that is timed separately)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gpu_ms = []
+    host = 0.0
+    for _ in range(steps):
+        t0 = time.perf_counter()
+        e0.record()
+        fa.kv_relocate(lay, a_k, a_v, b_k, b_v, tiles)
+        e1.record()
+        host += time.perf_counter() - t0
+        torch.cuda.synchronize()
+        gpu_ms.append(e0.elapsed_time(e1))
+    dt = sorted(gpu_ms)[len(gpu_ms) // 2] * 1e-3
+    moved = 2 * a_k.numel() * a_k.element_size()           # K and V bytes per pass
+    ok = bool(torch.equal(b_k[1, (L // T - 1) * T:], a_k[0, :T]))
+    return {"tiles": tiles[1], "tile_rows": T, "MB_moved": round(moved / 1e6, 1), "gpu_ms": round(dt * 1e3, 3),
+            "host_ms_per_call": round(host / steps * 1e3, 3),
+            "GBps_read_plus_write": round(2 * moved / dt / 1e9, 1),
+            "frac_hbm_peak": round(2 * moved / dt / 1e9 / HBM_PEAK_GBS, 4), "bytes_checked": ok}
+
+
 def cpu_baseline_decode(w, runs, synth, torch):
     """Time the CPU oracle on this step's inputs (all rows of both layers) and
     check the benchmarked GPU output against it."""
@@ -502,6 +541,9 @@ def main():
     if not args.no_prefill:
         pw = synth.WORKLOADS[args.prefill_workload]
         line["prefill"] = bench_prefill(pw, args.prefill_steps, 2, fa, synth, torch)
+    if args.relocate:
+        torch.cuda.empty_cache()
+        line["relocate"] = bench_relocate(fa, synth, torch)
     if args.schedule:
         torch.cuda.empty_cache()
         line["schedule"] = bench_schedule(synth.WORKLOADS["schedule_52x4_32768p4096_256d"], fa, synth, torch,

@@ -31,7 +31,7 @@ STATUS = {0: "MUSE_OK", 1: "MUSE_ERR_NULL", 2: "MUSE_ERR_SHAPE", 3: "MUSE_ERR_LA
 
 EXPORTS = ("muse_attn_prefill", "muse_attn_decode", "muse_attn_workspace_size",
            "muse_attn_layer_init", "muse_layer_kind_for", "muse_rope_theta_table",
-           "muse_status_str")
+           "muse_status_str", "muse_kv_relocate")
 
 
 class MuseError(RuntimeError):
@@ -53,6 +53,12 @@ class Layer(ctypes.Structure):
 class KvCache(ctypes.Structure):
     """muse_kv_cache."""
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("capacity", ctypes.c_int64)]
+
+
+class KvTile(ctypes.Structure):
+    """muse_kv_tile."""
+    _fields_ = [("src_seq", ctypes.c_int32), ("dst_seq", ctypes.c_int32), ("src_pos", ctypes.c_int64),
+                ("dst_pos", ctypes.c_int64), ("n_rows", ctypes.c_int64)]
 
 
 class KernelTimer(ctypes.Structure):
@@ -91,6 +97,9 @@ def lib() -> ctypes.CDLL:
         L.muse_rope_theta_table.restype = ctypes.c_int
         L.muse_status_str.argtypes = [ctypes.c_int]
         L.muse_status_str.restype = ctypes.c_char_p
+        cp = ctypes.POINTER(KvCache)
+        L.muse_kv_relocate.argtypes = [lp, cp, i32, cp, i32, ctypes.POINTER(KvTile), i32, vp]
+        L.muse_kv_relocate.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -237,3 +246,35 @@ def decode(layer: Layer, q, k, v, gate, cache_k, cache_v, seq_len, out=None, *,
         max_seq_len = cache_k.shape[1] - 1
     return _call(True, layer, q, k, v, gate, cache_k, cache_v, seq_len, out, max_seq_len,
                  workspace, stream, timer)
+
+
+def kv_tiles(tiles):
+    """A muse_kv_tile array from (src_seq, src_pos, dst_seq, dst_pos, n_rows) tuples."""
+    arr = (KvTile * max(1, len(tiles)))()
+    for i, (ss, sp, ds, dp, n) in enumerate(tiles):
+        arr[i] = KvTile(ss, ds, sp, dp, n)
+    return arr, len(tiles)
+
+
+def kv_relocate(layer: Layer, src_k, src_v, dst_k, dst_v, tiles, stream=None) -> None:
+    """muse_kv_relocate on torch caches [n_seq, capacity, 2, 128]; tiles is a
+    sequence of (src_seq, src_pos, dst_seq, dst_pos, n_rows), or the result of
+    kv_tiles()."""
+    dt = _TORCH.get(layer.dtype)
+    if dt is None:
+        raise MuseError(6, "layer.dtype")
+    for name, t in (("src_k", src_k), ("src_v", src_v), ("dst_k", dst_k), ("dst_v", dst_v)):
+        _expect(t, name, None, dt)
+        if t.dim() != 4 or tuple(t.shape[2:]) != (N_KV_HEADS, HEAD_DIM):
+            raise ValueError(f"{name} must be [n_seq, capacity, 2, 128]")
+    if src_v.shape != src_k.shape or dst_v.shape != dst_k.shape:
+        raise ValueError("K and V caches must have the same shape")
+    arr, n_tiles = tiles if isinstance(tiles, tuple) and len(tiles) == 2 and isinstance(tiles[1], int) \
+        else kv_tiles(tiles)
+    src = KvCache(src_k.data_ptr(), src_v.data_ptr(), src_k.shape[1])
+    dst = KvCache(dst_k.data_ptr(), dst_v.data_ptr(), dst_k.shape[1])
+    if stream is None:
+        stream = torch.cuda.current_stream(src_k.device).cuda_stream
+    rc = lib().muse_kv_relocate(ctypes.byref(layer), ctypes.byref(src), src_k.shape[0], ctypes.byref(dst),
+                                dst_k.shape[0], arr, n_tiles, ctypes.c_void_p(stream))
+    _check(rc, "muse_kv_relocate")

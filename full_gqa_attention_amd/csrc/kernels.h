@@ -96,6 +96,22 @@ struct DecodeArgs {
     float theta[64];        // f32 RoPE frequency table
 };
 
+// Relocation of NoPE cache tiles: up to kRelocTiles tiles per launch, byte
+// offsets into the K caches (the V caches use the same offsets).
+constexpr int kRelocTiles = 120;
+constexpr int kRelocChunk = 16 * 1024;  // bytes of K (and of V) per workgroup
+struct RelocArgs {
+    const char* src_k;
+    const char* src_v;
+    char* dst_k;
+    char* dst_v;
+    int32_t n_tiles;
+    int32_t block0[kRelocTiles + 1];   // first workgroup of each tile; block0[n_tiles] = grid
+    int64_t src_off[kRelocTiles];
+    int64_t dst_off[kRelocTiles];
+    int64_t bytes[kRelocTiles];
+};
+
 // Launch geometry shared by the host code and the kernels.
 constexpr int kPrefillBM = 128;  // query rows per prefill workgroup (4 waves x 32)
 constexpr int kPrefillBN = 64;   // keys per prefill tile
@@ -117,5 +133,6 @@ int prefill_grid(int n_seq, int n_new);
 hipError_t launch_prep(const PrepArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_prefill(const AttnArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_relocate(const RelocArgs& a, hipStream_t stream);
 
 }  // namespace muse

@@ -374,6 +374,82 @@ muse_status muse_attn_workspace_size(const muse_attn_layer* layer, int32_t n_seq
     return MUSE_OK;
 }
 
+muse_status muse_kv_relocate(const muse_attn_layer* layer, const muse_kv_cache* src, int32_t n_seq_src,
+                             const muse_kv_cache* dst, int32_t n_seq_dst, const muse_kv_tile* tiles,
+                             int32_t n_tiles, hipStream_t stream) {
+    muse_status st = check_layer(layer);
+    if (st != MUSE_OK) return st;
+    // only position-free rows may move ("Chapter 14" 14.6)
+    if (layer->kind != MUSE_FULL_NOPE || layer->rope_theta != 0.0f) return MUSE_ERR_LAYER;
+    if (!src || !dst) return MUSE_ERR_NULL;
+    if (n_tiles < 0 || n_seq_src < 1 || n_seq_dst < 1) return MUSE_ERR_SHAPE;
+    if (n_tiles == 0) return MUSE_OK;
+    if (!tiles || !src->k || !src->v || !dst->k || !dst->v) return MUSE_ERR_NULL;
+    if (!aligned16(src->k) || !aligned16(src->v) || !aligned16(dst->k) || !aligned16(dst->v)) return MUSE_ERR_ALIGN;
+    if (src->capacity < 0 || dst->capacity < 0) return MUSE_ERR_CAPACITY;
+    const size_t row = (size_t)kKvHeads * kHeadDim * elem_bytes(layer->dtype);
+    for (int32_t i = 0; i < n_tiles; ++i) {
+        const muse_kv_tile& t = tiles[i];
+        if (t.src_seq < 0 || t.src_seq >= n_seq_src || t.dst_seq < 0 || t.dst_seq >= n_seq_dst ||
+            t.src_pos < 0 || t.dst_pos < 0 || t.n_rows < 0)
+            return MUSE_ERR_SHAPE;
+        if (t.src_pos > src->capacity - t.n_rows || t.dst_pos > dst->capacity - t.n_rows) return MUSE_ERR_CAPACITY;
+        // byte ranges of the tile's K rows in each cache (V rows sit at the same offsets)
+        const uintptr_t s0 = (uintptr_t)src->k + ((size_t)t.src_seq * (size_t)src->capacity + (size_t)t.src_pos) * row;
+        const uintptr_t d0 = (uintptr_t)dst->k + ((size_t)t.dst_seq * (size_t)dst->capacity + (size_t)t.dst_pos) * row;
+        const size_t n = (size_t)t.n_rows * row;
+        const uintptr_t sv0 = (uintptr_t)src->v + (s0 - (uintptr_t)src->k);
+        const uintptr_t dv0 = (uintptr_t)dst->v + (d0 - (uintptr_t)dst->k);
+        const Range sk{s0, s0 + n}, dk{d0, d0 + n}, sv{sv0, sv0 + n}, dv{dv0, dv0 + n};
+        if (n && (overlap(sk, dk) || overlap(sv, dv) || overlap(sk, dv) || overlap(sv, dk))) return MUSE_ERR_ALIAS;
+    }
+    // Tiles go to the device in launches of at most kRelocTiles; a launch ends
+    // early where a tile reads or writes rows an earlier tile of the launch
+    // writes (or writes rows it reads), so tiles apply in order.
+    muse::RelocArgs ra;
+    std::memset(&ra, 0, sizeof ra);
+    ra.src_k = (const char*)src->k;
+    ra.src_v = (const char*)src->v;
+    ra.dst_k = (char*)dst->k;
+    ra.dst_v = (char*)dst->v;
+    Range reads[muse::kRelocTiles][2], writes[muse::kRelocTiles][2];
+    auto flush = [&]() {
+        const hipError_t e = muse::launch_relocate(ra, stream);
+        ra.n_tiles = 0;
+        ra.block0[0] = 0;
+        return e;
+    };
+    for (int32_t i = 0; i < n_tiles; ++i) {
+        const muse_kv_tile& t = tiles[i];
+        if (t.n_rows == 0) continue;
+        const size_t so = ((size_t)t.src_seq * (size_t)src->capacity + (size_t)t.src_pos) * row;
+        const size_t dof = ((size_t)t.dst_seq * (size_t)dst->capacity + (size_t)t.dst_pos) * row;
+        const size_t n = (size_t)t.n_rows * row;
+        const Range rk{(uintptr_t)src->k + so, (uintptr_t)src->k + so + n}, rv{(uintptr_t)src->v + so, (uintptr_t)src->v + so + n};
+        const Range wk{(uintptr_t)dst->k + dof, (uintptr_t)dst->k + dof + n}, wv{(uintptr_t)dst->v + dof, (uintptr_t)dst->v + dof + n};
+        bool dep = ra.n_tiles == muse::kRelocTiles;
+        for (int j = 0; j < ra.n_tiles && !dep; ++j)
+            for (int x = 0; x < 2 && !dep; ++x) {
+                const Range r = x ? rv : rk, w = x ? wv : wk;
+                for (int y = 0; y < 2; ++y)
+                    dep = dep || overlap(r, writes[j][y]) || overlap(w, writes[j][y]) || overlap(w, reads[j][y]);
+            }
+        if (dep && flush() != hipSuccess) return MUSE_ERR_HIP;
+        const int k = ra.n_tiles;
+        reads[k][0] = rk;
+        reads[k][1] = rv;
+        writes[k][0] = wk;
+        writes[k][1] = wv;
+        ra.src_off[k] = (int64_t)so;
+        ra.dst_off[k] = (int64_t)dof;
+        ra.bytes[k] = (int64_t)n;
+        ra.block0[k + 1] = ra.block0[k] + (int32_t)((n + muse::kRelocChunk - 1) / muse::kRelocChunk);
+        ra.n_tiles = k + 1;
+    }
+    if (ra.n_tiles && flush() != hipSuccess) return MUSE_ERR_HIP;
+    return MUSE_OK;
+}
+
 muse_status muse_attn_layer_init(muse_attn_layer* layer, int32_t layer_index, int32_t dtype) {
     if (!layer) return MUSE_ERR_NULL;
     if (layer_index < 0 || layer_index >= kModelLayers) return MUSE_ERR_SHAPE;

@@ -183,6 +183,42 @@ muse_status muse_attn_decode(const muse_attn_layer* layer, int32_t n_seq,
                              void* workspace, size_t workspace_bytes,
                              hipStream_t stream, const muse_kernel_timer* timer);
 
+/* One tile of cache rows to relocate: rows [src_pos, src_pos + n_rows) of
+ * sequence src_seq go to rows [dst_pos, dst_pos + n_rows) of sequence
+ * dst_seq. */
+typedef struct {
+    int32_t src_seq;
+    int32_t dst_seq;
+    int64_t src_pos;
+    int64_t dst_pos;
+    int64_t n_rows;
+} muse_kv_tile;
+
+/*
+ * Relocate K and V rows of a full (NoPE) layer's cache: for each of the
+ * n_tiles tiles (host array, applied in order), a byte copy of the rows'
+ * 1,024 bytes (bf16; 2,048 for f32) of K and of V from `src` to `dst` (which
+ * may be the same cache).  A NoPE row carries no position, so the copied
+ * bytes are valid at the new position without recomputation ("Chapter 14 -
+ * QK-norm and RoPE" 14.6: NoPE tiles relocate by memcpy, 512-token tiles in
+ * the engine; any row count is accepted here).  Fails closed:
+ *   a sliding (RoPE) layer, whose rows are bound to their positions   MUSE_ERR_LAYER
+ *   n_seq_src / n_seq_dst < 1, a sequence index outside them, a negative
+ *   position or n_rows                                                MUSE_ERR_SHAPE
+ *   rows beyond a cache's capacity                                    MUSE_ERR_CAPACITY
+ *   source and destination rows of one tile overlap                   MUSE_ERR_ALIAS
+ *   a NULL pointer (tiles may be NULL when n_tiles is 0)              MUSE_ERR_NULL
+ *   a cache pointer not 16-byte aligned                               MUSE_ERR_ALIGN
+ * Every tile is checked before the first copy is enqueued.  The copies run
+ * asynchronously on `stream`, many tiles per kernel launch (a tile that reads
+ * or writes rows an earlier tile writes, or writes rows it reads, starts a
+ * new launch, so the result is that of applying the tiles in order);
+ * n_rows == 0 tiles are skipped.
+ */
+muse_status muse_kv_relocate(const muse_attn_layer* layer, const muse_kv_cache* src, int32_t n_seq_src,
+                             const muse_kv_cache* dst, int32_t n_seq_dst, const muse_kv_tile* tiles,
+                             int32_t n_tiles, hipStream_t stream);
+
 /* Workspace bytes a call needs (is_decode != 0 selects decode, which ignores
  * n_new).  Writes the size to *bytes (host).  Same validation as the calls. */
 muse_status muse_attn_workspace_size(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new,

@@ -222,6 +222,34 @@ def test_validation_ring(lib, decode):
     assert f.call(lib) == NULL       # passes the capacity check, stops at the NULL workspace
 
 
+def _relocate(lib, layer, tiles, n_src=2, n_dst=2, cap=1024, same=False, null_tiles=False):
+    src = fa.KvCache(BASE, BASE + 512 * MB, cap)
+    dst = src if same else fa.KvCache(BASE + 1024 * MB, BASE + 1536 * MB, cap)
+    arr = (fa.KvTile * max(1, len(tiles)))(*[fa.KvTile(ss, ds, sp, dp, n) for ss, sp, ds, dp, n in tiles])
+    return lib.muse_kv_relocate(ctypes.byref(layer), ctypes.byref(src), n_src, ctypes.byref(dst), n_dst,
+                                None if null_tiles else arr, len(tiles), None)
+
+
+def test_relocate_validation(lib):
+    """NoPE rows only ("Chapter 14 - QK-norm and RoPE" 14.6), every tile checked
+    before anything is copied.  The addresses are fake: none of these copies."""
+    full = fa.make_layer(fa.FULL_NOPE, window=0, rope_theta=0.0, dtype=fa.BF16)
+    sliding = fa.make_layer(fa.SLIDING_ROPE, window=2048, rope_theta=5e5, dtype=fa.BF16)
+    good = (0, 0, 1, 512, 512)
+    assert _relocate(lib, sliding, [good]) == LAYER
+    assert _relocate(lib, full, []) == OK                       # nothing to copy
+    assert _relocate(lib, full, [good], n_src=0) == SHAPE
+    assert _relocate(lib, full, [good, (2, 0, 0, 0, 1)]) == SHAPE   # sequence 2 of 2
+    assert _relocate(lib, full, [(0, -1, 0, 0, 1)]) == SHAPE
+    assert _relocate(lib, full, [(0, 0, 0, 0, -5)]) == SHAPE
+    assert _relocate(lib, full, [good, (0, 600, 1, 0, 512)]) == CAPACITY   # rows 600..1111 of 1024
+    assert _relocate(lib, full, [(0, 0, 0, 256, 512)], same=True) == ALIAS    # overlapping rows
+    assert _relocate(lib, full, [good], null_tiles=True) == NULL
+    bad_theta = fa.make_layer(fa.FULL_NOPE, window=0, rope_theta=0.0, dtype=fa.BF16)
+    bad_theta.rope_theta = 10000.0                              # a NoPE layer cannot carry a RoPE base
+    assert _relocate(lib, bad_theta, [good]) == LAYER
+
+
 def test_empty_batches_are_valid_noops(lib):
     f = Fake()
     f.n_seq = 0
