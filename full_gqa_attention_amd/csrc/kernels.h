@@ -96,6 +96,35 @@ struct DecodeArgs {
     float theta[64];        // f32 RoPE frequency table
 };
 
+// Short bf16 chunks (at most kVerifyTokens new tokens per sequence): split-K
+// attention with all 16 heads x 16 token rows of a KV head per workgroup,
+// then a merge of the splits with the gate.
+constexpr int kVerifyTokens = 16;
+constexpr int kVerifyTile = 32;     // keys per tile
+struct VerifyArgs {
+    const void* q;          // [S][N][32][128] raw Q
+    const void* gate;       // [S][N][4096]
+    void* out;              // [S][N][4096]
+    const void* cache_k;    // [S][capacity][2][128] (the new rows already appended)
+    const void* cache_v;
+    int64_t capacity;
+    const int32_t* seq_len; // device [S]
+    int32_t max_seq_len;
+    int32_t n_seq;
+    int32_t n_new;          // 1 .. kVerifyTokens
+    int32_t window;         // 0: full causal; else keys with p - j < window
+    int32_t rope;           // 1: sliding layer (rotate Q)
+    float eps;
+    float q_gain;
+    float q_scale;          // attn_scale * log2(e)
+    float theta[64];        // f32 RoPE frequency table
+    int32_t nsplit;         // key-range splits per (sequence, KV head)
+    int32_t chunk_tiles;    // kVerifyTile-key tiles per split
+    float* part_o;          // [S][2][nsplit][16 heads][16 tokens][128]
+    float* part_m;          // [S][2][nsplit][16][16] row maxima (log2 domain)
+    float* part_l;          // [S][2][nsplit][16][16] row sums
+};
+
 // Relocation of NoPE cache tiles: up to kRelocTiles tiles per launch, byte
 // offsets into the K caches (the V caches use the same offsets).
 constexpr int kRelocTiles = 120;
@@ -134,5 +163,7 @@ hipError_t launch_prep(const PrepArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_prefill(const AttnArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_relocate(const RelocArgs& a, hipStream_t stream);
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
+hipError_t launch_verify_merge(const VerifyArgs& a, hipStream_t stream);
 
 }  // namespace muse

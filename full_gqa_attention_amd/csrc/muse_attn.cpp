@@ -18,6 +18,7 @@ namespace {
 using muse::AttnArgs;
 using muse::DecodeArgs;
 using muse::PrepArgs;
+using muse::VerifyArgs;
 
 constexpr int kHeads = 32, kKvHeads = 2, kHeadDim = 128;
 constexpr int kModelLayers = 52;          // "Chapter 9" 9.4: 52 blocks
@@ -62,6 +63,31 @@ int64_t copied_prefix(const muse_attn_layer* l, int32_t max_seq_len) {
     const int64_t win = (int64_t)l->window - 1 + (muse::kWindowAlign - 1);
     if (l->kind == MUSE_SLIDING_ROPE && win < prefix) prefix = win;
     return prefix;
+}
+
+// Short bf16 chunks (at most kVerifyTokens new tokens, linear cache) take the
+// verify kernels: split-K over the keys with every head of a KV head per
+// workgroup.
+bool use_verify(const muse_attn_layer* l, int32_t n_new) {
+    return l->dtype == MUSE_BF16 && !l->kv_ring && n_new >= 1 && n_new <= muse::kVerifyTokens;
+}
+
+// Verify splits: about 256 workgroups in total, at least 16 tiles (512 keys)
+// per split when the keys allow, at most 64 splits.
+void verify_split(const muse_attn_layer* l, int32_t n_seq, int32_t n_new, int32_t max_seq_len,
+                  int32_t* nsplit, int32_t* chunk_tiles) {
+    int64_t prefix = max_seq_len;
+    if (l->kind == MUSE_SLIDING_ROPE && (int64_t)l->window - 1 < prefix) prefix = (int64_t)l->window - 1;
+    const int64_t bn = muse::kVerifyTile;
+    const int64_t tiles = (prefix + n_new + 2 * bn - 1) / bn;   // covers any alignment of the key range
+    const int64_t seqs = n_seq > 0 ? n_seq : 1;
+    int64_t want = (256 + 2 * seqs - 1) / (2 * seqs);
+    if (want > tiles / 16) want = tiles / 16;
+    if (want > 64) want = 64;
+    if (want < 1) want = 1;
+    const int64_t ch = (tiles + want - 1) / want;
+    *chunk_tiles = (int32_t)ch;
+    *nsplit = (int32_t)((tiles + ch - 1) / ch);
 }
 
 // Rows the cache must hold: every position of the call, or on a ring layer
@@ -128,6 +154,7 @@ struct WorkspaceLayout {
     size_t qhat = 0, kq = 0, vq = 0, arrivals = 0, ready = 0, part_o = 0, part_m = 0, part_l = 0, total = 0;
     int64_t kq_capacity = 0;
     int32_t chunk = 0, nsplit = 0;
+    bool verify = false;
 };
 
 WorkspaceLayout layout_for(const muse_attn_layer* l, int32_t n_seq, int32_t n_new,
@@ -135,7 +162,18 @@ WorkspaceLayout layout_for(const muse_attn_layer* l, int32_t n_seq, int32_t n_ne
     WorkspaceLayout w;
     const size_t es = elem_bytes(l->dtype);
     size_t off = 0;
-    if (!decode) {
+    if (!decode && use_verify(l, n_new)) {
+        // short chunk: the verify partials [S][2][nsplit][16][16] x (128 + 2) floats
+        w.verify = true;
+        verify_split(l, n_seq, n_new, max_seq_len, &w.nsplit, &w.chunk);
+        const size_t rows = (size_t)n_seq * kKvHeads * w.nsplit * (kHeads / kKvHeads) * muse::kVerifyTokens;
+        w.part_o = 0;
+        off = round_up(rows * kHeadDim * sizeof(float), kAlign);
+        w.part_m = off;
+        off += round_up(rows * sizeof(float), kAlign);
+        w.part_l = off;
+        off += round_up(rows * sizeof(float), kAlign);
+    } else if (!decode) {
         // bf16 layers make Q-hat inside the attention kernel; f32 layers stage it
         w.qhat = 0;
         if (l->dtype != MUSE_BF16) off = round_up((size_t)n_seq * n_new * kHeads * kHeadDim * es, kAlign);
@@ -291,7 +329,7 @@ muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, cons
     pa.q_scale = scale_log2;
     pa.skip_q = layer->dtype == MUSE_BF16 ? 1 : 0;
     pa.window = rope ? layer->window : 0;
-    if (layer->dtype == MUSE_BF16) {
+    if (layer->dtype == MUSE_BF16 && !wl.verify) {
         // prefix rows the key copy holds (see copied_prefix), 64 per workgroup
         pa.kq = ws + wl.kq;
         pa.kq_capacity = wl.kq_capacity;
@@ -301,6 +339,40 @@ muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, cons
         pa.vq = layer->kv_ring ? (void*)(ws + wl.vq) : nullptr;
     }
     if (rope) rope_table(layer->rope_theta, pa.theta);
+
+    if (wl.verify) {
+        // a short chunk: append its K-hat and V rows, then the verify kernels
+        // read the keys straight from the cache (no prefix copy)
+        if (muse::launch_prep(pa, dt, stream) != hipSuccess) return MUSE_ERR_HIP;
+        VerifyArgs va;
+        std::memset(&va, 0, sizeof va);
+        va.q = q;
+        va.gate = gate;
+        va.out = out;
+        va.cache_k = cache->k;
+        va.cache_v = cache->v;
+        va.capacity = cache->capacity;
+        va.seq_len = seq_len;
+        va.max_seq_len = max_seq_len;
+        va.n_seq = n_seq;
+        va.n_new = n_new;
+        va.window = rope ? layer->window : 0;
+        va.rope = pa.rope;
+        va.eps = pa.eps;
+        va.q_gain = pa.q_gain;
+        va.q_scale = pa.q_scale;
+        std::memcpy(va.theta, pa.theta, sizeof va.theta);
+        va.nsplit = wl.nsplit;
+        va.chunk_tiles = wl.chunk;
+        va.part_o = (float*)(ws + wl.part_o);
+        va.part_m = (float*)(ws + wl.part_m);
+        va.part_l = (float*)(ws + wl.part_l);
+        if (timer && hipEventRecord(timer->start, stream) != hipSuccess) return MUSE_ERR_HIP;
+        if (muse::launch_verify(va, stream) != hipSuccess) return MUSE_ERR_HIP;
+        if (muse::launch_verify_merge(va, stream) != hipSuccess) return MUSE_ERR_HIP;
+        if (timer && hipEventRecord(timer->stop, stream) != hipSuccess) return MUSE_ERR_HIP;
+        return MUSE_OK;
+    }
 
     AttnArgs aa;
     std::memset(&aa, 0, sizeof aa);

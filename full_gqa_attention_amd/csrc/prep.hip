@@ -174,8 +174,8 @@ __device__ __forceinline__ void prep_kv_bf16(const PrepArgs& a, int blk) {
             for (int j = 0; j < 8; ++j) kv[j] = from_f32<bf16_t>(y[j]);
             const u32x4 kr = __builtin_bit_cast(u32x4, kv);
             if (to_cache) *(u32x4*)((bf16_t*)a.cache_k + row * kHeadDim + 8 * sub) = kr;
-            // the score copy holds the stored values
-            *(u32x4*)((f16_t*)a.kq + qrow * kHeadDim + 8 * sub) = k_chunk_to_score(kr, bf16_t{});
+            // the score copy holds the stored values (short chunks read the cache instead)
+            if (a.kq) *(u32x4*)((f16_t*)a.kq + qrow * kHeadDim + 8 * sub) = k_chunk_to_score(kr, bf16_t{});
         }
     }
 }

@@ -157,6 +157,11 @@ typedef struct {
  *   stream       HIP stream to enqueue on
  *   timer        optional (NULL = none)
  * n_seq == 0 or n_new == 0 is valid and enqueues nothing.
+ * Short chunks (n_new <= 16 on a bf16 layer without kv_ring: the verify step
+ * of speculative decoding, which scores a handful of drafted tokens against
+ * a long prefix) run as split-K over the keys, every head of a KV head in one
+ * workgroup, with the splits merged by a second kernel; the timer then spans
+ * both kernels.  The result is the same attention within the tolerances.
  */
 muse_status muse_attn_prefill(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new,
                               const int32_t* seq_len, int32_t max_seq_len,
