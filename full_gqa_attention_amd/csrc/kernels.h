@@ -99,6 +99,12 @@ struct DecodeArgs {
 // Short bf16 chunks (at most kVerifyTokens new tokens per sequence): split-K
 // attention with all 16 heads x 16 token rows of a KV head per workgroup,
 // then a merge of the splits with the gate.
+#ifndef MUSE_VERIFY_DEPTH
+#define MUSE_VERIFY_DEPTH 4     // key tiles in flight per verify workgroup (register slots)
+#endif
+#ifndef MUSE_VERIFY_BLOCKS
+#define MUSE_VERIFY_BLOCKS 256  // verify workgroups a call aims for (splits = this / (2 n_seq))
+#endif
 constexpr int kVerifyTokens = 16;
 constexpr int kVerifyTile = 32;     // keys per tile
 struct VerifyArgs {

@@ -72,7 +72,7 @@ bool use_verify(const muse_attn_layer* l, int32_t n_new) {
     return l->dtype == MUSE_BF16 && !l->kv_ring && n_new >= 1 && n_new <= muse::kVerifyTokens;
 }
 
-// Verify splits: about 256 workgroups in total, at least 16 tiles (512 keys)
+// Verify splits: about MUSE_VERIFY_BLOCKS workgroups in total, at least 16 tiles (512 keys)
 // per split when the keys allow, at most 64 splits.
 void verify_split(const muse_attn_layer* l, int32_t n_seq, int32_t n_new, int32_t max_seq_len,
                   int32_t* nsplit, int32_t* chunk_tiles) {
@@ -81,7 +81,7 @@ void verify_split(const muse_attn_layer* l, int32_t n_seq, int32_t n_new, int32_
     const int64_t bn = muse::kVerifyTile;
     const int64_t tiles = (prefix + n_new + 2 * bn - 1) / bn;   // covers any alignment of the key range
     const int64_t seqs = n_seq > 0 ? n_seq : 1;
-    int64_t want = (256 + 2 * seqs - 1) / (2 * seqs);
+    int64_t want = (MUSE_VERIFY_BLOCKS + 2 * seqs - 1) / (2 * seqs);
     if (want > tiles / 16) want = tiles / 16;
     if (want > 64) want = 64;
     if (want < 1) want = 1;

@@ -90,3 +90,30 @@ def test_verify_split_count_invariance():
     w1, inp1 = _inputs(spec, [3000], 16)          # 6 splits
     one = run_gpu(spec, w1.dtype, inp1, False).float()
     assert torch.allclose(many[0], one[0], atol=2e-2, rtol=1e-2)
+
+
+def test_verify_reference_far_below_row_max():
+    """Scores that climb by far more than 2^128 after a split's first keys.
+
+    Full (NoPE) layer with Q gain 16 and every query along one direction u;
+    cached keys 0..31 point along -u (score -B) and key 100 along +u (score
+    +B), with B = |q-hat| |k-hat| * scale * log2(e) ~ 261 in log2 units.  One
+    split covers the 216 keys, so a reference taken from its first tile sits
+    2B below the row maximum and exp2(s - ref) overflows f32: the kernel must
+    notice and recompute the split with exact row maxima.  Every row then
+    reduces to V[100] * sigmoid(gate) up to the weight of the random keys.
+    """
+    spec = synth.full(q_gain=16.0)
+    B = spec.q_gain * spec.k_gain * 128 * spec.scale * np.log2(np.e)
+    assert 2 * B > 300
+    w, inp = _inputs(spec, [200], 16, config=95)
+    gen = torch.Generator(device="cpu").manual_seed(2025)
+    u = torch.randn(128, generator=gen, dtype=torch.float64)
+    u = u / u.pow(2).mean().sqrt()                     # unit RMS, as a normed key row
+    q = u.view(1, 1, 1, 128) + 0.05 * torch.randn(1, 16, 32, 128, generator=gen, dtype=torch.float64)
+    inp.q.copy_(q.to(inp.q.dtype))
+    ck = inp.cache_k.double().cpu()
+    ck[0, :32] = -u
+    ck[0, 100] = u
+    inp.cache_k.copy_(ck.to(inp.cache_k.dtype))
+    check_layer(w, spec, inp, decode=False)
