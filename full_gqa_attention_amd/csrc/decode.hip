@@ -39,6 +39,7 @@
 // counts as zero, so the workspace needs no clearing; the merging split
 // resets the count.  Splits that would cover no row of a shorter sequence
 // exit at once.
+#include <cstddef>
 #include <type_traits>
 
 #include "device_common.h"
@@ -50,6 +51,7 @@
 #ifndef MUSE_DECODE_DEPTH
 #define MUSE_DECODE_DEPTH 3        // 16-row sub-tiles in flight per wave
 #endif
+
 
 namespace muse {
 
@@ -115,31 +117,10 @@ void decode_kernel(DecodeArgs a) {
     const int s = sg >> 1, g = sg & 1;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
-    const int L = a.seq_len[s];
-    const int W = a.window;
     const int64_t obase = ((int64_t)s * kHeads + g * HG) * D;     // out/gate/q of head 16g
-
-    if (L < 0 || L > a.max_seq_len) {                  // refused on the device
-        if (c == 0)
-            for (int i = tid; i < HG * D; i += NT) ((T*)a.out)[obase + i] = from_f32<T>(__builtin_nanf(""));
-        return;
-    }
-    const int64_t p = L;
-    const int64_t lo = (W > 0) ? max((int64_t)0, p - W + 1) : 0;
-    const int64_t cs = lo + (int64_t)c * a.chunk;
-    if (cs > p) return;                                // split beyond this sequence's rows
-    const int64_t ce = min(cs + (int64_t)a.chunk, p + 1);   // exclusive
-    const int n_live = (int)((p - lo) / a.chunk) + 1;       // splits with rows
-    const bool owns_p = (ce == p + 1);
-    const int n_sub = (int)((ce - cs + SUB - 1) / SUB);
-    const int my_cnt = n_sub > wave ? (n_sub - wave + NW - 1) / NW : 0;  // sub-tiles wave, wave+NW, ...
-
-    char* wave_lds = lds + wave * (WAVE_V + WAVE_K);
-    T* Vw = (T*)wave_lds;
-    T* Kw = (T*)(wave_lds + WAVE_V);
-
-    // ---- first the small loads, so that they do not queue behind the cache
-    // stream: the raw Q of the 16 heads in the B-operand layout of
+    // ---- first the small loads, which do not depend on the sequence's
+    // length (they go out before seq_len is read) and do not queue behind
+    // the cache stream: the raw Q of the 16 heads in the B-operand layout of
     // S^T = K Q^T (lane: head l16, k-group q4), the new K and V rows in the
     // chunk layout of a cache sub-tile (every wave loads them; rows equal to
     // p take them), and the gate values this thread applies at the end.
@@ -171,6 +152,46 @@ void decode_kernel(DecodeArgs a) {
     } else {
         graw[0] = *(const u32x4*)((const char*)a.gate + (obase + hh * D + d0) * ES);
     }
+    // this lane's RoPE frequency (pair = lane): one vector load from the
+    // kernel's argument block, issued with the loads above (picking it out of
+    // the scalar arguments took several dependent scalar round trips)
+    const float th = *((const __attribute__((address_space(4))) float*)
+                           ((const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr() +
+                            offsetof(DecodeArgs, theta)) + lane);
+    // The exits below use those loads too (an empty asm that takes them):
+    // otherwise the compiler moves the loads past the exits, behind the wait
+    // for seq_len, and the two round trips no longer overlap.
+    auto hold_loads = [&]() __attribute__((always_inline)) {
+        if constexpr (kBf16) asm volatile("" :: "v"(qv[0]), "v"(qv[1]), "v"(qv[2]), "v"(qv[3]));
+        else asm volatile("" :: "v"(qf32[0]));
+        asm volatile("" :: "v"(kn_raw), "v"(vnew_c), "v"(graw[0]), "v"(th));
+    };
+    const int L = a.seq_len[s];
+    const int W = a.window;
+
+    if (L < 0 || L > a.max_seq_len) {                  // refused on the device
+        hold_loads();
+        if (c == 0)
+            for (int i = tid; i < HG * D; i += NT) ((T*)a.out)[obase + i] = from_f32<T>(__builtin_nanf(""));
+        return;
+    }
+    const int64_t p = L;
+    const int64_t lo = (W > 0) ? max((int64_t)0, p - W + 1) : 0;
+    const int64_t cs = lo + (int64_t)c * a.chunk;
+    if (cs > p) {                                      // split beyond this sequence's rows
+        hold_loads();
+        return;
+    }
+    const int64_t ce = min(cs + (int64_t)a.chunk, p + 1);   // exclusive
+    const int n_live = (int)((p - lo) / a.chunk) + 1;       // splits with rows
+    const bool owns_p = (ce == p + 1);
+    const int n_sub = (int)((ce - cs + SUB - 1) / SUB);
+    const int my_cnt = n_sub > wave ? (n_sub - wave + NW - 1) / NW : 0;  // sub-tiles wave, wave+NW, ...
+
+    char* wave_lds = lds + wave * (WAVE_V + WAVE_K);
+    T* Vw = (T*)wave_lds;
+    T* Kw = (T*)(wave_lds + WAVE_V);
+
     auto gate_sig = [&](int x) __attribute__((always_inline)) {     // sigmoid of gate value d0 + x
         float gv;
         if constexpr (kBf16) {
@@ -224,19 +245,32 @@ void decode_kernel(DecodeArgs a) {
     // pipeline stages as named variables (an indexed array of them ends up in scratch)
     static_assert(DEPTH >= 1 && DEPTH <= 8, "pipeline depth 1..8");
     SubTile<T> b0, b1, b2, b3, b4, b5, b6, b7;
-    // (sub-tiles past the wave's share load clamped rows and are never
-    // processed).  The first sub-tile's loads go out now; the others after
-    // Q-hat, so that computing it does not wait behind a full queue of loads.
+    // The first DEPTH sub-tiles' loads go out as soon as the rows are known,
+    // so that they are under way while Q-hat is made (sub-tiles past the
+    // wave's share load clamped rows and are never processed).
     issue(b0, 0);
+    if constexpr (DEPTH > 1) issue(b1, 1);
+    if constexpr (DEPTH > 2) issue(b2, 2);
+    if constexpr (DEPTH > 3) issue(b3, 3);
+    if constexpr (DEPTH > 4) issue(b4, 4);
+    if constexpr (DEPTH > 5) issue(b5, 5);
+    if constexpr (DEPTH > 6) issue(b6, 6);
+    if constexpr (DEPTH > 7) issue(b7, 7);
 
     // ---- Q-hat and the new K row, wave by wave (no workgroup barrier): RMS
     // norm with gain, then RoPE on sliding layers ("Chapter 14 - QK-norm and
-    // RoPE" 14.3-14.5).  Lane i computes (cos, sin) of pair i; lanes fetch
-    // the pairs they hold with cross-lane reads.
-    float sn = 0.0f, cs_ = 1.0f;
-    if (a.rope) rope_sincos(a.theta, lane, p, sn, cs_);
+    // RoPE" 14.3-14.5).  Lane i computes (cos, sin) of pair i into a table in
+    // the wave's own LDS (its V buffer, unused until the loop); lanes read the
+    // pairs they hold from there, several per LDS read.
+    float2* rot = (float2*)Vw;
+    if (a.rope) {
+        float sn, cs_;
+        sincosf((float)p * th, &sn, &cs_);
+        rot[lane] = make_float2(cs_, sn);
+    }
     auto rotate = [&](float& y0, float& y1, int pair) __attribute__((always_inline)) {
-        const float c2 = __shfl(cs_, pair, 64), s2 = __shfl(sn, pair, 64);
+        const float2 cz = rot[pair];
+        const float c2 = cz.x, s2 = cz.y;
         const float z0 = y0 * c2 - y1 * s2;
         const float z1 = y0 * s2 + y1 * c2;
         y0 = z0;
@@ -257,8 +291,7 @@ void decode_kernel(DecodeArgs a) {
         float ss = 0.0f;
 #pragma unroll
         for (int i = 0; i < 32; ++i) ss += x[i] * x[i];
-        ss += __shfl_xor(ss, 16, 64);                  // the head's other k-groups
-        ss += __shfl_xor(ss, 32, 64);
+        ss = sum_halves(sum_rows16(ss));               // the head's other k-groups (lanes ^ 16, ^ 32)
         const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
 #pragma unroll
         for (int i = 0; i < 32; ++i) x[i] = (x[i] * r) * a.q_gain;
@@ -330,14 +363,6 @@ void decode_kernel(DecodeArgs a) {
         *(u32x4*)((char*)a.cache_k + row_off) = knew_c;
         *(u32x4*)((char*)a.cache_v + row_off) = vnew_c;
     }
-    if constexpr (DEPTH > 1) issue(b1, 1);
-    if constexpr (DEPTH > 2) issue(b2, 2);
-    if constexpr (DEPTH > 3) issue(b3, 3);
-    if constexpr (DEPTH > 4) issue(b4, 4);
-    if constexpr (DEPTH > 5) issue(b5, 5);
-    if constexpr (DEPTH > 6) issue(b6, 6);
-    if constexpr (DEPTH > 7) issue(b7, 7);
-
     floatx4 o[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{};
@@ -360,12 +385,16 @@ void decode_kernel(DecodeArgs a) {
                 *(u32x4*)(Kw + r * LDKW + l16 * 8) = kraw;
                 *(u32x4*)(Vw + r * LDV + l16 * 8) = vraw;
             }
+            // hi and lo parts in two accumulation chains (half the dependent
+            // MFMA latency), added at the end
+            floatx4 sl = floatx4{};
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 const bf16x8 kf = *(const bf16x8*)(Kw + l16 * LDKW + 8 * q4 + 32 * st);
                 sc = MW::mma(kf, qhi[st], sc);
-                sc = MW::mma(kf, qlo[st], sc);
+                sl = MW::mma(kf, qlo[st], sl);
             }
+            sc += sl;
         } else {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -389,8 +418,7 @@ void decode_kernel(DecodeArgs a) {
             sc[i] = x;
             mx = fmaxf(mx, x);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = max_halves(max_rows16(mx));                 // lanes ^ 16 and ^ 32 hold the head's other keys
         const float m_new = fmaxf(m_run, mx);            // finite: key j0 is visible
         const float alpha = fast_exp2(m_run - m_new);
         float rs = 0.0f;
@@ -449,8 +477,7 @@ void decode_kernel(DecodeArgs a) {
     }
 
     // ---- merge the waves: LDS holds per wave [16 heads][128 + 2] floats
-    l_run += __shfl_xor(l_run, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
+    l_run = sum_halves(sum_rows16(l_run));
     __syncthreads();
     float* mg = (float*)lds;
     float* mw = mg + (wave * HG + l16) * (D + 2);

@@ -60,6 +60,21 @@ __device__ __forceinline__ HalfPair halves(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return HalfPair{__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
+// v_permlane16_swap of x with itself: the two results are x of this lane
+// and of lane l ^ 16 (in an order that depends on the lane), so again a
+// symmetric combination is the same in both lanes.
+__device__ __forceinline__ HalfPair rows16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return HalfPair{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float max_rows16(float x) {
+    const HalfPair p = rows16(x);
+    return fmaxf(p.a, p.b);
+}
+__device__ __forceinline__ float sum_rows16(float x) {
+    const HalfPair p = rows16(x);
+    return p.a + p.b;
+}
 __device__ __forceinline__ float max_halves(float x) {
     const HalfPair p = halves(x);
     return fmaxf(p.a, p.b);
