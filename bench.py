@@ -51,6 +51,11 @@ PROFILES = os.path.join(ROOT, "profiles")
 COUNTERS_FILE = os.path.join(PROFILES, "decode_64x8192_bf16_hbm_counters.md")
 DECODE_SOURCES = ["full_gqa_attention_amd/csrc/decode.hip", "full_gqa_attention_amd/csrc/device_common.h",
                   "full_gqa_attention_amd/csrc/kernels.h", "full_gqa_attention_amd/csrc/muse_attn.cpp"]
+MFMA_FILE = os.path.join(PROFILES, "prefill_8x8192_bf16_mfma_counters.md")
+PREFILL_SOURCES = ["full_gqa_attention_amd/csrc/prefill.hip", "full_gqa_attention_amd/csrc/device_common.h",
+                   "full_gqa_attention_amd/csrc/kernels.h", "full_gqa_attention_amd/csrc/muse_attn.cpp"]
+SIMDS = 256 * 4                  # 256 CUs x 4 SIMDs
+XCDS = 8
 # A plain 1 GiB device copy read back 524,315 KiB on FETCH_SIZE and 1,048,576 KiB
 # on WRITE_SIZE: the factors that turn the counters into bytes.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
@@ -80,6 +85,89 @@ def counter_traffic():
         return float(kv["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def read_summary_values(path: str) -> dict:
+    """The indented `key: value` lines of a committed counter summary."""
+    kv = {}
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.startswith("    ") and ":" in line:
+                    k, v = line.strip().split(":", 1)
+                    kv[k.strip()] = v.strip()
+    except OSError:
+        pass
+    return kv
+
+
+def prefill_counters():
+    """MFMA utilisation of the prefill kernel per layer from the committed
+    counter summary, or None when the prefill sources changed since."""
+    kv = read_summary_values(MFMA_FILE)
+    if kv.get("prefill_sources_sha256_16") != sources_hash(PREFILL_SOURCES):
+        return None
+    try:
+        return {"mfma_busy": {"sliding": float(kv["mfma_busy_sliding"]), "full": float(kv["mfma_busy_full"])},
+                "clock_GHz": {"sliding": float(kv["clock_ghz_sliding"]), "full": float(kv["clock_ghz_full"])},
+                "source": os.path.relpath(MFMA_FILE, ROOT)}
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize_mfma(pmc1_csv: str, pmc2_csv: str, out: str, command: str):
+    """Write the prefill kernel's MFMA-utilisation summary from two --pmc runs
+    of `bench.py --prefill-only` (launches alternate sliding, full)."""
+    import csv
+    per = {}
+    for path in (pmc1_csv, pmc2_csv):
+        for r in csv.DictReader(open(path)):
+            if "prefill_group_kernel" not in r["Kernel_Name"]:
+                continue
+            key = (path, int(r["Dispatch_Id"]))
+            d = per.setdefault(key, {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+    layers = {"sliding": [], "full": []}
+    for path in (pmc1_csv, pmc2_csv):
+        ds = [per[k] for k in sorted(k for k in per if k[0] == path)]
+        layers["sliding"] += ds[0::2]
+        layers["full"] += ds[1::2]
+
+    def avg(ds, c):
+        vals = [d[c] for d in ds if c in d]
+        return sum(vals) / len(vals) if vals else float("nan")
+
+    flops = {"sliding": 1.9243e12, "full": 4.3986e12}     # algorithmic, 8 x 8,192 tokens
+    rows, vals = [], {}
+    for name, ds in layers.items():
+        ns = avg(ds, "ns")
+        cyc = avg(ds, "GRBM_GUI_ACTIVE") / XCDS                  # per-XCD busy cycles
+        clock = cyc / ns
+        busy = avg(ds, "SQ_VALU_MFMA_BUSY_CYCLES") / (SIMDS * cyc)
+        coexec = avg(ds, "SQ_VALU_MFMA_COEXEC_CYCLES") / (SIMDS * cyc)
+        mfma = avg(ds, "SQ_INSTS_MFMA")
+        executed = mfma * 32 * 32 * 16 * 2                        # v_mfma_f32_32x32x16 flops
+        rows.append(f"| {name} | {ns / 1e6:.3f} | {clock:.2f} | {busy * 100:.1f} | {coexec * 100:.1f} | "
+                    f"{flops[name] / (ns * 1e-9) / 1e12:.0f} | {executed / flops[name]:.3f} | "
+                    f"{avg(ds, 'SQ_INSTS_VALU') / mfma:.2f} | {avg(ds, 'SQ_INSTS_LDS') / mfma:.2f} |")
+        vals[name] = (busy, clock)
+    lines = ["# MFMA utilisation of the prefill kernel: 8 x 8,192 bf16 prefill (sliding W 2048, full NoPE)", "",
+             "Two counter runs (from /tmp, repository at $ROOT):", "", "```", command, "```", "",
+             "GRBM_GUI_ACTIVE is summed over the 8 XCDs, so the clock is GRBM_GUI_ACTIVE / 8 over the "
+             "dispatch time; SQ_VALU_MFMA_BUSY_CYCLES and SQ_VALU_MFMA_COEXEC_CYCLES are summed over the "
+             "1,024 SIMDs and divided by 1,024 times the per-XCD cycles.  Executed flops count every "
+             "`v_mfma_f32_32x32x16` (32,768 flop), masked tiles included.", "",
+             "| layer | ms per launch | clock GHz | MFMA busy % | VALU+MFMA co-issue % | algorithmic TFLOP/s "
+             "| executed / algorithmic flop | VALU instr per MFMA | LDS instr per MFMA |",
+             "|---|---|---|---|---|---|---|---|---|", *rows, "",
+             "Values read by bench.py (reported only while these sources are unchanged):", "",
+             f"    prefill_sources_sha256_16: {sources_hash(PREFILL_SOURCES)}",
+             f"    mfma_busy_sliding: {vals['sliding'][0]:.4f}",
+             f"    mfma_busy_full: {vals['full'][0]:.4f}",
+             f"    clock_ghz_sliding: {vals['sliding'][1]:.3f}",
+             f"    clock_ghz_full: {vals['full'][1]:.3f}", ""]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def summarize_trace(stats_csv: str, out: str, command: str):
@@ -165,6 +253,10 @@ def parse():
                     help="write a kernel-trace summary from rocprofv3 kernel_stats.csv and exit")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT", "COMMAND"),
                     help="write the decode kernel's HBM-traffic summary from two --pmc runs and exit")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prefill workload and print its JSON object (for counter runs)")
+    ap.add_argument("--summarize-mfma", nargs=4, metavar=("PMC1_CSV", "PMC2_CSV", "OUT", "COMMAND"),
+                    help="write the prefill kernel's MFMA-utilisation summary from two --pmc runs and exit")
     return ap.parse_args()
 
 
@@ -336,7 +428,8 @@ def bench_prefill(w, steps, warmup, fa, synth, torch):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel": "muse::prefill_group_kernel<1, 8, 1, false> (bf16)", "avg_launch_ms": round(kern, 4),
-                     "per_layer": per_layer},
+                     "per_layer": per_layer,
+                     "counters": prefill_counters() if w.name == "prefill_8x8192_bf16" else None},
         "flop_per_step": flops_step, "steps": steps, "warmup": warmup,
     }
 
@@ -498,6 +591,9 @@ def main():
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
         return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
               "multi-GPU path to measure.", file=sys.stderr)
@@ -515,6 +611,10 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+    if args.prefill_only:
+        pw = synth.WORKLOADS[args.prefill_workload]
+        print(json.dumps({"prefill": bench_prefill(pw, args.prefill_steps, 2, fa, synth, torch)}), flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
     if not w.is_decode:
         print(f"--workload must be a decode workload, got {w.name}", file=sys.stderr)

@@ -39,7 +39,6 @@
 // counts as zero, so the workspace needs no clearing; the merging split
 // resets the count.  Splits that would cover no row of a shorter sequence
 // exit at once.
-#include <cstddef>
 #include <type_traits>
 
 #include "device_common.h"
@@ -152,12 +151,8 @@ void decode_kernel(DecodeArgs a) {
     } else {
         graw[0] = *(const u32x4*)((const char*)a.gate + (obase + hh * D + d0) * ES);
     }
-    // this lane's RoPE frequency (pair = lane): one vector load from the
-    // kernel's argument block, issued with the loads above (picking it out of
-    // the scalar arguments took several dependent scalar round trips)
-    const float th = *((const __attribute__((address_space(4))) float*)
-                           ((const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr() +
-                            offsetof(DecodeArgs, theta)) + lane);
+    // this lane's RoPE frequency (pair = lane), loaded with the loads above
+    const float th = theta_of_lane<DecodeArgs>(lane);
     // The exits below use those loads too (an empty asm that takes them):
     // otherwise the compiler moves the loads past the exits, behind the wait
     // for seq_len, and the two round trips no longer overlap.

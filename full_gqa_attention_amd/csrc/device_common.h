@@ -1,6 +1,7 @@
 // device_common.h -- small device-side helpers shared by the gfx950 kernels:
 // storage types, conversions, wave reductions and MFMA wrappers.
 #pragma once
+#include <cstddef>
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -106,6 +107,17 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // sin/cos of the f32 angle f32(p) * theta[lane] (accurate sincosf).  The
 // table sits in kernel arguments; the unrolled select keeps every access at
 // a constant index.
+// theta[lane] of a kernel whose only argument is the struct Args (so the
+// struct sits at the start of the kernel's argument block): one vector load
+// at the table's offset.  Selecting it out of the scalar copies of the
+// arguments takes 64 selects and several dependent scalar-load round trips.
+template <typename Args>
+__device__ __forceinline__ float theta_of_lane(int lane) {
+    typedef const __attribute__((address_space(4))) char* KArg;
+    return *((const __attribute__((address_space(4))) float*)(
+                 (KArg)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(Args, theta)) + lane);
+}
+
 __device__ __forceinline__ void rope_sincos(const float (&theta)[64], int lane, int64_t p,
                                             float& sn, float& cs) {
     float th = 0.0f;

@@ -368,6 +368,9 @@ void prefill_kernel(AttnArgs a) {
 // the Q.K MFMAs start from -ref instead of 0, so no subtraction is left
 // either.  Row sums are taken from the bf16 P values that enter the P.V
 // product (v_dot2 against (1, 1)).
+#ifndef MUSE_PREFILL_PRIO
+#define MUSE_PREFILL_PRIO 0
+#endif
 template <int QG> struct GroupTraits {
     static constexpr int WAVES = QG == 1 ? 2 : 1;      // waves per SIMD the registers allow
 };
@@ -432,6 +435,26 @@ void prefill_group_kernel(AttnArgs a) {
         return;
     }
 
+    // ---- keys the workgroup can see (positions fit in int32: bounded by 2^24)
+    const int W = a.window;
+    const int P0 = L + q0, P1 = L + min(q0 + BMW - 1, N - 1);
+    const int kv_lo = (W > 0) ? max(0, P0 - W + 1) : 0;
+    const int kv_end = L + N;
+    const int tile_lo = kv_lo / BN, tile_hi = P1 / BN;
+    const int ntiles = tile_hi - tile_lo + 1;
+    const int pq0 = L + q0 + l32;                      // position of this lane's row in group 0
+
+    constexpr int64_t ROW = (int64_t)kKvHeads * D * ES;
+    constexpr int RSTEP = NT / CPR;
+    const int r_t = tid / CPR, c_t = tid % CPR;
+    // rows of the K copy (and of V on ring layers) start on sliding layers at
+    // the window's first visible position rounded down to kWindowAlign; every
+    // tile read here starts at or past that (tiles start at multiples of BN,
+    // which divides kWindowAlign)
+    static_assert(kWindowAlign % BN == 0, "key tiles start inside the windowed copy");
+    const int64_t win0 = W > 0 ? max(0, L - W + 1) / kWindowAlign * kWindowAlign : 0;
+    const char* kbase = (const char*)a.kq + ((((int64_t)s * a.kq_capacity) - (a.kq_windowed ? win0 : 0)) * kKvHeads + g) * D * ES + c_t * 16;
+    const char* vbase = (const char*)a.cache_v + ((((int64_t)s * a.capacity) - (a.v_windowed ? win0 : 0)) * kKvHeads + g) * D * ES + c_t * 16;
     // ---- Q-hat of the wave's rows (B operand of S^T = K Q^T), made here from the
     // raw Q: QK-norm with gain ("Chapter 9 - The Muse Glimmer architecture" 9.5;
     // "Chapter 14 - QK-norm and RoPE" 14.3), RoPE on sliding layers (Ch 14,
@@ -441,10 +464,27 @@ void prefill_group_kernel(AttnArgs a) {
     // writing Q-hat to HBM and reading it back.  The workgroup's rows share one
     // (cos, sin) table in LDS.
     __shared__ float2 rot[BMW][kHeadDim / 2 + 1];       // padded: rows start 2 banks apart
-    if (a.rope) {
-        float th = 0.0f;                               // theta[lane] without indexing the argument block
+    // the raw Q rows and the first K/V tile go out before the (cos, sin)
+    // table is built, so that both memory round trips overlap it
+    bf16x8 qraw[QG][NST];
 #pragma unroll
-        for (int i = 0; i < 64; ++i) th = (lane == i) ? a.theta[i] : th;
+    for (int qg = 0; qg < QG; ++qg) {
+        const int tq = q0 + 32 * qg + l32;
+        const bf16_t* qrow = (const bf16_t*)a.q + (((int64_t)s * N + min(tq, N - 1)) * kHeads + h) * D;
+#pragma unroll
+        for (int st = 0; st < NST; ++st) qraw[qg][st] = *(const bf16x8*)(qrow + 2 * MQ::KPL * st + MQ::KPL * gl);
+    }
+    u32x4 ka0[NCH], va0[NCH];                          // the loop's first K/V tile
+    if constexpr (!PIPE) {
+#pragma unroll
+        for (int u = 0; u < NCH; ++u) {
+            const int64_t off = (int64_t)min(tile_lo * BN + r_t + u * RSTEP, kv_end - 1) * ROW;
+            ka0[u] = *(const u32x4*)(kbase + off);
+            va0[u] = *(const u32x4*)(vbase + off);
+        }
+    }
+    if (a.rope) {
+        const float th = theta_of_lane<AttnArgs>(lane);
         for (int row = wave; row < BMW; row += WPB) {
             float sn, cs;
             sincosf((float)((int64_t)L + q0 + row) * th, &sn, &cs);
@@ -456,15 +496,13 @@ void prefill_group_kernel(AttnArgs a) {
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
         const int tq = q0 + 32 * qg + l32;
-        const bf16_t* qrow = (const bf16_t*)a.q + (((int64_t)s * N + min(tq, N - 1)) * kHeads + h) * D;
         float x[NST][8];
         float ss = 0.0f;
 #pragma unroll
         for (int st = 0; st < NST; ++st) {
-            const bf16x8 raw = *(const bf16x8*)(qrow + 2 * MQ::KPL * st + MQ::KPL * gl);
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                x[st][t] = (float)raw[t];
+                x[st][t] = (float)qraw[qg][st][t];
                 ss += x[st][t] * x[st][t];
             }
         }
@@ -489,26 +527,6 @@ void prefill_group_kernel(AttnArgs a) {
         }
     }
 
-    // ---- keys the workgroup can see (positions fit in int32: bounded by 2^24)
-    const int W = a.window;
-    const int P0 = L + q0, P1 = L + min(q0 + BMW - 1, N - 1);
-    const int kv_lo = (W > 0) ? max(0, P0 - W + 1) : 0;
-    const int kv_end = L + N;
-    const int tile_lo = kv_lo / BN, tile_hi = P1 / BN;
-    const int ntiles = tile_hi - tile_lo + 1;
-    const int pq0 = L + q0 + l32;                      // position of this lane's row in group 0
-
-    constexpr int64_t ROW = (int64_t)kKvHeads * D * ES;
-    constexpr int RSTEP = NT / CPR;
-    const int r_t = tid / CPR, c_t = tid % CPR;
-    // rows of the K copy (and of V on ring layers) start on sliding layers at
-    // the window's first visible position rounded down to kWindowAlign; every
-    // tile read here starts at or past that (tiles start at multiples of BN,
-    // which divides kWindowAlign)
-    static_assert(kWindowAlign % BN == 0, "key tiles start inside the windowed copy");
-    const int64_t win0 = W > 0 ? max(0, L - W + 1) / kWindowAlign * kWindowAlign : 0;
-    const char* kbase = (const char*)a.kq + ((((int64_t)s * a.kq_capacity) - (a.kq_windowed ? win0 : 0)) * kKvHeads + g) * D * ES + c_t * 16;
-    const char* vbase = (const char*)a.cache_v + ((((int64_t)s * a.capacity) - (a.v_windowed ? win0 : 0)) * kKvHeads + g) * D * ES + c_t * 16;
     u32x4 kreg[NCH], vreg[NCH];
     // Tile rows into registers.  Rows past the last cached position are
     // clamped to it (in-bounds, finite data): every key there lies after
@@ -740,7 +758,15 @@ void prefill_group_kernel(AttnArgs a) {
                     *(u32x4*)(vd + u * RSTEP * LDV * ES) = vr[u];
                 }
             };
-            ld2(ka, va, tile_lo);
+            if (pass == 0) {                           // loaded before Q-hat
+#pragma unroll
+                for (int u = 0; u < NCH; ++u) {
+                    ka[u] = ka0[u];
+                    va[u] = va0[u];
+                }
+            } else {
+                ld2(ka, va, tile_lo);
+            }
             st2(ka, va, 0);
             ld2(kb2, vb2, min(tile_lo + 1, tile_hi));
             __syncthreads();
@@ -753,10 +779,25 @@ void prefill_group_kernel(AttnArgs a) {
                 bool unset[QG];
                 record_unset(unset);
                 floatx16 sc[KT][QG];
+#if MUSE_PREFILL_PRIO == 1 || MUSE_PREFILL_PRIO == 2
+                __builtin_amdgcn_s_setprio(1);
+#endif
                 qk(sc, Ks[cur], nref);
+#if MUSE_PREFILL_PRIO == 1
+                __builtin_amdgcn_s_setprio(0);
+#endif
                 st2(kn, vn, cur ^ 1);                      // that buffer is free since the last barrier
                 fix_tile(sc, (tile_lo + it) * BN, unset);
+#if MUSE_PREFILL_PRIO == 2
+                __builtin_amdgcn_s_setprio(0);
+#endif
+#if MUSE_PREFILL_PRIO == 3
+                __builtin_amdgcn_s_setprio(1);
+#endif
                 softmax_pv(sc, Vs[cur]);
+#if MUSE_PREFILL_PRIO == 3
+                __builtin_amdgcn_s_setprio(0);
+#endif
                 __syncthreads();
             };
             for (int it = 0; it < ntiles; it += 2) {
@@ -817,41 +858,60 @@ void prefill_group_kernel(AttnArgs a) {
         if (!__syncthreads_or(!__builtin_isfinite(chk))) break;
     }
 
-    // ---- epilogue: normalise, gate, store.  All of a row's gate values are
-    // loaded before any output is stored: interleaved, every load would wait
-    // for the stores before it (the two buffers may alias as far as the
-    // compiler knows), one memory round trip per value.
+    // ---- epilogue: normalise, gate, store.  The wave's 32-row x 128 tile goes
+    // through its own LDS buffer: the gate rows are loaded whole (16 lanes per
+    // 256-byte row), read back in the accumulator layout, combined with O and
+    // written back in place, then stored as whole rows.  (Straight from the
+    // accumulator layout every load and store instruction touched 32 rows, 16
+    // bytes in each.)  Only this wave touches its buffer, and a wave's LDS
+    // accesses complete in order, so the phases need no barrier; the wave
+    // barriers keep the compiler from moving accesses across phases.
+    constexpr int LDE = D + 8;                         // 272-byte rows
+    __shared__ __attribute__((aligned(16))) T ebuf[WPB][32 * LDE];
+    T* eb = ebuf[wave];
+    const int er = lane >> 4, ec = lane & 15;          // whole-row phases: row 4u + er, 16-byte chunk ec
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
-        const float l_tot = sum_halves(l_run[qg]);
-        const int tq = q0 + 32 * qg + l32;
-        if (tq >= N) continue;
-        const float inv = 1.0f / l_tot;
-        const int64_t base = (((int64_t)s * N + tq) * kHeads + h) * D;
-        const T* gate = (const T*)a.gate + base;
-        T* dst = out + base;
-        uint2 graw[4][4];                              // dims 32 dt + 8 ig + 4 gl .. + 3
+        const int t0 = q0 + 32 * qg;
+        u32x4 graw[8];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+        for (int u = 0; u < 8; ++u) {
+            const int t = min(t0 + 4 * u + er, N - 1);
+            graw[u] = *(const u32x4*)((const T*)a.gate + (((int64_t)s * N + t) * kHeads + h) * D + 8 * ec);
+        }
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int ig = 0; ig < 4; ++ig) graw[dt][ig] = *(const uint2*)(gate + 32 * dt + 8 * ig + 4 * gl);
+        for (int u = 0; u < 8; ++u) *(u32x4*)(eb + (4 * u + er) * LDE + 8 * ec) = graw[u];
+        __builtin_amdgcn_wave_barrier();
+        const float inv = 1.0f / sum_halves(l_run[qg]);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
             for (int ig = 0; ig < 4; ++ig) {
+                // dims 32 dt + 8 ig + 4 gl .. + 3 of row l32
+                T* e = eb + l32 * LDE + 32 * dt + 8 * ig + 4 * gl;
+                const uint2 g2 = *(const uint2*)e;
                 unsigned packed[2];
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
-                    const unsigned w = x < 2 ? graw[dt][ig].x : graw[dt][ig].y;
+                    const unsigned w = x < 2 ? g2.x : g2.y;
                     const float gv = __uint_as_float((x & 1) ? (w & 0xffff0000u) : (w << 16));
                     const T y = from_f32<T>(o[dt][qg][4 * ig + x] * inv * sigmoid(gv));
-                    const unsigned u = __builtin_bit_cast(unsigned short, y);
-                    if (x & 1) packed[x / 2] |= u << 16;
-                    else packed[x / 2] = u;
+                    const unsigned u16 = __builtin_bit_cast(unsigned short, y);
+                    if (x & 1) packed[x / 2] |= u16 << 16;
+                    else packed[x / 2] = u16;
                 }
-                *(uint2*)(dst + 32 * dt + 8 * ig + 4 * gl) = make_uint2(packed[0], packed[1]);
+                *(uint2*)e = make_uint2(packed[0], packed[1]);
             }
         }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int t = t0 + 4 * u + er;
+            const u32x4 v = *(const u32x4*)(eb + (4 * u + er) * LDE + 8 * ec);
+            if (t < N) *(u32x4*)(out + (((int64_t)s * N + t) * kHeads + h) * D + 8 * ec) = v;
+        }
+        __builtin_amdgcn_wave_barrier();
     }
 }
 

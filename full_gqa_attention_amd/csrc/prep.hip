@@ -124,9 +124,7 @@ __device__ __forceinline__ void prep_kv_bf16(const PrepArgs& a, int blk) {
         raw[i] = *(const u32x4*)src;
         Ls[i] = a.seq_len[tok / a.n_new];
     }
-    float th = 0.0f;                               // theta[lane] without indexing the argument block
-#pragma unroll
-    for (int i = 0; i < 64; ++i) th = (lane == i) ? a.theta[i] : th;
+    const float th = theta_of_lane<PrepArgs>(lane);
 #pragma unroll
     for (int i = 0; i < kKvTokensPerWave; ++i) {
         const int tok = tok0 + i;

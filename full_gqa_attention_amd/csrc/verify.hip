@@ -70,9 +70,7 @@ void verify_kernel(VerifyArgs a) {
     // ---- Q-hat of this lane's row (B operand of S^T = K Q^T; the row's other
     // 64 values sit in lane l ^ 32)
     if (a.rope) {
-        float th = 0.0f;                               // theta[lane] without indexing the argument block
-#pragma unroll
-        for (int i = 0; i < 64; ++i) th = (lane == i) ? a.theta[i] : th;
+        const float th = theta_of_lane<VerifyArgs>(lane);
         for (int tt = wave; tt < kVerifyTokens; tt += NT / 64) {
             float sn, cs;
             sincosf((float)(L + tt) * th, &sn, &cs);
