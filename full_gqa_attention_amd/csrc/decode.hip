@@ -260,7 +260,7 @@ void decode_kernel(DecodeArgs a) {
     float2* rot = (float2*)Vw;
     if (a.rope) {
         float sn, cs_;
-        sincosf((float)p * th, &sn, &cs_);
+        sincos_rope((float)p * th, &sn, &cs_);
         rot[lane] = make_float2(cs_, sn);
     }
     auto rotate = [&](float& y0, float& y1, int pair) __attribute__((always_inline)) {

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "trig.h"
+
 namespace muse {
 
 typedef __bf16 bf16_t;
@@ -95,8 +97,13 @@ __device__ __forceinline__ float wave_sum(float x) {
 // domain: scores are pre-multiplied by scale * log2(e).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// sigma(g) = 1 / (1 + e^-g).
-__device__ __forceinline__ float sigmoid(float g) { return 1.0f / (1.0f + __expf(-g)); }
+// sigma(g) = 1 / (1 + e^-g), with the hardware reciprocal (about 1 ulp; an
+// IEEE division costs a dozen instructions per value, and the prefill
+// epilogue evaluates 4,096 of these per token).  For g below about -88,
+// e^-g overflows to inf and the reciprocal gives 0, the correct limit.
+__device__ __forceinline__ float sigmoid(float g) {
+    return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-g * 1.4426950408889634f));
+}
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -104,9 +111,6 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // One head vector of 128 values per wave: lane i holds the adjacent pair
 // (x[2i], x[2i+1]), which is RoPE pair i.
 
-// sin/cos of the f32 angle f32(p) * theta[lane] (accurate sincosf).  The
-// table sits in kernel arguments; the unrolled select keeps every access at
-// a constant index.
 // theta[lane] of a kernel whose only argument is the struct Args (so the
 // struct sits at the start of the kernel's argument block): one vector load
 // at the table's offset.  Selecting it out of the scalar copies of the
@@ -118,13 +122,16 @@ __device__ __forceinline__ float theta_of_lane(int lane) {
                  (KArg)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(Args, theta)) + lane);
 }
 
+// sin/cos of the f32 angle f32(p) * theta[lane] (accurate: trig.h).  The
+// table sits in kernel arguments; the unrolled select keeps every access at
+// a constant index.
 __device__ __forceinline__ void rope_sincos(const float (&theta)[64], int lane, int64_t p,
                                             float& sn, float& cs) {
     float th = 0.0f;
 #pragma unroll
     for (int i = 0; i < 64; ++i) th = (lane == i) ? theta[i] : th;
     const float ang = (float)p * th;
-    sincosf(ang, &sn, &cs);
+    sincos_rope(ang, &sn, &cs);
 }
 
 // RMS-normalise the wave's 128-vector, scale by gain, then (rope) rotate the

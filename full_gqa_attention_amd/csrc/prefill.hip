@@ -458,7 +458,7 @@ void prefill_group_kernel(AttnArgs a) {
     // ---- Q-hat of the wave's rows (B operand of S^T = K Q^T), made here from the
     // raw Q: QK-norm with gain ("Chapter 9 - The Muse Glimmer architecture" 9.5;
     // "Chapter 14 - QK-norm and RoPE" 14.3), RoPE on sliding layers (Ch 14,
-    // 14.4-14.5: angle f32(p) * theta_i in f32, accurate sincosf), then
+    // 14.4-14.5: angle f32(p) * theta_i in f32, accurate sin and cos), then
     // attn_scale * log2(e), rounded to fp16.  Each (row, head) is made by
     // exactly one wave, so this costs no more than a separate pass and saves
     // writing Q-hat to HBM and reading it back.  The workgroup's rows share one
@@ -487,7 +487,7 @@ void prefill_group_kernel(AttnArgs a) {
         const float th = theta_of_lane<AttnArgs>(lane);
         for (int row = wave; row < BMW; row += WPB) {
             float sn, cs;
-            sincosf((float)((int64_t)L + q0 + row) * th, &sn, &cs);
+            sincos_rope((float)((int64_t)L + q0 + row) * th, &sn, &cs);
             rot[row][lane] = make_float2(cs, sn);
         }
         __syncthreads();

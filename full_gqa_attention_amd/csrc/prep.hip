@@ -14,7 +14,7 @@
 //     ("Chapter 9 - The Muse Glimmer architecture" 9.5 RMSNorm formula;
 //     "Chapter 14 - QK-norm and RoPE" 14.3: Q gain about 3.87, K gain 1).
 //   * RoPE (sliding layers only): angle = f32(p) * theta_i in f32 with the
-//     f32 table theta_i = base^(-2i/128); accurate sincosf, no fast math
+//     f32 table theta_i = base^(-2i/128); accurate sin and cos (trig.h)
 //     (Ch 14, 14.4.1 table, 14.4.2 rotation, 14.5 kernel).
 //   * Append: the rotated K goes to cache row p, V is copied unchanged
 //     (Ch 14, 14.7: keys rotate before the store; V never rotates).
@@ -157,7 +157,7 @@ __device__ __forceinline__ void prep_kv_bf16(const PrepArgs& a, int blk) {
         for (int j = 0; j < 8; ++j) y[j] = (y[j] * r) * a.k_gain;
         if (a.rope) {
             float sn, cs;
-            sincosf((float)p * th, &sn, &cs);
+            sincos_rope((float)p * th, &sn, &cs);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float c2 = __shfl(cs, 4 * sub + j, 64), s2 = __shfl(sn, 4 * sub + j, 64);

@@ -73,7 +73,7 @@ void verify_kernel(VerifyArgs a) {
         const float th = theta_of_lane<VerifyArgs>(lane);
         for (int tt = wave; tt < kVerifyTokens; tt += NT / 64) {
             float sn, cs;
-            sincosf((float)(L + tt) * th, &sn, &cs);
+            sincos_rope((float)(L + tt) * th, &sn, &cs);
             rot[tt][lane] = make_float2(cs, sn);
         }
         __syncthreads();
