@@ -243,6 +243,8 @@ def parse():
                     help="also time the 52-layer schedule workload (chunked prefill phase + 256 decode steps)")
     ap.add_argument("--ring", action="store_true",
                     help="sliding layers keep their window in a ring cache (kv_ring) in the decode and schedule runs")
+    ap.add_argument("--verify", action="store_true",
+                    help="also time the 16-token verify call (64 x 8,192 cached rows, both layers)")
     ap.add_argument("--relocate", action="store_true",
                     help="also time NoPE tile relocation (muse_kv_relocate) of a 64 x 8,192 full-layer cache")
     ap.add_argument("--eager", action="store_true",
@@ -512,6 +514,46 @@ def bench_schedule(w, fa, synth, torch, ring=False):
                        "launch": "each step (52 decode calls + seq_len increment) replayed from a HIP graph"}}
 
 
+def bench_verify(fa, synth, torch, steps=20, warmup=3, n_new=16):
+    """Multi-token verify: 16 drafted tokens per sequence scored against the
+    64 x 8,192 cached rows (the drafting-and-verifying section of "How Muse
+    Glimmer Fits an Agent on Your Device"), one sliding and one full layer,
+    through muse_attn_prefill (which takes the verify kernels for such short
+    bf16 chunks).  The roofline is HBM: the call reads every visible cache row
+    once (1,024 B per row per sequence) and does 16,384 flop per visible
+    (query, key) pair, 256 flop per byte at 16 tokens, under the 312 flop/B
+    ridge of 2.5 PFLOP/s over 8 TB/s.  Kernel time = the split kernel and the
+    merge kernel, between the library's events; call = prep (append) too."""
+    import dataclasses
+    base = synth.WORKLOADS["decode_64x8192_bf16"]
+    w = dataclasses.replace(base, name="verify_64x8192p16_bf16", n_new=n_new)
+    runs = [LayerRun(w, spec, 2, False, fa, synth) for spec in w.layers]
+    torch.cuda.synchronize()
+    wall, per_launch = run_timed(runs, steps, warmup, 2, fa, torch)
+    per_layer, total_bytes, total_kern = {}, 0, 0.0
+    for j, r in enumerate(runs):
+        lt = per_launch[j::len(runs)]
+        avg = sum(lt) / len(lt)
+        rows = sum(visible_rows(r.spec, w.prefix + t) for t in range(n_new)) // n_new   # per token, ~window or L
+        kv = w.n_seq * (min(w.prefix + n_new, r.spec.window + n_new - 1) if r.spec.window else w.prefix + n_new) * 1024
+        flop = FLOP_PER_PAIR * w.n_seq * prefill_pairs(r.spec, w.prefix, n_new)
+        per_layer[r.spec.name] = {"kernel_us": round(avg * 1e3, 2), "kv_MB": round(kv / 1e6, 3),
+                                  "kernel_GBps": round(kv / (avg * 1e-3) / 1e9, 1),
+                                  "kernel_TFLOPs": round(flop / (avg * 1e-3) / 1e12, 1),
+                                  "visible_rows_per_token": rows,
+                                  "p10_p50_p90_us": [round(x * 1e3, 2) for x in percentiles(lt)]}
+        total_bytes += kv
+        total_kern += avg
+    achieved = total_bytes / (total_kern * 1e-3) / 1e9
+    return {"workload": w.name, "n_seq": w.n_seq, "cached_tokens": w.prefix, "new_tokens": n_new,
+            "call_us_per_layer": round(wall / steps / len(runs) * 1e6, 2),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "muse::verify_kernel + muse::verify_merge_kernel (bf16)",
+                         "per_layer": per_layer},
+            "steps": steps, "warmup": warmup}
+
+
 def bench_relocate(fa, synth, torch, steps=10):
     """NoPE tile relocation ("Chapter 14 - QK-norm and RoPE" 14.6): the whole
     cache of a full layer of the 64 x 8,192 decode workload, moved as 512-row
@@ -641,6 +683,9 @@ def main():
     if not args.no_prefill:
         pw = synth.WORKLOADS[args.prefill_workload]
         line["prefill"] = bench_prefill(pw, args.prefill_steps, 2, fa, synth, torch)
+    if args.verify:
+        torch.cuda.empty_cache()
+        line["verify"] = bench_verify(fa, synth, torch)
     if args.relocate:
         torch.cuda.empty_cache()
         line["relocate"] = bench_relocate(fa, synth, torch)

@@ -54,14 +54,6 @@
 
 namespace muse {
 
-// Split partials cross workgroups (and XCDs): written and read with
-// agent-scope atomic accesses, which are coherent per access.
-__device__ __forceinline__ void publish(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float observe(const float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 template <typename T> struct DecodeTraits;
 // bf16: K in registers in MFMA layout (4 x 16 B per lane), V row-major (4 x 16 B)
@@ -85,13 +77,6 @@ struct SubTile {
     u32x4 v[DecodeTraits<T>::VREG];
 };
 
-// Vector accesses to the split partials with the same per-dword coherence as
-// the agent-scope atomics above (the sc1 cache policy).  The buffer resource
-// spans one (sequence, KV head)'s partials; an access beyond it reads zeros.
-constexpr int kCoherent = 16;                          // sc1
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
-}
 
 template <typename T, int DEPTH>
 __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(MUSE_DECODE_WAVES, MUSE_DECODE_WAVES)))
@@ -533,28 +518,9 @@ void decode_kernel(DecodeArgs a) {
     const int n_grps = (n_live + G - 1) / G;
     const int grp = c / G, c0 = grp * G, gsize = min(G, n_live - c0);
     if (tid == 0) {
-        // count this split's arrival on a tagged word (tag << 32 | count); true
-        // for the arrival that completes n, which resets the word for a replay
-        // with the same tag.  The first attempt assumes it completes n: right
-        // for the split whose merge ends the call, one round trip saved.
-        auto arrive = [&](unsigned long long* word, int n) {
-            unsigned long long old = ((unsigned long long)a.tag << 32) | (unsigned int)(n - 1);
-            unsigned int arrived = 0;
-            for (;;) {                                 // retries only on contention
-                const unsigned int cnt = ((unsigned int)(old >> 32) == a.tag) ? (unsigned int)old : 0u;
-                const unsigned long long want = ((unsigned long long)a.tag << 32) | (cnt + 1);
-                if (__hip_atomic_compare_exchange_strong(word, &old, want, __ATOMIC_RELAXED,
-                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-                    arrived = cnt + 1;
-                    break;
-                }
-            }
-            const bool done = arrived == (unsigned int)n;
-            if (done)
-                __hip_atomic_store(word, (unsigned long long)a.tag << 32, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            return done;
-        };
+        // count this split's arrival (arrive_tagged: the first attempt assumes
+        // it completes n, right for the split whose merge ends the call)
+        auto arrive = [&](unsigned long long* word, int n) { return arrive_tagged(word, a.tag, n); };
         unsigned long long* words = a.arrivals + (int64_t)(s * kKvHeads + g) * kArriveWords;   // pair, then groups
         int role = 0;                                  // 0 publish, 1 group merger, 2 final merger
         if (n_grps == 1) role = arrive(words, n_live) ? 2 : 0;

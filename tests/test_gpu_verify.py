@@ -117,3 +117,37 @@ def test_verify_reference_far_below_row_max():
     ck[0, 100] = u
     inp.cache_k.copy_(ck.to(inp.cache_k.dtype))
     check_layer(w, spec, inp, decode=False)
+
+
+@pytest.mark.parametrize("lens", [[40000], [3000, 2047, 100, 0]], ids=["one_seq_many_splits", "ragged"])
+def test_verify_graph_replays_match_eager(lens):
+    """A captured verify call (split kernel, then merge kernel) replays with new
+    inputs copied in and eager work in between; every replay must equal the
+    eager result on the same inputs, bit for bit."""
+    spec = synth.full()
+    N, L = 16, max(lens)
+    w, inp = _inputs(spec, lens, N, config=96)
+    lay = fa.make_layer(spec.kind, window=spec.window, rope_theta=spec.rope_theta, dtype=w.dtype)
+    ws = fa.workspace(lay, len(lens), N, L, False)
+    q, k, v, g = inp.q.clone(), inp.k.clone(), inp.v.clone(), inp.gate.clone()
+    out = torch.empty_like(g)
+    ck, cv = inp.cache_k.clone(), inp.cache_v.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                         # warm-up outside the capture
+        fa.prefill(lay, q, k, v, g, ck, cv, inp.seq_len, out, max_seq_len=L, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fa.prefill(lay, q, k, v, g, ck, cv, inp.seq_len, out, max_seq_len=L, workspace=ws)
+    for rep in range(3):
+        new = synth.layer_inputs(w, spec, device=DEV, n_new=N, prefix=0, step=20 + rep, with_cache=False)
+        q.copy_(new.q); k.copy_(new.k); v.copy_(new.v); g.copy_(new.gate)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        eager = fa.prefill(lay, q, k, v, g, ck.clone(), cv.clone(), inp.seq_len, max_seq_len=L)
+        torch.cuda.synchronize()
+        assert torch.equal(got, eager), f"replay {rep}"
