@@ -107,6 +107,10 @@ def _load():
             ctypes.c_int, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
             vp, vp, dp, dp, dp]
         lib.oracle_attn_rows.restype = ctypes.c_int
+        lib.oracle_out_proj.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp,
+                                        ctypes.c_double, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64),
+                                        dp, dp]
+        lib.oracle_out_proj.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -223,3 +227,42 @@ def all_rows(n_seq: int, n_new: int) -> np.ndarray:
     """Every (s, t) row of an [S, N] batch, in row-major order."""
     s, t = np.meshgrid(np.arange(n_seq), np.arange(n_new), indexing="ij")
     return np.stack([s.ravel(), t.ravel()], axis=1).astype(np.int32)
+
+
+# ------------------------------------------------- next step: o_proj + post-norm
+
+POST_NORM_EPS = 1e-8      # [Ch9] 9.9: the post-sublayer norms' own epsilon
+HIDDEN = 6656             # model width ([Ch9] 9.8: o_proj [4096 -> 6656])
+
+
+def out_proj_rows(attn, w, gamma, residual, rows=None, eps: float = POST_NORM_EPS, want_proj: bool = False):
+    """The attention block's tail on chosen token rows ([Ch9] 9.8, 9.9 and
+    Figure 9.1): y = RMSNorm_eps(attn . W^T) * gamma + residual.
+
+    attn      [M, K] bf16 bit patterns (uint16): the gated attention output
+    w         [N, K] bf16 bit patterns: o_proj, one row per output channel
+    gamma     [N] float32: the post-attention norm's effective gain
+    residual  [M, N] bf16 bit patterns
+    rows      int array of token indices (default: all M)
+    Returns y [R, N] float64 (and proj [R, N] float64 when want_proj).
+    """
+    attn = _storage(attn, BF16)
+    w = _storage(w, BF16)
+    residual = _storage(residual, BF16)
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    M, K = attn.shape
+    N = w.shape[0]
+    if w.shape != (N, K) or gamma.shape != (N,) or residual.shape != (M, N):
+        raise ValueError("shapes must be attn [M, K], w [N, K], gamma [N], residual [M, N]")
+    rows = np.arange(M, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    R = rows.size
+    y = np.empty((R, N), dtype=np.float64)
+    proj = np.empty((R, N), dtype=np.float64) if want_proj else None
+    rc = _load().oracle_out_proj(M, K, N, attn.ctypes.data, w.ctypes.data, gamma.ctypes.data,
+                                 residual.ctypes.data, float(eps), R,
+                                 rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _dp(y),
+                                 _dp(proj) if want_proj else None)
+    if rc != 0:
+        raise ValueError("oracle_out_proj rejected its arguments")
+    return (y, proj) if want_proj else y
+

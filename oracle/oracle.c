@@ -307,3 +307,65 @@ int oracle_attn_rows(const oracle_layer* L, int n_seq, int n_new, const int32_t*
     free(vst);
     return bad ? -1 : 0;
 }
+
+/* ------------------------------- next step: o_proj and the post-attention norm */
+
+/*
+ * The attention block's tail ([Ch9] 9.8 and 9.9, Figure 9.1): the gated
+ * attention output goes through o_proj [4096 -> 6656], the post-attention
+ * RMSNorm (its own epsilon, 1e-8 in the model) scales the projection, and
+ * the result joins the residual stream:
+ *
+ *   proj[n] = sum_k attn[k] * W[n][k]              (W is [n_out][k_in])
+ *   y[n]    = proj[n] / sqrt(mean_n(proj^2) + eps) * gamma[n] + residual[n]
+ *
+ * gamma is the norm's effective gain: [News] ("Sandwich norms control what
+ * each branch writes") stores it as an offset from one; the caller passes
+ * the gain itself.  attn, W and residual are bf16 bit patterns; gamma is f32.
+ * Rows (tokens) are independent, so a chosen list of rows is evaluated.
+ * Everything is double; nothing is rounded.  proj_out may be NULL.
+ * Returns 0, or -1 on bad arguments / allocation failure.
+ */
+int oracle_out_proj(int64_t n_rows_total, int k_in, int n_out, const uint16_t* attn, const uint16_t* w,
+                    const float* gamma, const uint16_t* residual, double eps,
+                    int64_t n_rows, const int64_t* rows, double* y_out, double* proj_out) {
+    if (k_in <= 0 || n_out <= 0 || n_rows < 0 || !attn || !w || !gamma || !residual || !rows || !y_out)
+        return -1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= n_rows_total) return -1;
+    double* wd = (double*)malloc(sizeof(double) * (size_t)n_out * (size_t)k_in);
+    if (!wd) return -1;
+    for (int64_t i = 0; i < (int64_t)n_out * k_in; ++i) wd[i] = bf16_bits_to_double(w[i]);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t t = rows[r];
+        double* x = (double*)malloc(sizeof(double) * (size_t)k_in);
+        double* p = (double*)malloc(sizeof(double) * (size_t)n_out);
+        if (!x || !p) {
+            free(x);
+            free(p);
+#pragma omp atomic write
+            bad = 1;
+            continue;
+        }
+        for (int k = 0; k < k_in; ++k) x[k] = bf16_bits_to_double(attn[t * k_in + k]);
+        double ss = 0.0;
+        for (int n = 0; n < n_out; ++n) {
+            const double* wr = wd + (int64_t)n * k_in;
+            double acc = 0.0;
+            for (int k = 0; k < k_in; ++k) acc += x[k] * wr[k];
+            p[n] = acc;
+            ss += acc * acc;
+        }
+        const double inv = 1.0 / sqrt(ss / (double)n_out + eps);
+        for (int n = 0; n < n_out; ++n) {
+            y_out[r * n_out + n] = p[n] * inv * (double)gamma[n] + bf16_bits_to_double(residual[t * n_out + n]);
+            if (proj_out) proj_out[r * n_out + n] = p[n];
+        }
+        free(x);
+        free(p);
+    }
+    free(wd);
+    return bad ? -1 : 0;
+}
