@@ -31,7 +31,7 @@ STATUS = {0: "MUSE_OK", 1: "MUSE_ERR_NULL", 2: "MUSE_ERR_SHAPE", 3: "MUSE_ERR_LA
 
 EXPORTS = ("muse_attn_prefill", "muse_attn_decode", "muse_attn_workspace_size",
            "muse_attn_layer_init", "muse_layer_kind_for", "muse_rope_theta_table",
-           "muse_status_str", "muse_kv_relocate")
+           "muse_status_str", "muse_kv_relocate", "muse_out_proj", "muse_out_proj_workspace_size")
 
 
 class MuseError(RuntimeError):
@@ -100,6 +100,11 @@ def lib() -> ctypes.CDLL:
         cp = ctypes.POINTER(KvCache)
         L.muse_kv_relocate.argtypes = [lp, cp, i32, cp, i32, ctypes.POINTER(KvTile), i32, vp]
         L.muse_kv_relocate.restype = ctypes.c_int
+        L.muse_out_proj.argtypes = [i32, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp,
+                                    ctypes.POINTER(KernelTimer)]
+        L.muse_out_proj.restype = ctypes.c_int
+        L.muse_out_proj_workspace_size.argtypes = [i32, ctypes.POINTER(sz)]
+        L.muse_out_proj_workspace_size.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -278,3 +283,46 @@ def kv_relocate(layer: Layer, src_k, src_v, dst_k, dst_v, tiles, stream=None) ->
     rc = lib().muse_kv_relocate(ctypes.byref(layer), ctypes.byref(src), src_k.shape[0], ctypes.byref(dst),
                                 dst_k.shape[0], arr, n_tiles, ctypes.c_void_p(stream))
     _check(rc, "muse_kv_relocate")
+
+
+# ------------------------------------------ the block's tail: o_proj + post-norm
+
+MODEL_DIM = 6656
+POST_NORM_EPS = 1e-8
+
+
+def out_proj_workspace_size(n_tokens: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().muse_out_proj_workspace_size(n_tokens, ctypes.byref(n)), "muse_out_proj_workspace_size")
+    return n.value
+
+
+def out_proj(attn, w, gamma, residual, out=None, *, eps: float = POST_NORM_EPS,
+             workspace: Optional[torch.Tensor] = None, stream=None,
+             timer: Optional[KernelTimer] = None) -> torch.Tensor:
+    """muse_out_proj on torch tensors (see include/muse_attn.h): attn [..., 4096]
+    bf16 (the attention output), w [6656, 4096] bf16, gamma [6656] f32,
+    residual [..., 6656] bf16; returns hidden [..., 6656] bf16 (out may be
+    residual itself)."""
+    lead = tuple(attn.shape[:-1])
+    M = 1
+    for d in lead:
+        M *= d
+    _expect(attn, "attn", lead + (ATTN_DIM,), torch.bfloat16)
+    _expect(w, "w", (MODEL_DIM, ATTN_DIM), torch.bfloat16)
+    _expect(gamma, "gamma", (MODEL_DIM,), torch.float32)
+    _expect(residual, "residual", lead + (MODEL_DIM,), torch.bfloat16)
+    if out is None:
+        out = torch.empty(residual.shape, dtype=torch.bfloat16, device=residual.device)
+    _expect(out, "out", lead + (MODEL_DIM,), torch.bfloat16)
+    if workspace is None:
+        workspace = torch.empty(max(out_proj_workspace_size(M), 16), dtype=torch.uint8, device=attn.device)
+    _expect(workspace, "workspace", None, torch.uint8)
+    if stream is None:
+        stream = torch.cuda.current_stream(attn.device).cuda_stream
+    tptr = ctypes.byref(timer) if timer is not None else None
+    _check(lib().muse_out_proj(M, _ptr(attn), _ptr(w), _ptr(gamma), _ptr(residual), _ptr(out), float(eps),
+                               _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream), tptr),
+           "muse_out_proj")
+    return out
+

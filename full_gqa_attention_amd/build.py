@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libmuse_attn.so")
-SOURCES = ["muse_attn.cpp", "prep.hip", "prefill.hip", "decode.hip", "relocate.hip", "verify.hip"]
+SOURCES = ["muse_attn.cpp", "prep.hip", "prefill.hip", "decode.hip", "relocate.hip", "verify.hip",
+           "outproj.hip"]
 ARCH = "gfx950"
 # The prefill kernels keep their Q.K and P.V accumulators in VGPRs: the scores
 # feed the VALU softmax directly, and the AGPRs serve as spill space.

@@ -148,6 +148,21 @@ struct RelocArgs {
 };
 
 // Launch geometry shared by the host code and the kernels.
+// The block's tail after attention: o_proj [4096 -> 6656] into an f32
+// workspace, then the post-attention RMSNorm with the residual add.
+constexpr int kAttnDim = 4096;
+constexpr int kModelDim = 6656;
+struct OutProjArgs {
+    const void* attn;       // bf16 [m][4096]
+    const void* w;          // bf16 [6656][4096]
+    const float* gamma;     // f32 [6656]
+    const void* residual;   // bf16 [m][6656]
+    void* out;              // bf16 [m][6656] (may be residual itself)
+    float* proj;            // f32 [m][6656] workspace
+    int32_t m;              // tokens
+    float eps;
+};
+
 constexpr int kPrefillBM = 128;  // query rows per prefill workgroup (4 waves x 32)
 constexpr int kPrefillBN = 64;   // keys per prefill tile
 constexpr int kDecodeTile = 64;  // split granularity of the decode (keys)
@@ -171,5 +186,7 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_relocate(const RelocArgs& a, hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_verify_merge(const VerifyArgs& a, hipStream_t stream);
+hipError_t launch_out_proj_gemm(const OutProjArgs& a, hipStream_t stream);
+hipError_t launch_out_proj_norm(const OutProjArgs& a, hipStream_t stream);
 
 }  // namespace muse

@@ -555,6 +555,56 @@ muse_status muse_rope_theta_table(float theta, float* out_host64) {
     return MUSE_OK;
 }
 
+muse_status muse_out_proj_workspace_size(int32_t n_tokens, size_t* bytes) {
+    if (!bytes) return MUSE_ERR_NULL;
+    if (n_tokens < 0 || n_tokens > kMaxPositions) return MUSE_ERR_SHAPE;
+    *bytes = round_up((size_t)n_tokens * muse::kModelDim * sizeof(float), kAlign);
+    return MUSE_OK;
+}
+
+muse_status muse_out_proj(int32_t n_tokens, const void* attn, const void* w, const float* gamma,
+                          const void* residual, void* hidden_out, float eps,
+                          void* workspace, size_t workspace_bytes,
+                          hipStream_t stream, const muse_kernel_timer* timer) {
+    if (!attn || !w || !gamma || !residual || !hidden_out || !workspace) return MUSE_ERR_NULL;
+    if (timer && (!timer->start || !timer->stop)) return MUSE_ERR_NULL;
+    size_t need = 0;
+    muse_status st = muse_out_proj_workspace_size(n_tokens, &need);
+    if (st != MUSE_OK) return st;
+    if (!finite_pos(eps)) return MUSE_ERR_LAYER;
+    if (!aligned16(attn) || !aligned16(w) || !aligned16(gamma) || !aligned16(residual) || !aligned16(hidden_out) ||
+        !aligned16(workspace))
+        return MUSE_ERR_ALIGN;
+    if (workspace_bytes < need) return MUSE_ERR_WORKSPACE;
+    const size_t M = (size_t)n_tokens;
+    auto range = [](const void* p, size_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + bytes}; };
+    const Range ra = range(attn, M * muse::kAttnDim * 2), rw = range(w, (size_t)muse::kModelDim * muse::kAttnDim * 2),
+                rg = range(gamma, muse::kModelDim * 4), rr = range(residual, M * muse::kModelDim * 2),
+                ro = range(hidden_out, M * muse::kModelDim * 2), rs = range(workspace, need);
+    if (M > 0) {
+        // hidden_out may be the residual itself (each element is read, then written, by one thread)
+        if ((hidden_out != residual && overlap(ro, rr)) || overlap(ro, ra) || overlap(ro, rw) || overlap(ro, rg))
+            return MUSE_ERR_ALIAS;
+        if (overlap(rs, ra) || overlap(rs, rw) || overlap(rs, rg) || overlap(rs, rr) || overlap(rs, ro))
+            return MUSE_ERR_ALIAS;
+    }
+    if (n_tokens == 0) return MUSE_OK;
+    muse::OutProjArgs oa;
+    oa.attn = attn;
+    oa.w = w;
+    oa.gamma = gamma;
+    oa.residual = residual;
+    oa.out = hidden_out;
+    oa.proj = (float*)workspace;
+    oa.m = n_tokens;
+    oa.eps = eps;
+    if (timer && hipEventRecord(timer->start, stream) != hipSuccess) return MUSE_ERR_HIP;
+    if (muse::launch_out_proj_gemm(oa, stream) != hipSuccess) return MUSE_ERR_HIP;
+    if (timer && hipEventRecord(timer->stop, stream) != hipSuccess) return MUSE_ERR_HIP;
+    if (muse::launch_out_proj_norm(oa, stream) != hipSuccess) return MUSE_ERR_HIP;
+    return MUSE_OK;
+}
+
 const char* muse_status_str(muse_status s) {
     switch (s) {
         case MUSE_OK: return "MUSE_OK";

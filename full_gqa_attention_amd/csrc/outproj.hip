@@ -1,0 +1,190 @@
+// outproj.hip -- the attention block's tail after the gate ("Chapter 9 - The
+// Muse Glimmer architecture" 9.8 and 9.9, Figure 9.1): o_proj maps the 4,096
+// gated attention channels of each token to the model width 6,656, the
+// post-attention RMSNorm (its own epsilon, 1e-8 in the model) scales each
+// token's projection, and the result joins the residual stream.
+//
+// Two kernels.  The projection is a plain GEMM, proj = attn . W^T, on
+// v_mfma_f32_32x32x16_bf16 with f32 accumulation, written in f32 to the
+// workspace.  The norm needs a whole 6,656-wide row, which no GEMM tile holds,
+// so a second, memory-bound kernel takes one row per workgroup: sum of
+// squares, 1 / sqrt(mean + eps), times the gain, plus the residual, rounded
+// once to bf16.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace muse {
+
+// ---- GEMM: a workgroup computes a 256 x 128 tile of proj with 8 waves (4
+// along the tokens x 2 along the channels, 64 x 64 each: 2 x 2 MFMA tiles).
+// K advances 64 at a time through two LDS buffers; global loads run two
+// k-steps ahead in alternating register sets.  Both operands are K-contiguous
+// (attn rows and W rows), so every MFMA operand is one 16-byte LDS read.
+constexpr int kOpBM = 256, kOpBN = 128, kOpBK = 64;
+constexpr int kOpLds = kOpBK + 8;                      // 144-byte rows: b128 reads conflict-free
+constexpr int kOpThreads = 512;
+constexpr int kOpAChunks = kOpBM * kOpBK * 2 / 16 / kOpThreads;   // 16-byte chunks per thread (4)
+constexpr int kOpBChunks = kOpBN * kOpBK * 2 / 16 / kOpThreads;   // (2)
+static_assert(kModelDim % kOpBN == 0 && kAttnDim % kOpBK == 0, "tile sizes divide the shapes");
+
+__global__ __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void out_proj_gemm_kernel(OutProjArgs a) {
+    using MP = Mma32<bf16_t>;
+    constexpr int K = kAttnDim, N = kModelDim, NK = K / kOpBK;
+    __shared__ __attribute__((aligned(16))) bf16_t As[2][kOpBM * kOpLds];
+    __shared__ __attribute__((aligned(16))) bf16_t Bs[2][kOpBN * kOpLds];
+
+    const int nblk = N / kOpBN;
+    const int nb = blockIdx.x % nblk, mb = blockIdx.x / nblk;   // the channel blocks of a token block run together
+    const int m0 = mb * kOpBM, n0 = nb * kOpBN;
+    const int M = a.m;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, gl = lane >> 5;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // staging: chunk c = tid + 512 u is row c / 8, 16-byte piece c % 8 of a 64-wide k slice
+    const bf16_t* A = (const bf16_t*)a.attn;
+    const bf16_t* B = (const bf16_t*)a.w;
+    auto load = [&](u32x4 (&ra)[kOpAChunks], u32x4 (&rb)[kOpBChunks], int ks) __attribute__((always_inline)) {
+        const int k0 = min(ks, NK - 1) * kOpBK;                  // past the end: harmless repeats
+#pragma unroll
+        for (int u = 0; u < kOpAChunks; ++u) {
+            const int c = tid + kOpThreads * u, r = c >> 3, p = c & 7;
+            const int row = min(m0 + r, M - 1);                  // rows past the last token repeat it
+            ra[u] = *(const u32x4*)(A + (int64_t)row * K + k0 + 8 * p);
+        }
+#pragma unroll
+        for (int u = 0; u < kOpBChunks; ++u) {
+            const int c = tid + kOpThreads * u, r = c >> 3, p = c & 7;
+            rb[u] = *(const u32x4*)(B + (int64_t)(n0 + r) * K + k0 + 8 * p);
+        }
+    };
+    auto store = [&](const u32x4 (&ra)[kOpAChunks], const u32x4 (&rb)[kOpBChunks], int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kOpAChunks; ++u) {
+            const int c = tid + kOpThreads * u, r = c >> 3, p = c & 7;
+            *(u32x4*)(As[buf] + r * kOpLds + 8 * p) = ra[u];
+        }
+#pragma unroll
+        for (int u = 0; u < kOpBChunks; ++u) {
+            const int c = tid + kOpThreads * u, r = c >> 3, p = c & 7;
+            *(u32x4*)(Bs[buf] + r * kOpLds + 8 * p) = rb[u];
+        }
+    };
+
+    floatx16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
+    // C[m][n] += A[m][k] W[n][k]: lane (l32, gl) gives A row l32 and W row l32
+    // (the B column), k = 8 gl .. 8 gl + 7 of each 16-wide step
+    auto compute = [&](int buf) __attribute__((always_inline)) {
+        const bf16_t* Ab = As[buf] + (64 * wm + l32) * kOpLds + 8 * gl;
+        const bf16_t* Bb = Bs[buf] + (64 * wn + l32) * kOpLds + 8 * gl;
+#pragma unroll
+        for (int kk = 0; kk < kOpBK / 16; ++kk) {
+            bf16x8 af[2], bfr[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) af[i] = *(const bf16x8*)(Ab + 32 * i * kOpLds + 16 * kk);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bfr[j] = *(const bf16x8*)(Bb + 32 * j * kOpLds + 16 * kk);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = MP::mma(af[i], bfr[j], acc[i][j]);
+        }
+    };
+
+    u32x4 ra0[kOpAChunks], rb0[kOpBChunks], ra1[kOpAChunks], rb1[kOpBChunks];
+    load(ra0, rb0, 0);
+    store(ra0, rb0, 0);
+    load(ra1, rb1, 1);
+    __syncthreads();
+    // step ks: buffer ks & 1 holds k-slice ks, (rn, bn) holds slice ks + 1,
+    // (rf, bf) receives slice ks + 2
+    auto step = [&](int ks, u32x4 (&rn)[kOpAChunks], u32x4 (&bn)[kOpBChunks],
+                    u32x4 (&rf)[kOpAChunks], u32x4 (&bf)[kOpBChunks]) __attribute__((always_inline)) {
+        load(rf, bf, ks + 2);
+        compute(ks & 1);
+        store(rn, bn, (ks + 1) & 1);                   // free since the last barrier
+        __syncthreads();
+    };
+    static_assert(NK % 2 == 0, "k-steps come in pairs");
+    for (int ks = 0; ks < NK; ks += 2) {
+        step(ks, ra1, rb1, ra0, rb0);
+        step(ks + 1, ra0, rb0, ra1, rb1);
+    }
+
+    // ---- proj rows m0 + 64 wm + 32 i + 8 (e / 4) + 4 gl + e % 4, channel
+    // n0 + 64 wn + 32 j + l32: 32 lanes store 128 contiguous bytes per item
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int m = m0 + 64 * wm + 32 * i + 8 * (e / 4) + 4 * gl + (e % 4);
+            if (m >= M) continue;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) a.proj[(int64_t)m * N + n0 + 64 * wn + 32 * j + l32] = acc[i][j][e];
+        }
+}
+
+// ---- post-attention RMSNorm + residual: one token row per workgroup, 256
+// threads, 4 channels per thread and step (6,656 = 1,664 groups of 4).
+constexpr int kNormThreads = 256;
+constexpr int kNormGroups = kModelDim / 4;
+constexpr int kNormPer = (kNormGroups + kNormThreads - 1) / kNormThreads;   // 7
+
+__global__ __launch_bounds__(kNormThreads) void out_proj_norm_kernel(OutProjArgs a) {
+    __shared__ float red[kNormThreads / 64];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const float* prow = a.proj + (int64_t)t * kModelDim;
+    floatx4 x[kNormPer];
+    float ss = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kNormPer; ++u) {
+        const int gidx = tid + kNormThreads * u;
+        x[u] = gidx < kNormGroups ? *(const floatx4*)(prow + 4 * gidx) : floatx4{};
+        ss += x[u][0] * x[u][0] + x[u][1] * x[u][1] + x[u][2] * x[u][2] + x[u][3] * x[u][3];
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    float tot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kNormThreads / 64; ++w) tot += red[w];
+    const float inv = 1.0f / sqrtf(tot * (1.0f / kModelDim) + a.eps);
+    const bf16_t* res = (const bf16_t*)a.residual + (int64_t)t * kModelDim;
+    bf16_t* out = (bf16_t*)a.out + (int64_t)t * kModelDim;
+#pragma unroll
+    for (int u = 0; u < kNormPer; ++u) {
+        const int gidx = tid + kNormThreads * u;
+        if (gidx >= kNormGroups) break;
+        const floatx4 g = *(const floatx4*)(a.gamma + 4 * gidx);
+        const uint2 rr = *(const uint2*)(res + 4 * gidx);
+        const float r4[4] = {__uint_as_float(rr.x << 16), __uint_as_float(rr.x & 0xffff0000u),
+                             __uint_as_float(rr.y << 16), __uint_as_float(rr.y & 0xffff0000u)};
+        unsigned packed[2];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const unsigned u16 = __builtin_bit_cast(unsigned short, from_f32<bf16_t>(x[u][c] * inv * g[c] + r4[c]));
+            if (c & 1) packed[c / 2] |= u16 << 16;
+            else packed[c / 2] = u16;
+        }
+        *(uint2*)(out + 4 * gidx) = make_uint2(packed[0], packed[1]);
+    }
+}
+
+hipError_t launch_out_proj_gemm(const OutProjArgs& a, hipStream_t stream) {
+    const int64_t mblk = (a.m + kOpBM - 1) / kOpBM;
+    hipLaunchKernelGGL(out_proj_gemm_kernel, dim3((unsigned)(mblk * (kModelDim / kOpBN))), dim3(kOpThreads), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_out_proj_norm(const OutProjArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(out_proj_norm_kernel, dim3((unsigned)a.m), dim3(kNormThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace muse

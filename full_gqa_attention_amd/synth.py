@@ -28,7 +28,8 @@ import numpy as np
 import torch
 
 SEED = 1234
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "gate": 3, "cache_k": 4, "cache_v": 5}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "gate": 3, "cache_k": 4, "cache_v": 5,
+              "attn": 6, "o_proj_w": 7, "post_gain": 8, "residual": 9}
 
 N_HEADS, N_KV_HEADS, HEAD_DIM = 32, 2, 128
 ATTN_DIM = N_HEADS * HEAD_DIM
@@ -197,3 +198,29 @@ def to_storage_numpy(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.float32:
         return t.numpy()
     raise TypeError(f"unsupported storage dtype {t.dtype}")
+
+
+# ------------------------------------------------ the block's tail (o_proj + post-norm)
+
+MODEL_DIM = 6656
+
+
+@dataclass
+class OutProjInputs:
+    attn: torch.Tensor       # bf16 [M, 4096]: stands for the gated attention output
+    w: torch.Tensor          # bf16 [6656, 4096]: o_proj, N(0, 1/4096) so proj keeps attn's scale
+    gamma: torch.Tensor      # f32 [6656]: 1 + 0.1 N(0, 1) (the norm's gain, an offset from one)
+    residual: torch.Tensor   # bf16 [M, 6656]
+
+
+def out_proj_inputs(n_tokens: int, *, config: int, layer: int = 0, step: int = 0, device="cpu",
+                    backend: str = "numpy") -> OutProjInputs:
+    """Seeded synthetic weights and activations for the block's tail (no
+    trained weights exist here)."""
+    kw = dict(config=config, layer=layer, step=step, device=device, backend=backend)
+    attn = normal((n_tokens, ATTN_DIM), tensor="attn", **kw)
+    w = (normal((MODEL_DIM, ATTN_DIM), tensor="o_proj_w", dtype=F32, **kw) * (1.0 / 64.0)).to(torch.bfloat16)
+    gamma = 1.0 + 0.1 * normal((MODEL_DIM,), tensor="post_gain", dtype=F32, **kw)
+    residual = normal((n_tokens, MODEL_DIM), tensor="residual", **kw)
+    return OutProjInputs(attn, w, gamma.to(torch.float32), residual)
+

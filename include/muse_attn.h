@@ -249,6 +249,54 @@ muse_status muse_rope_theta_table(float theta, float* out_host64);
 /* Static string naming a status code (never NULL). */
 const char* muse_status_str(muse_status status);
 
+/* ------------------------------------------------ the block's tail (next step)
+ *
+ * o_proj and the post-attention norm, with the residual add ("Chapter 9 - The
+ * Muse Glimmer architecture" 9.8 and 9.9, Figure 9.1): the gated attention
+ * output (4,096 channels, heads concatenated, as muse_attn_* write it) is
+ * projected to the model width 6,656, the projection of each token is RMS
+ * normalised with its own epsilon (1e-8 in the model, unlike the other norms'
+ * 1e-5) and scaled by the norm's gain, and the result is added to the
+ * residual stream:
+ *
+ *   proj[t][n]   = sum_k attn[t][k] * w[n][k]
+ *   hidden[t][n] = proj[t][n] / sqrt(mean_n proj[t][n]^2 + eps) * gamma[n]
+ *                  + residual[t][n]
+ *
+ * Arguments (every pointer a DEVICE pointer, 16-byte aligned):
+ *   n_tokens    rows of attn / residual / hidden (0 enqueues nothing)
+ *   attn        bf16 [n_tokens][4096]
+ *   w           bf16 [6656][4096]: row n holds output channel n's weights
+ *   gamma       f32 [6656]: the norm's effective gain ("How Muse Glimmer Fits
+ *               an Agent on Your Device" stores it as an offset from one; the
+ *               caller passes 1 + offset)
+ *   residual    bf16 [n_tokens][6656]
+ *   hidden_out  bf16 [n_tokens][6656]; may be residual itself (an in-place
+ *               update of the stream), must not otherwise overlap an input
+ *   eps         > 0 and finite
+ *   workspace   muse_out_proj_workspace_size(n_tokens) bytes or more: the f32
+ *               projection; contents on entry are ignored
+ *   timer       optional: brackets the projection (GEMM) kernel
+ * The projection accumulates in f32 from the bf16 operands; the norm reads
+ * the f32 projection; hidden is rounded to nearest even into bf16.
+ * Fails closed, before anything is enqueued: NULL pointer MUSE_ERR_NULL;
+ * n_tokens < 0 or above 2^24 MUSE_ERR_SHAPE; eps not positive and finite
+ * MUSE_ERR_LAYER; a misaligned pointer MUSE_ERR_ALIGN; hidden_out partly
+ * overlapping residual, or overlapping attn, w, gamma or the workspace, or
+ * the workspace overlapping an input MUSE_ERR_ALIAS; workspace too small
+ * MUSE_ERR_WORKSPACE; a failed launch MUSE_ERR_HIP.  Asynchronous on stream.
+ */
+#define MUSE_ATTN_DIM 4096
+#define MUSE_MODEL_DIM 6656
+muse_status muse_out_proj(int32_t n_tokens, const void* attn, const void* w, const float* gamma,
+                          const void* residual, void* hidden_out, float eps,
+                          void* workspace, size_t workspace_bytes,
+                          hipStream_t stream, const muse_kernel_timer* timer);
+
+/* Workspace bytes muse_out_proj needs for n_tokens rows (n_tokens * 6656 * 4,
+ * rounded up); MUSE_ERR_SHAPE for n_tokens outside [0, 2^24]. */
+muse_status muse_out_proj_workspace_size(int32_t n_tokens, size_t* bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -285,3 +285,50 @@ def test_workspace_sizes():
     assert fa.workspace_size(sl, 16, 1, 131072, True) == fa.workspace_size(sl, 16, 1, 4096, True)
     with pytest.raises(fa.MuseError):
         fa.workspace_size(lay, -1, 1, 10, True)
+
+
+# ---------------------------------------------- the block's tail: muse_out_proj
+
+def _op_call(lib, n=4, attn=0x10000, w=0x20000000, gamma=0x40000000, res=0x50000000, out=0x60000000,
+             eps=1e-8, ws=0x70000000, ws_bytes=None):
+    """Fake 16-byte-aligned device addresses, far apart: every check runs on
+    the host before anything is enqueued, so no pointer is dereferenced."""
+    vp = ctypes.c_void_p
+    if ws_bytes is None:
+        ws_bytes = fa.out_proj_workspace_size(n) if 0 <= n <= (1 << 24) else 0
+    return lib.muse_out_proj(n, vp(attn) if attn else None, vp(w) if w else None, vp(gamma) if gamma else None,
+                             vp(res) if res else None, vp(out) if out else None, ctypes.c_float(eps),
+                             vp(ws) if ws else None, ws_bytes, None, None)
+
+
+def test_out_proj_workspace_size():
+    assert fa.out_proj_workspace_size(0) == 0
+    assert fa.out_proj_workspace_size(64) == 64 * 6656 * 4
+    assert fa.out_proj_workspace_size(65536) == 65536 * 6656 * 4
+    with pytest.raises(fa.MuseError):
+        fa.out_proj_workspace_size(-1)
+    with pytest.raises(fa.MuseError):
+        fa.out_proj_workspace_size((1 << 24) + 1)
+
+
+@pytest.mark.parametrize("kw, code", [
+    ({"attn": 0}, 1), ({"w": 0}, 1), ({"gamma": 0}, 1), ({"res": 0}, 1), ({"out": 0}, 1), ({"ws": 0}, 1),
+    ({"n": -1}, 2), ({"n": (1 << 24) + 1}, 2),
+    ({"eps": 0.0}, 3), ({"eps": -1e-8}, 3), ({"eps": float("inf")}, 3), ({"eps": float("nan")}, 3),
+    ({"attn": 0x10008}, 8), ({"w": 0x20000004}, 8), ({"gamma": 0x40000002}, 8), ({"out": 0x60000008}, 8),
+    ({"ws": 0x70000001}, 8),
+    ({"ws_bytes": 4 * 6656 * 4 - 1}, 5),
+    ({"out": 0x50000000 + 16}, 9),                  # partly over the residual
+    ({"out": 0x10000}, 9),                          # over attn
+    ({"ws": 0x20000000 + 4096}, 9),                 # workspace over w
+    ({"ws": 0x60000000}, 9),                        # workspace over out
+])
+def test_out_proj_fails_closed(lib, kw, code):
+    assert _op_call(lib, **kw) == code
+
+
+def test_out_proj_in_place_residual_and_empty(lib):
+    assert _op_call(lib, n=0) == OK                 # nothing enqueued
+    # out == residual is the in-place stream update (validated, then nothing
+    # enqueued for n == 0; with n > 0 the launch needs a GPU)
+    assert _op_call(lib, n=0, out=0x50000000) == OK

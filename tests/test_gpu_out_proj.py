@@ -1,0 +1,67 @@
+"""The block's tail on the GPU (muse_out_proj: o_proj 4096 -> 6656, the
+post-attention RMSNorm with epsilon 1e-8, the residual add; "Chapter 9 - The
+Muse Glimmer architecture" 9.8, 9.9 and Figure 9.1) against the oracle, on
+seeded synthetic weights.
+
+Tolerance: the bf16 bound, |gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise (the
+GPU accumulates the bf16 products in f32 and rounds the output to bf16; the
+oracle is double throughout).  Token counts cover one row, a full 256-row tile,
+a ragged tile edge, and a prefill-sized batch checked on sampled rows (rows
+are independent, so a sample is exact for its rows).
+"""
+import numpy as np
+import pytest
+import torch
+
+import full_gqa_attention_amd as fa
+import oracle
+from full_gqa_attention_amd import synth
+from parity import assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def run_case(M, rows=None, config=70, in_place=False):
+    inp = synth.out_proj_inputs(M, config=config, device=DEV, backend="numpy" if M <= 4096 else "torch")
+    res_before = inp.residual.clone()
+    if in_place:
+        out = fa.out_proj(inp.attn, inp.w, inp.gamma, inp.residual, out=inp.residual)
+    else:
+        out = fa.out_proj(inp.attn, inp.w, inp.gamma, inp.residual)
+    torch.cuda.synchronize()
+    if rows is None:
+        rows = np.arange(M)
+    ref = oracle.out_proj_rows(bits(inp.attn), bits(inp.w), inp.gamma.cpu().numpy(), bits(res_before), rows=rows)
+    got = out[torch.as_tensor(rows, device=DEV).long()].double().cpu().numpy()
+    return assert_close(got, ref, synth.BF16, f"out_proj M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 64, 256, 257])
+def test_out_proj_all_rows(M):
+    run_case(M)
+
+
+def test_out_proj_prefill_sized_sampled_rows():
+    """8 x 8,192 tokens (the prefill workload's batch) on sampled rows,
+    including both ends of every 256-row tile edge near the sample."""
+    M = 65536
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 257, 4095, 4096, 32767, 65279, 65280, 65535],
+                                     np.random.default_rng(3).integers(0, M, 21)]))
+    run_case(M, rows=rows, config=71)
+
+
+def test_out_proj_in_place_residual():
+    run_case(300, in_place=True, config=72)
+
+
+def test_out_proj_deterministic():
+    inp = synth.out_proj_inputs(513, config=73, device=DEV)
+    a = fa.out_proj(inp.attn, inp.w, inp.gamma, inp.residual).clone()
+    b = fa.out_proj(inp.attn, inp.w, inp.gamma, inp.residual)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
