@@ -558,7 +558,9 @@ muse_status muse_rope_theta_table(float theta, float* out_host64) {
 muse_status muse_out_proj_workspace_size(int32_t n_tokens, size_t* bytes) {
     if (!bytes) return MUSE_ERR_NULL;
     if (n_tokens < 0 || n_tokens > kMaxPositions) return MUSE_ERR_SHAPE;
-    *bytes = round_up((size_t)n_tokens * muse::kModelDim * sizeof(float), kAlign);
+    // the f32 projection; a few tokens (at most 64) keep its 8 K slices apart
+    const size_t parts = n_tokens <= 64 ? 8 : 1;
+    *bytes = round_up(parts * (size_t)n_tokens * muse::kModelDim * sizeof(float), kAlign);
     return MUSE_OK;
 }
 

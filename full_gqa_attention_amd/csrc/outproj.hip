@@ -129,22 +129,93 @@ void out_proj_gemm_kernel(OutProjArgs a) {
         }
 }
 
-// ---- post-attention RMSNorm + residual: one token row per workgroup, 256
-// threads, 4 channels per thread and step (6,656 = 1,664 groups of 4).
-constexpr int kNormThreads = 256;
-constexpr int kNormGroups = kModelDim / 4;
-constexpr int kNormPer = (kNormGroups + kNormThreads - 1) / kNormThreads;   // 7
+// ---- GEMM for a few tokens (a decode step: at most 64).  Reading W's 54.5
+// MB is the whole cost, and every CU must stream part of it, so the work is
+// split into 8 slices of K (512 each) x 26 blocks of 256 channels: 208
+// workgroups.  A workgroup stages its slice of attn (all tokens x 512, 64 KB)
+// in LDS once, with whole-row loads, and each of its 8 waves streams W for 32
+// channels of that slice straight from global memory into the MFMA layout
+// (lane (l32, gl): 16 bytes of W row n + l32 at k + 8 gl).  A workgroup writes
+// its slice's partial product; the norm kernel adds the 8 slices in slice
+// order (the sum does not depend on timing).
+constexpr int kSkinnyMaxM = 64;
+constexpr int kSkinnySlices = 8, kSkinnyK = kAttnDim / kSkinnySlices;   // 512
+constexpr int kSkinnyNB = 256;                          // channels per workgroup (8 waves x 32)
+constexpr int kSkinnyLds = kSkinnyK + 8;                // 1,040-byte rows: b128 reads conflict-free
+constexpr int kSkinnyAhead = 8;                         // k16 steps of W loads in flight per wave
+static_assert(kModelDim % kSkinnyNB == 0 && (kSkinnyK / 16) % kSkinnyAhead == 0, "skinny tiling");
 
-__global__ __launch_bounds__(kNormThreads) void out_proj_norm_kernel(OutProjArgs a) {
-    __shared__ float red[kNormThreads / 64];
+template <int MT>
+__global__ __launch_bounds__(512) void out_proj_skinny_kernel(OutProjArgs a) {
+    using MP = Mma32<bf16_t>;
+    __shared__ __attribute__((aligned(16))) bf16_t As[32 * MT * kSkinnyLds];
+    const int ks = blockIdx.x % kSkinnySlices, nb = blockIdx.x / kSkinnySlices;
+    const int k0 = ks * kSkinnyK;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, gl = lane >> 5;
+    const int M = a.m;
+    // attn rows (32 MT of them, rows past M repeat the last) x this slice: 64
+    // threads per 1 KB row
+    for (int c = tid; c < 32 * MT * (kSkinnyK / 8); c += 512) {
+        const int r = c / (kSkinnyK / 8), p = c % (kSkinnyK / 8);
+        *(u32x4*)(As + r * kSkinnyLds + 8 * p) =
+            *(const u32x4*)((const bf16_t*)a.attn + (int64_t)min(r, M - 1) * kAttnDim + k0 + 8 * p);
+    }
+    const int n = nb * kSkinnyNB + 32 * wave;           // this wave's 32 channels
+    const bf16_t* wrow = (const bf16_t*)a.w + (int64_t)(n + l32) * kAttnDim + k0 + 8 * gl;
+    __syncthreads();
+    floatx16 acc[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[i] = floatx16{};
+    for (int kb = 0; kb < kSkinnyK; kb += 16 * kSkinnyAhead) {
+        bf16x8 bw[kSkinnyAhead];
+#pragma unroll
+        for (int s = 0; s < kSkinnyAhead; ++s) bw[s] = *(const bf16x8*)(wrow + kb + 16 * s);
+#pragma unroll
+        for (int s = 0; s < kSkinnyAhead; ++s)
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const bf16x8 af = *(const bf16x8*)(As + (32 * i + l32) * kSkinnyLds + kb + 16 * s + 8 * gl);
+                acc[i] = MP::mma(af, bw[s], acc[i]);
+            }
+    }
+    // partial of slice ks: rows 32 i + 8 (e / 4) + 4 gl + e % 4, channel n + l32
+    float* part = a.proj + (int64_t)ks * M * kModelDim;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int m = 32 * i + 8 * (e / 4) + 4 * gl + (e % 4);
+            if (m < M) part[(int64_t)m * kModelDim + n + l32] = acc[i][e];
+        }
+}
+
+// ---- post-attention RMSNorm + residual: one token row per workgroup, 4
+// channels per thread and step (6,656 = 1,664 groups of 4).  NPARTS K slices
+// of the projection (a few tokens) are added in slice order, all their loads
+// in flight together; those rows get 1,024 threads so that the loads of a
+// thread stay few.
+constexpr int kNormGroups = kModelDim / 4;
+
+template <int NPARTS, int THREADS>
+__global__ __launch_bounds__(THREADS) void out_proj_norm_kernel(OutProjArgs a) {
+    constexpr int PER = (kNormGroups + THREADS - 1) / THREADS;
+    __shared__ float red[THREADS / 64];
     const int t = blockIdx.x, tid = threadIdx.x;
     const float* prow = a.proj + (int64_t)t * kModelDim;
-    floatx4 x[kNormPer];
+    const int64_t pstride = (int64_t)a.m * kModelDim;  // between K slices
+    floatx4 x[PER];
     float ss = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kNormPer; ++u) {
-        const int gidx = tid + kNormThreads * u;
-        x[u] = gidx < kNormGroups ? *(const floatx4*)(prow + 4 * gidx) : floatx4{};
+    for (int u = 0; u < PER; ++u) {
+        const int gidx = min(tid + THREADS * u, kNormGroups - 1);
+        floatx4 part[NPARTS];
+#pragma unroll
+        for (int q = 0; q < NPARTS; ++q) part[q] = *(const floatx4*)(prow + q * pstride + 4 * gidx);
+        x[u] = part[0];
+#pragma unroll
+        for (int q = 1; q < NPARTS; ++q) x[u] += part[q];
+        if (tid + THREADS * u >= kNormGroups) x[u] = floatx4{};
         ss += x[u][0] * x[u][0] + x[u][1] * x[u][1] + x[u][2] * x[u][2] + x[u][3] * x[u][3];
     }
     ss = wave_sum(ss);
@@ -152,13 +223,13 @@ __global__ __launch_bounds__(kNormThreads) void out_proj_norm_kernel(OutProjArgs
     __syncthreads();
     float tot = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kNormThreads / 64; ++w) tot += red[w];
+    for (int w = 0; w < THREADS / 64; ++w) tot += red[w];
     const float inv = 1.0f / sqrtf(tot * (1.0f / kModelDim) + a.eps);
     const bf16_t* res = (const bf16_t*)a.residual + (int64_t)t * kModelDim;
     bf16_t* out = (bf16_t*)a.out + (int64_t)t * kModelDim;
 #pragma unroll
-    for (int u = 0; u < kNormPer; ++u) {
-        const int gidx = tid + kNormThreads * u;
+    for (int u = 0; u < PER; ++u) {
+        const int gidx = tid + THREADS * u;
         if (gidx >= kNormGroups) break;
         const floatx4 g = *(const floatx4*)(a.gamma + 4 * gidx);
         const uint2 rr = *(const uint2*)(res + 4 * gidx);
@@ -176,6 +247,15 @@ __global__ __launch_bounds__(kNormThreads) void out_proj_norm_kernel(OutProjArgs
 }
 
 hipError_t launch_out_proj_gemm(const OutProjArgs& a, hipStream_t stream) {
+    const dim3 sgrid(kSkinnySlices * (kModelDim / kSkinnyNB)), sblock(512);
+    if (a.m <= 32) {
+        hipLaunchKernelGGL(out_proj_skinny_kernel<1>, sgrid, sblock, 0, stream, a);
+        return hipGetLastError();
+    }
+    if (a.m <= kSkinnyMaxM) {
+        hipLaunchKernelGGL(out_proj_skinny_kernel<2>, sgrid, sblock, 0, stream, a);
+        return hipGetLastError();
+    }
     const int64_t mblk = (a.m + kOpBM - 1) / kOpBM;
     hipLaunchKernelGGL(out_proj_gemm_kernel, dim3((unsigned)(mblk * (kModelDim / kOpBN))), dim3(kOpThreads), 0,
                        stream, a);
@@ -183,7 +263,10 @@ hipError_t launch_out_proj_gemm(const OutProjArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_out_proj_norm(const OutProjArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(out_proj_norm_kernel, dim3((unsigned)a.m), dim3(kNormThreads), 0, stream, a);
+    if (a.m <= kSkinnyMaxM)
+        hipLaunchKernelGGL((out_proj_norm_kernel<kSkinnySlices, 1024>), dim3((unsigned)a.m), dim3(1024), 0, stream, a);
+    else
+        hipLaunchKernelGGL((out_proj_norm_kernel<1, 256>), dim3((unsigned)a.m), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -293,8 +293,10 @@ muse_status muse_out_proj(int32_t n_tokens, const void* attn, const void* w, con
                           void* workspace, size_t workspace_bytes,
                           hipStream_t stream, const muse_kernel_timer* timer);
 
-/* Workspace bytes muse_out_proj needs for n_tokens rows (n_tokens * 6656 * 4,
- * rounded up); MUSE_ERR_SHAPE for n_tokens outside [0, 2^24]. */
+/* Workspace bytes muse_out_proj needs for n_tokens rows: n_tokens * 6656 * 4
+ * (the f32 projection), 8 times that for n_tokens <= 64 (its K slices, added
+ * by the norm kernel), rounded up; MUSE_ERR_SHAPE for n_tokens outside
+ * [0, 2^24]. */
 muse_status muse_out_proj_workspace_size(int32_t n_tokens, size_t* bytes);
 
 #ifdef __cplusplus

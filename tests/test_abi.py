@@ -303,7 +303,8 @@ def _op_call(lib, n=4, attn=0x10000, w=0x20000000, gamma=0x40000000, res=0x50000
 
 def test_out_proj_workspace_size():
     assert fa.out_proj_workspace_size(0) == 0
-    assert fa.out_proj_workspace_size(64) == 64 * 6656 * 4
+    assert fa.out_proj_workspace_size(64) == 8 * 64 * 6656 * 4
+    assert fa.out_proj_workspace_size(65) == 65 * 6656 * 4
     assert fa.out_proj_workspace_size(65536) == 65536 * 6656 * 4
     with pytest.raises(fa.MuseError):
         fa.out_proj_workspace_size(-1)

@@ -5,9 +5,10 @@ seeded synthetic weights.
 
 Tolerance: the bf16 bound, |gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise (the
 GPU accumulates the bf16 products in f32 and rounds the output to bf16; the
-oracle is double throughout).  Token counts cover one row, a full 256-row tile,
-a ragged tile edge, and a prefill-sized batch checked on sampled rows (rows
-are independent, so a sample is exact for its rows).
+oracle is double throughout).  Token counts cover the few-token kernel (1 to
+64 rows: one or two 32-row tiles, full and ragged), the tiled kernel (65, a
+full 256-row tile, a ragged tile edge), and a prefill-sized batch checked on
+sampled rows (rows are independent, so a sample is exact for its rows).
 """
 import numpy as np
 import pytest
@@ -41,7 +42,7 @@ def run_case(M, rows=None, config=70, in_place=False):
     return assert_close(got, ref, synth.BF16, f"out_proj M={M}")
 
 
-@pytest.mark.parametrize("M", [1, 64, 256, 257])
+@pytest.mark.parametrize("M", [1, 4, 32, 33, 64, 65, 256, 257])
 def test_out_proj_all_rows(M):
     run_case(M)
 
