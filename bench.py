@@ -245,6 +245,8 @@ def parse():
                     help="sliding layers keep their window in a ring cache (kv_ring) in the decode and schedule runs")
     ap.add_argument("--verify", action="store_true",
                     help="also time the 16-token verify call (64 x 8,192 cached rows, both layers)")
+    ap.add_argument("--out-proj", action="store_true",
+                    help="also time the block's tail (o_proj + post-attention norm) at 65,536 and 64 tokens")
     ap.add_argument("--relocate", action="store_true",
                     help="also time NoPE tile relocation (muse_kv_relocate) of a 64 x 8,192 full-layer cache")
     ap.add_argument("--eager", action="store_true",
@@ -554,6 +556,50 @@ def bench_verify(fa, synth, torch, steps=20, warmup=3, n_new=16):
             "steps": steps, "warmup": warmup}
 
 
+def bench_out_proj(fa, synth, torch, steps=10, warmup=3):
+    """The block's tail after attention (muse_out_proj: o_proj 4096 -> 6656,
+    post-attention RMSNorm eps 1e-8, residual add; "Chapter 9 - The Muse
+    Glimmer architecture" 9.8, 9.9) on seeded synthetic weights, at the token
+    counts of the two headline workloads: 65,536 (the 8 x 8,192 prefill
+    batch; the GEMM is MFMA-bound, 2 * 4096 * 6656 flop per token) and 64
+    (one decode step of 64 sequences; reading W's 54.5 MB bounds it).  The
+    kernel timer brackets the GEMM; the call adds the norm pass."""
+    from full_gqa_attention_amd.timing import KernelTimers
+    res = {}
+    for M in (65536, 64):
+        inp = synth.out_proj_inputs(M, config=80, device="cuda", backend="torch")
+        ws = torch.empty(max(fa.out_proj_workspace_size(M), 16), dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(inp.residual)
+        for _ in range(warmup):
+            fa.out_proj(inp.attn, inp.w, inp.gamma, inp.residual, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        timers = KernelTimers(steps)
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fa.out_proj(inp.attn, inp.w, inp.gamma, inp.residual, out=out, workspace=ws, timer=timers[i])
+        torch.cuda.synchronize()
+        call = (time.perf_counter() - t0) / steps
+        g = [timers.elapsed_ms(i) for i in range(steps)]
+        timers.close()
+        gemm = sorted(g)[len(g) // 2] * 1e-3
+        flop = 2.0 * M * 4096 * 6656
+        wbytes = 6656 * 4096 * 2 + M * 4096 * 2              # W and attn, read once
+        r = {"tokens": M, "call_us": round(call * 1e6, 1), "gemm_us": round(gemm * 1e6, 1),
+             "gemm_TFLOPs": round(flop / gemm / 1e12, 1), "gemm_GBps_W_and_attn": round(wbytes / gemm / 1e9, 1)}
+        if M >= 4096:
+            r["roofline"] = {"bound": "mfma", "achieved": r["gemm_TFLOPs"], "peak": MFMA_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(r["gemm_TFLOPs"] / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                             "kernel": "muse::out_proj_gemm_kernel (bf16)"}
+        else:
+            r["roofline"] = {"bound": "hbm", "achieved": r["gemm_GBps_W_and_attn"], "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(r["gemm_GBps_W_and_attn"] / HBM_PEAK_GBS, 4),
+                             "traffic": None, "kernel": "muse::out_proj_skinny_kernel<2> (bf16)"}
+        res[f"tokens_{M}"] = r
+        del inp, ws, out
+        torch.cuda.empty_cache()
+    return res
+
+
 def bench_relocate(fa, synth, torch, steps=10):
     """NoPE tile relocation ("Chapter 14 - QK-norm and RoPE" 14.6): the whole
     cache of a full layer of the 64 x 8,192 decode workload, moved as 512-row
@@ -686,6 +732,9 @@ def main():
     if args.verify:
         torch.cuda.empty_cache()
         line["verify"] = bench_verify(fa, synth, torch)
+    if args.out_proj:
+        torch.cuda.empty_cache()
+        line["out_proj"] = bench_out_proj(fa, synth, torch)
     if args.relocate:
         torch.cuda.empty_cache()
         line["relocate"] = bench_relocate(fa, synth, torch)
