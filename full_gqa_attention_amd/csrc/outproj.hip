@@ -15,12 +15,25 @@
 
 namespace muse {
 
-// ---- GEMM: a workgroup computes a 256 x 128 tile of proj with 8 waves (4
-// along the tokens x 2 along the channels, 64 x 64 each: 2 x 2 MFMA tiles).
+// ---- GEMM: a workgroup computes a kOpBM x kOpBN tile of proj with 8 waves
+// (kOpWM along the tokens x kOpWN along the channels, each 32 kOpTM x 32 kOpTN:
+// kOpTM x kOpTN MFMA tiles).  256 x 256 tiles of 64 x 128 per wave (4 x 2
+// waves) measured 15% faster than 256 x 128 tiles of 64 x 64: each operand
+// read from LDS feeds more MFMAs.
 // K advances 64 at a time through two LDS buffers; global loads run two
 // k-steps ahead in alternating register sets.  Both operands are K-contiguous
 // (attn rows and W rows), so every MFMA operand is one 16-byte LDS read.
-constexpr int kOpBM = 256, kOpBN = 128, kOpBK = 64;
+#ifndef MUSE_OP_TM
+#define MUSE_OP_TM 2
+#endif
+#ifndef MUSE_OP_TN
+#define MUSE_OP_TN 4
+#endif
+#ifndef MUSE_OP_WM
+#define MUSE_OP_WM 4
+#endif
+constexpr int kOpTM = MUSE_OP_TM, kOpTN = MUSE_OP_TN, kOpWM = MUSE_OP_WM, kOpWN = 8 / kOpWM;
+constexpr int kOpBM = 32 * kOpTM * kOpWM, kOpBN = 32 * kOpTN * kOpWN, kOpBK = 64;
 constexpr int kOpLds = kOpBK + 8;                      // 144-byte rows: b128 reads conflict-free
 constexpr int kOpThreads = 512;
 constexpr int kOpAChunks = kOpBM * kOpBK * 2 / 16 / kOpThreads;   // 16-byte chunks per thread (4)
@@ -40,7 +53,7 @@ void out_proj_gemm_kernel(OutProjArgs a) {
     const int M = a.m;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, gl = lane >> 5;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / kOpWN, wn = wave % kOpWN;
 
     // staging: chunk c = tid + 512 u is row c / 8, 16-byte piece c % 8 of a 64-wide k slice
     const bf16_t* A = (const bf16_t*)a.attn;
@@ -72,27 +85,27 @@ void out_proj_gemm_kernel(OutProjArgs a) {
         }
     };
 
-    floatx16 acc[2][2];
+    floatx16 acc[kOpTM][kOpTN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kOpTM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
+        for (int j = 0; j < kOpTN; ++j) acc[i][j] = floatx16{};
     // C[m][n] += A[m][k] W[n][k]: lane (l32, gl) gives A row l32 and W row l32
     // (the B column), k = 8 gl .. 8 gl + 7 of each 16-wide step
     auto compute = [&](int buf) __attribute__((always_inline)) {
-        const bf16_t* Ab = As[buf] + (64 * wm + l32) * kOpLds + 8 * gl;
-        const bf16_t* Bb = Bs[buf] + (64 * wn + l32) * kOpLds + 8 * gl;
+        const bf16_t* Ab = As[buf] + (32 * kOpTM * wm + l32) * kOpLds + 8 * gl;
+        const bf16_t* Bb = Bs[buf] + (32 * kOpTN * wn + l32) * kOpLds + 8 * gl;
 #pragma unroll
         for (int kk = 0; kk < kOpBK / 16; ++kk) {
-            bf16x8 af[2], bfr[2];
+            bf16x8 af[kOpTM], bfr[kOpTN];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) af[i] = *(const bf16x8*)(Ab + 32 * i * kOpLds + 16 * kk);
+            for (int i = 0; i < kOpTM; ++i) af[i] = *(const bf16x8*)(Ab + 32 * i * kOpLds + 16 * kk);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) bfr[j] = *(const bf16x8*)(Bb + 32 * j * kOpLds + 16 * kk);
+            for (int j = 0; j < kOpTN; ++j) bfr[j] = *(const bf16x8*)(Bb + 32 * j * kOpLds + 16 * kk);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < kOpTM; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = MP::mma(af[i], bfr[j], acc[i][j]);
+                for (int j = 0; j < kOpTN; ++j) acc[i][j] = MP::mma(af[i], bfr[j], acc[i][j]);
         }
     };
 
@@ -116,16 +129,16 @@ void out_proj_gemm_kernel(OutProjArgs a) {
         step(ks + 1, ra0, rb0, ra1, rb1);
     }
 
-    // ---- proj rows m0 + 64 wm + 32 i + 8 (e / 4) + 4 gl + e % 4, channel
-    // n0 + 64 wn + 32 j + l32: 32 lanes store 128 contiguous bytes per item
+    // ---- proj rows m0 + 32 (kOpTM wm + i) + 8 (e / 4) + 4 gl + e % 4, channel
+    // n0 + 32 (kOpTN wn + j) + l32: 32 lanes store 128 contiguous bytes per item
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kOpTM; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int m = m0 + 64 * wm + 32 * i + 8 * (e / 4) + 4 * gl + (e % 4);
+            const int m = m0 + 32 * (kOpTM * wm + i) + 8 * (e / 4) + 4 * gl + (e % 4);
             if (m >= M) continue;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) a.proj[(int64_t)m * N + n0 + 64 * wn + 32 * j + l32] = acc[i][j][e];
+            for (int j = 0; j < kOpTN; ++j) a.proj[(int64_t)m * N + n0 + 32 * (kOpTN * wn + j) + l32] = acc[i][j][e];
         }
 }
 
