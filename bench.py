@@ -593,7 +593,8 @@ def bench_out_proj(fa, synth, torch, steps=10, warmup=3):
         else:
             r["roofline"] = {"bound": "hbm", "achieved": r["gemm_GBps_W_and_attn"], "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": round(r["gemm_GBps_W_and_attn"] / HBM_PEAK_GBS, 4),
-                             "traffic": None, "kernel": "muse::out_proj_skinny_kernel<2> (bf16)"}
+                             "traffic": None,
+                             "kernel": f"muse::out_proj_skinny_kernel<{(M + 15) // 16}> (bf16)"}
         res[f"tokens_{M}"] = r
         del inp, ws, out
         torch.cuda.empty_cache()

@@ -143,64 +143,100 @@ void out_proj_gemm_kernel(OutProjArgs a) {
 }
 
 // ---- GEMM for a few tokens (a decode step: at most 64).  Reading W's 54.5
-// MB is the whole cost, and every CU must stream part of it, so the work is
-// split into 8 slices of K (512 each) x 26 blocks of 256 channels: 208
-// workgroups.  A workgroup stages its slice of attn (all tokens x 512, 64 KB)
-// in LDS once, with whole-row loads, and each of its 8 waves streams W for 32
-// channels of that slice straight from global memory into the MFMA layout
-// (lane (l32, gl): 16 bytes of W row n + l32 at k + 8 gl).  A workgroup writes
-// its slice's partial product; the norm kernel adds the 8 slices in slice
-// order (the sum does not depend on timing).
+// MB is the whole cost, so every CU must stream an equal share with as much
+// of it in flight as it can hold.  The product is cut into 8 slices of K (512
+// each) x 32 blocks of 208 channels: 256 workgroups, one per CU, each reading
+// 208 KB of W.  A block is 13 groups of 16 channels; wave v takes groups v
+// and v + 8 (waves 5-7 only the first) and requests every W load of its
+// groups at once, straight into the layout of the 16 x 16 x 32 MFMA (lane
+// (l16, g4): 16 bytes of row n + l16 at k + 8 g4 of each 32-wide step).  The
+// attn slice (all tokens x 512; rows past the last token repeat it) is
+// requested before W and staged in LDS while W streams in.  A workgroup
+// writes its slice's partial product; the norm kernel adds the 8 slices in
+// slice order (the sum does not depend on timing).
 constexpr int kSkinnyMaxM = 64;
-constexpr int kSkinnySlices = 8, kSkinnyK = kAttnDim / kSkinnySlices;   // 512
-constexpr int kSkinnyNB = 256;                          // channels per workgroup (8 waves x 32)
+constexpr int kSkinnySlices = 8, kSkinnyK = kAttnDim / kSkinnySlices;    // 512
+constexpr int kSkinnyBlocks = 32, kSkinnyCh = kModelDim / kSkinnyBlocks;  // 208 channels
+constexpr int kSkinnyGroups = kSkinnyCh / 16;                             // 13
 constexpr int kSkinnyLds = kSkinnyK + 8;                // 1,040-byte rows: b128 reads conflict-free
-constexpr int kSkinnyAhead = 8;                         // k16 steps of W loads in flight per wave
-static_assert(kModelDim % kSkinnyNB == 0 && (kSkinnyK / 16) % kSkinnyAhead == 0, "skinny tiling");
+static_assert(kSkinnyCh * kSkinnyBlocks == kModelDim && kSkinnyCh % 16 == 0 && kSkinnyGroups > 8 &&
+                  kSkinnyGroups <= 16,
+              "skinny tiling");
+
+// MT tiles of 16 tokens x NG groups of 16 channels (the wave's first group,
+// and the one 8 groups on) x one K slice.
+template <int MT, int NG>
+__device__ __forceinline__ void skinny_wave(const OutProjArgs& a, bf16_t* As, int ks, int blk, int wave, int lane) {
+    using MP = Mma16Wide<bf16_t>;
+    constexpr int KS = kSkinnyK / 32;                   // 32-wide k steps
+    constexpr int CPR = kSkinnyK / 8;                   // 16-byte chunks per attn row
+    constexpr int STAGE = 16 * MT * CPR / 512;          // chunks per thread
+    static_assert(16 * MT * CPR % 512 == 0, "staging split");
+    const int tid = 64 * wave + lane, l16 = lane & 15, g4 = lane >> 4;
+    const int k0 = ks * kSkinnyK, M = a.m;
+    const bf16_t* attn = (const bf16_t*)a.attn;
+    u32x4 st[STAGE];
+#pragma unroll
+    for (int s = 0; s < STAGE; ++s) {
+        const int c = tid + 512 * s, r = c / CPR, p = c % CPR;
+        st[s] = *(const u32x4*)(attn + (int64_t)min(r, M - 1) * kAttnDim + k0 + 8 * p);
+    }
+    __builtin_amdgcn_sched_barrier(0);                  // attn first: its wait leaves W in flight
+    const int n = blk * kSkinnyCh + 16 * wave;
+    const bf16_t* wp = (const bf16_t*)a.w + (int64_t)(n + l16) * kAttnDim + k0 + 8 * g4;
+    bf16x8 bw[KS][NG];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) bw[s][g] = *(const bf16x8*)(wp + (int64_t)g * 128 * kAttnDim + 32 * s);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < STAGE; ++s) {
+        const int c = tid + 512 * s, r = c / CPR, p = c % CPR;
+        *(u32x4*)(As + r * kSkinnyLds + 8 * p) = st[s];
+    }
+    __syncthreads();
+    floatx4 acc[NG][MT];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int i = 0; i < MT; ++i) acc[g][i] = floatx4{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            const bf16x8 af = *(const bf16x8*)(As + (16 * i + l16) * kSkinnyLds + 32 * s + 8 * g4);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) acc[g][i] = MP::mma(af, bw[s][g], acc[g][i]);
+        }
+    // partial of slice ks: token 16 i + 4 g4 + e, channel n + 128 g + l16
+    float* part = a.proj + (int64_t)ks * M * kModelDim + n + l16;
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = 16 * i + 4 * g4 + e;
+                if (m < M) part[(int64_t)m * kModelDim + 128 * g] = acc[g][i][e];
+            }
+}
 
 template <int MT>
 __global__ __launch_bounds__(512) void out_proj_skinny_kernel(OutProjArgs a) {
-    using MP = Mma32<bf16_t>;
-    __shared__ __attribute__((aligned(16))) bf16_t As[32 * MT * kSkinnyLds];
-    const int ks = blockIdx.x % kSkinnySlices, nb = blockIdx.x / kSkinnySlices;
-    const int k0 = ks * kSkinnyK;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, gl = lane >> 5;
-    const int M = a.m;
-    // attn rows (32 MT of them, rows past M repeat the last) x this slice: 64
-    // threads per 1 KB row
-    for (int c = tid; c < 32 * MT * (kSkinnyK / 8); c += 512) {
-        const int r = c / (kSkinnyK / 8), p = c % (kSkinnyK / 8);
-        *(u32x4*)(As + r * kSkinnyLds + 8 * p) =
-            *(const u32x4*)((const bf16_t*)a.attn + (int64_t)min(r, M - 1) * kAttnDim + k0 + 8 * p);
-    }
-    const int n = nb * kSkinnyNB + 32 * wave;           // this wave's 32 channels
-    const bf16_t* wrow = (const bf16_t*)a.w + (int64_t)(n + l32) * kAttnDim + k0 + 8 * gl;
-    __syncthreads();
-    floatx16 acc[MT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) acc[i] = floatx16{};
-    for (int kb = 0; kb < kSkinnyK; kb += 16 * kSkinnyAhead) {
-        bf16x8 bw[kSkinnyAhead];
-#pragma unroll
-        for (int s = 0; s < kSkinnyAhead; ++s) bw[s] = *(const bf16x8*)(wrow + kb + 16 * s);
-#pragma unroll
-        for (int s = 0; s < kSkinnyAhead; ++s)
-#pragma unroll
-            for (int i = 0; i < MT; ++i) {
-                const bf16x8 af = *(const bf16x8*)(As + (32 * i + l32) * kSkinnyLds + kb + 16 * s + 8 * gl);
-                acc[i] = MP::mma(af, bw[s], acc[i]);
-            }
-    }
-    // partial of slice ks: rows 32 i + 8 (e / 4) + 4 gl + e % 4, channel n + l32
-    float* part = a.proj + (int64_t)ks * M * kModelDim;
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int m = 32 * i + 8 * (e / 4) + 4 * gl + (e % 4);
-            if (m < M) part[(int64_t)m * kModelDim + n + l32] = acc[i][e];
-        }
+    __shared__ __attribute__((aligned(16))) bf16_t As[16 * MT * kSkinnyLds];
+    // blockIdx = 64 q + 8 r + x: slice r, block 8 q + x.  Consecutive
+    // workgroups go to the 8 XCDs in turn, so XCD x holds blocks x, x + 8, ...
+    // with all 8 slices of each: its L2 sees every part of W's rows, and a
+    // block's partials are written within one XCD.
+    static_assert(kSkinnySlices == 8 && kSkinnyBlocks == 32, "block mapping");
+    const int ks = (blockIdx.x >> 3) & 7, blk = ((blockIdx.x >> 6) << 3) | (blockIdx.x & 7);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // wave-uniform: each path reaches the workgroup barrier once
+    if (wave + 8 < kSkinnyGroups)
+        skinny_wave<MT, 2>(a, As, ks, blk, wave, lane);
+    else
+        skinny_wave<MT, 1>(a, As, ks, blk, wave, lane);
 }
 
 // ---- post-attention RMSNorm + residual: one token row per workgroup, 4
@@ -260,13 +296,14 @@ __global__ __launch_bounds__(THREADS) void out_proj_norm_kernel(OutProjArgs a) {
 }
 
 hipError_t launch_out_proj_gemm(const OutProjArgs& a, hipStream_t stream) {
-    const dim3 sgrid(kSkinnySlices * (kModelDim / kSkinnyNB)), sblock(512);
-    if (a.m <= 32) {
-        hipLaunchKernelGGL(out_proj_skinny_kernel<1>, sgrid, sblock, 0, stream, a);
-        return hipGetLastError();
-    }
     if (a.m <= kSkinnyMaxM) {
-        hipLaunchKernelGGL(out_proj_skinny_kernel<2>, sgrid, sblock, 0, stream, a);
+        const dim3 sgrid(kSkinnySlices * kSkinnyBlocks), sblock(512);
+        switch ((a.m + 15) / 16) {
+        case 1: hipLaunchKernelGGL(out_proj_skinny_kernel<1>, sgrid, sblock, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL(out_proj_skinny_kernel<2>, sgrid, sblock, 0, stream, a); break;
+        case 3: hipLaunchKernelGGL(out_proj_skinny_kernel<3>, sgrid, sblock, 0, stream, a); break;
+        default: hipLaunchKernelGGL(out_proj_skinny_kernel<4>, sgrid, sblock, 0, stream, a); break;
+        }
         return hipGetLastError();
     }
     const int64_t mblk = (a.m + kOpBM - 1) / kOpBM;
