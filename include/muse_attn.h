@@ -275,7 +275,8 @@ const char* muse_status_str(muse_status status);
  *               update of the stream), must not otherwise overlap an input
  *   eps         > 0 and finite
  *   workspace   muse_out_proj_workspace_size(n_tokens) bytes or more: the f32
- *               projection; contents on entry are ignored
+ *               projection; contents on entry are ignored; calls that overlap
+ *               in time must not share one
  *   timer       optional: brackets the projection (GEMM) kernel
  * The projection accumulates in f32 from the bf16 operands; the norm reads
  * the f32 projection; hidden is rounded to nearest even into bf16.

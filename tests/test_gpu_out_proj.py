@@ -6,7 +6,7 @@ seeded synthetic weights.
 Tolerance: the bf16 bound, |gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise (the
 GPU accumulates the bf16 products in f32 and rounds the output to bf16; the
 oracle is double throughout).  Token counts cover the few-token kernel (1 to
-64 rows: one or two 32-row tiles, full and ragged), the tiled kernel (65, a
+64 rows: one to four 16-row tiles, full and ragged), the tiled kernel (65, a
 full 256-row tile, a ragged tile edge), and a prefill-sized batch checked on
 sampled rows (rows are independent, so a sample is exact for its rows).
 """
@@ -42,7 +42,7 @@ def run_case(M, rows=None, config=70, in_place=False):
     return assert_close(got, ref, synth.BF16, f"out_proj M={M}")
 
 
-@pytest.mark.parametrize("M", [1, 4, 32, 33, 64, 65, 256, 257])
+@pytest.mark.parametrize("M", [1, 4, 16, 17, 32, 33, 48, 64, 65, 256, 257])
 def test_out_proj_all_rows(M):
     run_case(M)
 
@@ -66,3 +66,44 @@ def test_out_proj_deterministic():
     b = fa.out_proj(inp.attn, inp.w, inp.gamma, inp.residual)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_out_proj_few_tokens_reused_workspace():
+    """One workspace (filled with junk first) through few-token calls of
+    different sizes: the slice partials a previous call left behind must not
+    leak into the next."""
+    ws = torch.empty(fa.out_proj_workspace_size(64), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xA5)
+    for i, M in enumerate([64, 7, 64, 1, 40]):
+        inp = synth.out_proj_inputs(M, config=74, step=i, device=DEV, backend="numpy")
+        out = fa.out_proj(inp.attn, inp.w, inp.gamma, inp.residual, workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle.out_proj_rows(bits(inp.attn), bits(inp.w), inp.gamma.cpu().numpy(), bits(inp.residual))
+        assert_close(out.double().cpu().numpy(), ref, synth.BF16, f"out_proj reused workspace call {i} M={M}")
+
+
+def test_out_proj_few_tokens_graph_replays_match_eager():
+    """A captured few-token call replays with new attn rows copied in and eager
+    calls in between; every replay equals the eager result bit for bit."""
+    M = 48
+    inp = synth.out_proj_inputs(M, config=75, device=DEV)
+    ws = torch.empty(fa.out_proj_workspace_size(M), dtype=torch.uint8, device=DEV)
+    attn, out = inp.attn.clone(), torch.empty_like(inp.residual)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                         # warm-up outside the capture
+        fa.out_proj(attn, inp.w, inp.gamma, inp.residual, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fa.out_proj(attn, inp.w, inp.gamma, inp.residual, out=out, workspace=ws)
+    for rep in range(3):
+        attn.copy_(synth.out_proj_inputs(M, config=75, step=10 + rep, device=DEV).attn)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        eager = fa.out_proj(attn, inp.w, inp.gamma, inp.residual)
+        torch.cuda.synchronize()
+        assert torch.equal(got, eager), f"replay {rep}"
