@@ -249,6 +249,9 @@ constexpr int kNormGroups = kModelDim / 4;
 template <int NPARTS, int THREADS>
 __global__ __launch_bounds__(THREADS) void out_proj_norm_kernel(OutProjArgs a) {
     constexpr int PER = (kNormGroups + THREADS - 1) / THREADS;
+    // a long batch's projection, residual and output are each touched once:
+    // nontemporal (the few-token slices were just written and are read cached)
+    constexpr bool kStream = NPARTS == 1;
     __shared__ float red[THREADS / 64];
     const int t = blockIdx.x, tid = threadIdx.x;
     const float* prow = a.proj + (int64_t)t * kModelDim;
@@ -260,7 +263,10 @@ __global__ __launch_bounds__(THREADS) void out_proj_norm_kernel(OutProjArgs a) {
         const int gidx = min(tid + THREADS * u, kNormGroups - 1);
         floatx4 part[NPARTS];
 #pragma unroll
-        for (int q = 0; q < NPARTS; ++q) part[q] = *(const floatx4*)(prow + q * pstride + 4 * gidx);
+        for (int q = 0; q < NPARTS; ++q) {
+            const floatx4* src = (const floatx4*)(prow + q * pstride + 4 * gidx);
+            part[q] = kStream ? __builtin_nontemporal_load(src) : *src;
+        }
         x[u] = part[0];
 #pragma unroll
         for (int q = 1; q < NPARTS; ++q) x[u] += part[q];
@@ -281,7 +287,9 @@ __global__ __launch_bounds__(THREADS) void out_proj_norm_kernel(OutProjArgs a) {
         const int gidx = tid + THREADS * u;
         if (gidx >= kNormGroups) break;
         const floatx4 g = *(const floatx4*)(a.gamma + 4 * gidx);
-        const uint2 rr = *(const uint2*)(res + 4 * gidx);
+        const unsigned long long* rsrc = (const unsigned long long*)(res + 4 * gidx);
+        const unsigned long long r64 = kStream ? __builtin_nontemporal_load(rsrc) : *rsrc;
+        const uint2 rr = make_uint2((unsigned)r64, (unsigned)(r64 >> 32));
         const float r4[4] = {__uint_as_float(rr.x << 16), __uint_as_float(rr.x & 0xffff0000u),
                              __uint_as_float(rr.y << 16), __uint_as_float(rr.y & 0xffff0000u)};
         unsigned packed[2];
@@ -291,7 +299,9 @@ __global__ __launch_bounds__(THREADS) void out_proj_norm_kernel(OutProjArgs a) {
             if (c & 1) packed[c / 2] |= u16 << 16;
             else packed[c / 2] = u16;
         }
-        *(uint2*)(out + 4 * gidx) = make_uint2(packed[0], packed[1]);
+        const unsigned long long o64 = (unsigned long long)packed[0] | ((unsigned long long)packed[1] << 32);
+        if (kStream) __builtin_nontemporal_store(o64, (unsigned long long*)(out + 4 * gidx));
+        else *(unsigned long long*)(out + 4 * gidx) = o64;
     }
 }
 
