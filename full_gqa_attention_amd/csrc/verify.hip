@@ -117,6 +117,7 @@ void verify_kernel(VerifyArgs a) {
     // fp16) and of V.  Rows past the last position are clamped to it (masked
     // later, like every key outside a row's window).  Tile k of the split
     // waits in register slot k % DEP, DEP tiles ahead of the one in use.
+    // Each cached row is read by one workgroup: nontemporal loads.
     const int r_t = tid / CPR, c_t = tid % CPR;
     constexpr int64_t ROW = (int64_t)kKvHeads * D * ES;
     const char* kbase = (const char*)a.cache_k + (((int64_t)s * a.capacity) * kKvHeads + g) * D * ES + c_t * 16;
@@ -124,8 +125,8 @@ void verify_kernel(VerifyArgs a) {
     u32x4 kr[DEP], vr[DEP];
     auto load = [&](int slot, int k) __attribute__((always_inline)) {
         const int64_t off = (int64_t)min(min(tile_first + k, tile_last) * BN + r_t, hi - 1) * ROW;
-        kr[slot] = *(const u32x4*)(kbase + off);
-        vr[slot] = *(const u32x4*)(vbase + off);
+        kr[slot] = __builtin_nontemporal_load((const u32x4*)(kbase + off));
+        vr[slot] = __builtin_nontemporal_load((const u32x4*)(vbase + off));
     };
     auto store = [&](int slot, int bufi, bool with_v) __attribute__((always_inline)) {
         *(u32x4*)((char*)Ks[bufi] + (r_t * LDK + c_t * 8) * 2) = k_chunk_to_score(kr[slot], T{});
