@@ -293,6 +293,51 @@ def _visible(p, j, kind, W):
     return j <= p and (kind == FULL_NOPE or p - j < W)
 
 
+def _nearest_storage(x64, dtype):
+    """The storage value nearest to each float64 (ties to the even pattern),
+    found by comparing neighbours rather than by the oracle's frexp rounding.
+    numpy's float64 -> float32 cast is correctly rounded; torch's float64 ->
+    bfloat16 cast goes through float32 (a double rounding), so its result is
+    only a starting point: the nearest of it and its two bf16 neighbours wins."""
+    x64 = np.asarray(x64, dtype=np.float64)
+    if dtype == F32:
+        return np.float32(x64).astype(np.float64)
+    start = torch.from_numpy(x64.ravel()).float().to(torch.bfloat16).view(torch.int16).numpy()
+    bits = start.astype(np.int64) & 0xFFFF
+    cand = np.stack([(bits + d) & 0xFFFF for d in (-1, 0, 1)])            # [3, n]
+    vals = (cand.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    dist = np.abs(vals - x64.ravel()[None])
+    dist[~np.isfinite(vals)] = np.inf
+    dist[(cand & 0x7FFF) == 0x7F80] = np.inf                               # +-inf patterns
+    best = dist.min(axis=0)
+    tie_even = np.where(dist == best[None], (cand & 1), 2)                 # prefer an even pattern
+    pick = np.argmin(tie_even, axis=0)
+    return vals[pick, np.arange(vals.shape[1])].reshape(x64.shape)
+
+
+def _khat_independent(k_raw64, positions, kind, theta, k_gain, eps=1e-5):
+    """K-hat of raw key rows, written apart from the oracle: torch's fp64
+    rms_norm with the K gain ("Chapter 14 - QK-norm and RoPE" 14.3: K is a plain
+    normalize, gain 1 in the model, Q alone takes the 3.87 factor), then on
+    sliding layers the adjacent-pair rotation as a complex product
+    (x0 + i x1) * e^(i a) with a the f32 product f32(p) * f32(theta_i)
+    (14.4.1, 14.5 listing); keys rotate before they are stored (14.7).
+    k_raw64 [..., 128] float64, positions broadcastable to k_raw64.shape[:-1]."""
+    x = torch.tensor(k_raw64, dtype=torch.float64)
+    y = torch.nn.functional.rms_norm(x, (D,), weight=torch.full((D,), float(np.float32(k_gain)),
+                                                                dtype=torch.float64),
+                                     eps=float(np.float32(eps))).numpy()
+    if kind == FULL_NOPE:
+        return y
+    th32 = np.float32(float(np.float32(theta)) ** (-np.arange(D // 2) * 2.0 / D))
+    pos32 = np.float32(np.broadcast_to(positions, y.shape[:-1]))[..., None]
+    ang = (pos32 * th32).astype(np.float64)                                 # numpy f32 multiply
+    z = (y[..., 0::2] + 1j * y[..., 1::2]) * np.exp(1j * ang)
+    out = np.empty_like(y)
+    out[..., 0::2], out[..., 1::2] = z.real, z.imag
+    return out
+
+
 @pytest.mark.parametrize("dtype", [F32, BF16])
 @pytest.mark.parametrize("kind,W", [(SLIDING_ROPE, 1), (SLIDING_ROPE, 2), (SLIDING_ROPE, 3),
                                     (SLIDING_ROPE, 5), (SLIDING_ROPE, 12), (SLIDING_ROPE, 15),
@@ -310,9 +355,15 @@ def test_layer_matches_sdpa_fp64(kind, W, L, dtype):
     out, kst, vst = _run(layer, L, q, k, v, gate, ck, cv, want_store=True)
     out = out.reshape(S, T, H * D)
     assert np.array_equal(vst, _to_f64(v, dtype))
+    # the appended keys, recomputed apart from the oracle and rounded to the
+    # nearest storage value: the stored rows must be exactly these
+    pos = L + np.arange(T)[None, :, None]
+    kexact = _khat_independent(_to_f64(k, dtype), pos, kind, theta, 1.0)
+    knew = _nearest_storage(kexact, dtype)
+    assert np.array_equal(kst, knew)
     q64 = _to_f64(q, dtype)
     for s in range(S):
-        keys = np.concatenate([_to_f64(ck[s, :L], dtype), kst[s]], axis=0)   # [L+T, G, D]
+        keys = np.concatenate([_to_f64(ck[s, :L], dtype), knew[s]], axis=0)   # [L+T, G, D]
         vals = np.concatenate([_to_f64(cv[s, :L], dtype), vst[s]], axis=0)
         qh = np.empty((H, T, D))
         for t in range(T):
@@ -458,6 +509,36 @@ def test_chunked_and_decode_equal_monolithic(kind, W, dtype):
     cv = _as_storage(np.concatenate([vst[:, :T - 1], np.zeros((S, 1, G, D))], axis=1), dtype)
     dec = _run(lay, T - 1, q[:, T - 1:], k[:, T - 1:], v[:, T - 1:], gate[:, T - 1:], ck, cv)
     assert np.array_equal(dec.reshape(S, H * D), mono[:, T - 1])
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("kind", [SLIDING_ROPE, FULL_NOPE])
+@pytest.mark.parametrize("gk", [1.0, 0.5])
+def test_appended_keys_match_independent_khat(kind, dtype, gk):
+    """Every appended K row is the nearest storage value to K-hat recomputed
+    outside the oracle (torch rms_norm with the K gain, then the rotation at
+    the row's position on sliding layers): catches the Q gain used for K, an
+    unnormalised K, a position offset on K, or a missing or wrong rounding.
+    A K gain apart from the Q gain (3.87) and from 1 separates the gains."""
+    S, T, L = 2, 24, 37
+    theta = 500000.0
+    layer = _layer(kind, 8, theta, dtype, gq=3.87, gk=gk)
+    rng = np.random.default_rng(81)
+    q, k, v, gate, ck, cv = _case(S, T, L, dtype, seed=81)
+    # a spread of magnitudes per row, so that a missing normalisation shows
+    k = _as_storage(_to_f64(k, dtype) * rng.uniform(0.05, 20.0, (S, T, G, 1)), dtype)
+    _, kst, _ = _run(layer, L, q, k, v, gate, ck, cv, rows=[(0, 0)], want_store=True)
+    pos = L + np.arange(T)[None, :, None]
+    kexact = _khat_independent(_to_f64(k, dtype), pos, kind, theta, gk)
+    assert np.array_equal(kst, _nearest_storage(kexact, dtype))
+    # and the stored value is within half a storage ulp of the exact K-hat
+    ulp = np.spacing(np.abs(kexact).astype(np.float32)).astype(np.float64) * (65536.0 if dtype == BF16 else 1.0)
+    assert np.all(np.abs(kst - kexact) <= 0.5 * ulp * (1 + 1e-12))
+    # closed form of the stored rows' RMS: gk * sqrt(ms / (ms + eps)) of the raw row
+    ms = np.mean(_to_f64(k, dtype) ** 2, axis=-1)
+    rms = np.sqrt(np.mean(kst * kst, axis=-1))
+    assert np.allclose(rms, gk * np.sqrt(ms / (ms + float(np.float32(1e-5)))),
+                       rtol=4e-3 if dtype == BF16 else 1e-6)
 
 
 def test_nope_rows_are_position_free():
