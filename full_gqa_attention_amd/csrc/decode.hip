@@ -44,12 +44,6 @@
 #include "device_common.h"
 #include "kernels.h"
 
-#ifndef MUSE_DECODE_WAVES
-#define MUSE_DECODE_WAVES 2        // waves per SIMD the register budget targets
-#endif
-#ifndef MUSE_DECODE_DEPTH
-#define MUSE_DECODE_DEPTH 3        // 16-row sub-tiles in flight per wave
-#endif
 
 
 namespace muse {
@@ -79,7 +73,7 @@ struct SubTile {
 
 
 template <typename T, int DEPTH>
-__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(MUSE_DECODE_WAVES, MUSE_DECODE_WAVES)))
+__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_kernel(DecodeArgs a) {
     using Tr = DecodeTraits<T>;
     constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
@@ -655,7 +649,7 @@ void decode_kernel(DecodeArgs a) {
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream) {
     const dim3 grid((unsigned)(a.n_seq * kKvHeads * a.nsplit)), block(64 * kDecodeWaves);
     if (dtype == 1)
-        hipLaunchKernelGGL((decode_kernel<bf16_t, MUSE_DECODE_DEPTH>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((decode_kernel<bf16_t, kDecodeDepth>), grid, block, 0, stream, a);
     else
         hipLaunchKernelGGL((decode_kernel<float, 2>), grid, block, 0, stream, a);
     return hipGetLastError();

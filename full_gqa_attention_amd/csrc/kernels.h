@@ -99,12 +99,8 @@ struct DecodeArgs {
 // Short bf16 chunks (at most kVerifyTokens new tokens per sequence): split-K
 // attention with all 16 heads x 16 token rows of a KV head per workgroup,
 // then a merge of the splits with the gate.
-#ifndef MUSE_VERIFY_DEPTH
-#define MUSE_VERIFY_DEPTH 4     // key tiles in flight per verify workgroup (register slots)
-#endif
-#ifndef MUSE_VERIFY_BLOCKS
-#define MUSE_VERIFY_BLOCKS 256  // verify workgroups a call aims for (splits = this / (2 n_seq))
-#endif
+constexpr int kVerifyDepth = 4;     // key tiles in flight per verify workgroup (register slots)
+constexpr int kVerifyBlocks = 256;  // verify workgroups a call aims for (splits = this / (2 n_seq))
 constexpr int kVerifyTokens = 16;
 constexpr int kVerifyTile = 32;     // keys per tile
 struct VerifyArgs {
@@ -172,6 +168,9 @@ constexpr int kDecodeTile = 64;  // split granularity of the decode (keys)
 // their size, at most this) lies inside the copy.
 constexpr int kWindowAlign = 64;
 constexpr int kDecodeWaves = 8;  // waves per decode workgroup (two per SIMD)
+constexpr int kDecodeDepth = 3;  // 16-row sub-tiles of loads in flight per decode wave
+constexpr int kDecodeTargetBlocks = 256;   // decode workgroups a call aims for: one per CU
+constexpr int kDecodeMinSplitRows = 512;   // rows per decode split, at least (when the span allows)
 constexpr int kDecodeReadySpins = 1 << 20;  // polls of a ready word before the merge gives up
 constexpr int kMaxSplits = 128;  // decode splits per (sequence, KV head), at most
 constexpr int kArriveGroup = 8;   // decode splits per merge group (and group arrival word)

@@ -8,7 +8,6 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
 #include <cstring>
 
 #include "kernels.h"
@@ -72,7 +71,7 @@ bool use_verify(const muse_attn_layer* l, int32_t n_new) {
     return l->dtype == MUSE_BF16 && !l->kv_ring && n_new >= 1 && n_new <= muse::kVerifyTokens;
 }
 
-// Verify splits: about MUSE_VERIFY_BLOCKS workgroups in total, at least 16 tiles (512 keys)
+// Verify splits: about kVerifyBlocks workgroups in total, at least 16 tiles (512 keys)
 // per split when the keys allow, at most 64 splits.
 void verify_split(const muse_attn_layer* l, int32_t n_seq, int32_t n_new, int32_t max_seq_len,
                   int32_t* nsplit, int32_t* chunk_tiles) {
@@ -81,7 +80,7 @@ void verify_split(const muse_attn_layer* l, int32_t n_seq, int32_t n_new, int32_
     const int64_t bn = muse::kVerifyTile;
     const int64_t tiles = (prefix + n_new + 2 * bn - 1) / bn;   // covers any alignment of the key range
     const int64_t seqs = n_seq > 0 ? n_seq : 1;
-    int64_t want = (MUSE_VERIFY_BLOCKS + 2 * seqs - 1) / (2 * seqs);
+    int64_t want = (muse::kVerifyBlocks + 2 * seqs - 1) / (2 * seqs);
     if (want > tiles / 16) want = tiles / 16;
     if (want > 64) want = 64;
     if (want < 1) want = 1;
@@ -104,21 +103,9 @@ muse_status check_sizes(int32_t n_seq, int32_t n_new, int32_t max_seq_len) {
     return MUSE_OK;
 }
 
-int64_t decode_target_blocks() {
-    const char* e = std::getenv("MUSE_DECODE_TARGET_BLOCKS");
-    const long v = e ? std::strtol(e, nullptr, 10) : 0;
-    return v > 0 ? v : 256;                            // one workgroup per CU
-}
-
-int64_t decode_min_split_rows() {
-    const char* e = std::getenv("MUSE_DECODE_MIN_SPLIT_ROWS");
-    const long v = e ? std::strtol(e, nullptr, 10) : 0;
-    return v > 0 ? v : 512;
-}
-
-// Decode split: about decode_target_blocks() workgroups in total, chunks a
+// Decode split: about kDecodeTargetBlocks workgroups in total, chunks a
 // multiple of the 64-row tile and (when the span allows) of at least
-// decode_min_split_rows() rows: a split costs a fixed few microseconds (its
+// kDecodeMinSplitRows rows: a split costs a fixed few microseconds (its
 // first loads, its partial and the merge), which short splits do not repay.
 // The span of visible rows is at most window (sliding) or max_seq_len + 1
 // (full).
@@ -127,10 +114,10 @@ void decode_split(const muse_attn_layer* l, int32_t n_seq, int32_t max_seq_len,
     int64_t span = (int64_t)max_seq_len + 1;
     if (l->kind == MUSE_SLIDING_ROPE && l->window < span) span = l->window;
     const int64_t pairs = (int64_t)(n_seq > 0 ? n_seq : 1) * kKvHeads;
-    const int64_t target = decode_target_blocks();
+    const int64_t target = muse::kDecodeTargetBlocks;
     int64_t want = (target + pairs - 1) / pairs;
     const int64_t tiles = (span + muse::kDecodeTile - 1) / muse::kDecodeTile;
-    const int64_t by_rows = span / decode_min_split_rows();
+    const int64_t by_rows = span / muse::kDecodeMinSplitRows;
     if (want > by_rows) want = by_rows;
     if (want > tiles) want = tiles;
     if (want > muse::kMaxSplits) want = muse::kMaxSplits;

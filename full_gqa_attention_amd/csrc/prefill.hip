@@ -13,7 +13,7 @@
 // Two kernels share the scheme below.  prefill_kernel (f32 layers): one
 // workgroup = 128 query rows of one head (4 waves x 32 rows), 64-key tiles,
 // online softmax whose reference moves lazily.  prefill_group_kernel (bf16
-// layers, further down): one workgroup = 4 heads of one KV group over the same
+// layers, further down): one workgroup = 8 heads of one KV group over the same
 // 32 query rows, 32-key tiles, a fixed per-row softmax reference.
 //
 // Each wave computes S^T = K Q^T on 32x32 MFMA tiles (fp16 32x32x16 on bf16
@@ -35,18 +35,9 @@
 #include "device_common.h"
 #include "kernels.h"
 
-#ifndef MUSE_PREFILL_QG
-#define MUSE_PREFILL_QG 1   // 32-row query groups per wave on bf16 layers
-#endif
-#ifndef MUSE_PREFILL_WPB
-#define MUSE_PREFILL_WPB 8   // waves (heads of one KV group) per workgroup on bf16 layers
-#endif
-#ifndef MUSE_PREFILL_KT
-#define MUSE_PREFILL_KT 1    // 32-key halves per K/V tile on bf16 layers
-#endif
-#ifndef MUSE_PREFILL_PIPE
-#define MUSE_PREFILL_PIPE 0  // software-pipelined tile loop on bf16 layers
-#endif
+// bf16 layers: 32-row query groups per wave, waves (heads of one KV group)
+// per workgroup, 32-key halves per K/V tile
+constexpr int kGroupQG = 1, kGroupWPB = 8, kGroupKT = 1;
 
 namespace muse {
 
@@ -368,9 +359,6 @@ void prefill_kernel(AttnArgs a) {
 // the Q.K MFMAs start from -ref instead of 0, so no subtraction is left
 // either.  Row sums are taken from the bf16 P values that enter the P.V
 // product (v_dot2 against (1, 1)).
-#ifndef MUSE_PREFILL_PRIO
-#define MUSE_PREFILL_PRIO 0
-#endif
 template <int QG> struct GroupTraits {
     static constexpr int WAVES = QG == 1 ? 2 : 1;      // waves per SIMD the registers allow
 };
@@ -382,9 +370,8 @@ int prefill_grid_group(int n_seq, int n_new, int rows_per_wave, int heads_per_bl
 }
 
 // QG: 32-row query groups per wave; WPB: waves (= heads of one KV group) per
-// workgroup; KT: 32-key halves per K/V tile; PIPE: issue the Q.K of the next
-// tile next to the softmax and P.V of the current one
-template <int QG, int WPB, int KT, bool PIPE>
+// workgroup; KT: 32-key halves per K/V tile
+template <int QG, int WPB, int KT>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(GroupTraits<QG>::WAVES)))
 void prefill_group_kernel(AttnArgs a) {
     typedef bf16_t T;
@@ -475,13 +462,11 @@ void prefill_group_kernel(AttnArgs a) {
         for (int st = 0; st < NST; ++st) qraw[qg][st] = *(const bf16x8*)(qrow + 2 * MQ::KPL * st + MQ::KPL * gl);
     }
     u32x4 ka0[NCH], va0[NCH];                          // the loop's first K/V tile
-    if constexpr (!PIPE) {
 #pragma unroll
-        for (int u = 0; u < NCH; ++u) {
-            const int64_t off = (int64_t)min(tile_lo * BN + r_t + u * RSTEP, kv_end - 1) * ROW;
-            ka0[u] = *(const u32x4*)(kbase + off);
-            va0[u] = *(const u32x4*)(vbase + off);
-        }
+    for (int u = 0; u < NCH; ++u) {
+        const int64_t off = (int64_t)min(tile_lo * BN + r_t + u * RSTEP, kv_end - 1) * ROW;
+        ka0[u] = *(const u32x4*)(kbase + off);
+        va0[u] = *(const u32x4*)(vbase + off);
     }
     if (a.rope) {
         const float th = theta_of_lane<AttnArgs>(lane);
@@ -551,29 +536,6 @@ void prefill_group_kernel(AttnArgs a) {
             *(u32x4*)(kd + u * RSTEP * LDK * ES) = kreg[u];
             if (with_v) *(u32x4*)(vd + u * RSTEP * LDV * ES) = vreg[u];
         }
-    };
-
-    auto load_k = [&](int tile) __attribute__((always_inline)) {
-        const int j0 = tile * BN;
-#pragma unroll
-        for (int u = 0; u < NCH; ++u)
-            kreg[u] = *(const u32x4*)(kbase + (int64_t)min(j0 + r_t + u * RSTEP, kv_end - 1) * ROW);
-    };
-    auto load_v = [&](int tile) __attribute__((always_inline)) {
-        const int j0 = tile * BN;
-#pragma unroll
-        for (int u = 0; u < NCH; ++u)
-            vreg[u] = *(const u32x4*)(vbase + (int64_t)min(j0 + r_t + u * RSTEP, kv_end - 1) * ROW);
-    };
-    auto store_k = [&](int bufi) __attribute__((always_inline)) {
-        char* kd = (char*)Ks[bufi] + r_t * LDK * ES + c_t * 16;
-#pragma unroll
-        for (int u = 0; u < NCH; ++u) *(u32x4*)(kd + u * RSTEP * LDK * ES) = kreg[u];
-    };
-    auto store_v = [&](int bufi) __attribute__((always_inline)) {
-        char* vd = (char*)Vs[bufi] + r_t * LDV * ES + c_t * 16;
-#pragma unroll
-        for (int u = 0; u < NCH; ++u) *(u32x4*)(vd + u * RSTEP * LDV * ES) = vreg[u];
     };
 
     // S^T halves (keys 32kt..32kt+31 x the wave's row groups), started at c0
@@ -737,112 +699,56 @@ void prefill_group_kernel(AttnArgs a) {
             l_run[qg] = 0.0f;
         }
 
-        if constexpr (!PIPE) {
-            // loads run two tiles ahead, alternating between two register sets
-            u32x4 ka[NCH], va[NCH], kb2[NCH], vb2[NCH];
-            auto ld2 = [&](u32x4 (&kr)[NCH], u32x4 (&vr)[NCH], int tile) __attribute__((always_inline)) {
-                const int j0 = tile * BN;
+        // loads run two tiles ahead, alternating between two register sets
+        u32x4 ka[NCH], va[NCH], kb2[NCH], vb2[NCH];
+        auto ld2 = [&](u32x4 (&kr)[NCH], u32x4 (&vr)[NCH], int tile) __attribute__((always_inline)) {
+            const int j0 = tile * BN;
 #pragma unroll
-                for (int u = 0; u < NCH; ++u) {
-                    const int64_t off = (int64_t)min(j0 + r_t + u * RSTEP, kv_end - 1) * ROW;
-                    kr[u] = *(const u32x4*)(kbase + off);
-                    vr[u] = *(const u32x4*)(vbase + off);
-                }
-            };
-            auto st2 = [&](const u32x4 (&kr)[NCH], const u32x4 (&vr)[NCH], int bufi) __attribute__((always_inline)) {
-                char* kd = (char*)Ks[bufi] + r_t * LDK * ES + c_t * 16;
-                char* vd = (char*)Vs[bufi] + r_t * LDV * ES + c_t * 16;
-#pragma unroll
-                for (int u = 0; u < NCH; ++u) {
-                    *(u32x4*)(kd + u * RSTEP * LDK * ES) = kr[u];
-                    *(u32x4*)(vd + u * RSTEP * LDV * ES) = vr[u];
-                }
-            };
-            if (pass == 0) {                           // loaded before Q-hat
-#pragma unroll
-                for (int u = 0; u < NCH; ++u) {
-                    ka[u] = ka0[u];
-                    va[u] = va0[u];
-                }
-            } else {
-                ld2(ka, va, tile_lo);
+            for (int u = 0; u < NCH; ++u) {
+                const int64_t off = (int64_t)min(j0 + r_t + u * RSTEP, kv_end - 1) * ROW;
+                kr[u] = *(const u32x4*)(kbase + off);
+                vr[u] = *(const u32x4*)(vbase + off);
             }
-            st2(ka, va, 0);
-            ld2(kb2, vb2, min(tile_lo + 1, tile_hi));
-            __syncthreads();
-            auto step = [&](int it, u32x4 (&kn)[NCH], u32x4 (&vn)[NCH], u32x4 (&kf)[NCH], u32x4 (&vf)[NCH])
-                __attribute__((always_inline)) {
-                // kn/vn hold tile it+1 (loaded one iteration ago); kf/vf take tile it+2
-                const int cur = it & 1;
-                ld2(kf, vf, min(tile_lo + it + 2, tile_hi));
-                __builtin_amdgcn_sched_barrier(0);
-                bool unset[QG];
-                record_unset(unset);
-                floatx16 sc[KT][QG];
-#if MUSE_PREFILL_PRIO == 1 || MUSE_PREFILL_PRIO == 2
-                __builtin_amdgcn_s_setprio(1);
-#endif
-                qk(sc, Ks[cur], nref);
-#if MUSE_PREFILL_PRIO == 1
-                __builtin_amdgcn_s_setprio(0);
-#endif
-                st2(kn, vn, cur ^ 1);                      // that buffer is free since the last barrier
-                fix_tile(sc, (tile_lo + it) * BN, unset);
-#if MUSE_PREFILL_PRIO == 2
-                __builtin_amdgcn_s_setprio(0);
-#endif
-#if MUSE_PREFILL_PRIO == 3
-                __builtin_amdgcn_s_setprio(1);
-#endif
-                softmax_pv(sc, Vs[cur]);
-#if MUSE_PREFILL_PRIO == 3
-                __builtin_amdgcn_s_setprio(0);
-#endif
-                __syncthreads();
-            };
-            for (int it = 0; it < ntiles; it += 2) {
-                step(it, kb2, vb2, ka, va);
-                if (it + 1 < ntiles) step(it + 1, ka, va, kb2, vb2);
+        };
+        auto st2 = [&](const u32x4 (&kr)[NCH], const u32x4 (&vr)[NCH], int bufi) __attribute__((always_inline)) {
+            char* kd = (char*)Ks[bufi] + r_t * LDK * ES + c_t * 16;
+            char* vd = (char*)Vs[bufi] + r_t * LDV * ES + c_t * 16;
+#pragma unroll
+            for (int u = 0; u < NCH; ++u) {
+                *(u32x4*)(kd + u * RSTEP * LDK * ES) = kr[u];
+                *(u32x4*)(vd + u * RSTEP * LDV * ES) = vr[u];
+            }
+        };
+        if (pass == 0) {                               // loaded before Q-hat
+#pragma unroll
+            for (int u = 0; u < NCH; ++u) {
+                ka[u] = ka0[u];
+                va[u] = va0[u];
             }
         } else {
-            // K runs one tile ahead of V: iteration it issues the Q.K of tile it+1
-            // (K slot (it+1)&1) next to the softmax and P.V of tile it (V slot
-            // it&1), while the loads of K[it+2] and V[it+1] are in flight; those
-            // land in K slot it&1 and V slot (it+1)&1, both last read before the
-            // previous barrier.  The mask and references of tile it+1 are applied
-            // after that barrier, so the loop body has no branch between the
-            // MFMAs of one tile and the VALU work of the other.
-            load_k(tile_lo);
-            load_v(tile_lo);
-            store_k(0);
-            store_v(0);
-            load_k(min(tile_lo + 1, tile_hi));
-            store_k(1);
+            ld2(ka, va, tile_lo);
+        }
+        st2(ka, va, 0);
+        ld2(kb2, vb2, min(tile_lo + 1, tile_hi));
+        __syncthreads();
+        auto step = [&](int it, u32x4 (&kn)[NCH], u32x4 (&vn)[NCH], u32x4 (&kf)[NCH], u32x4 (&vf)[NCH])
+            __attribute__((always_inline)) {
+            // kn/vn hold tile it+1 (loaded one iteration ago); kf/vf take tile it+2
+            const int cur = it & 1;
+            ld2(kf, vf, min(tile_lo + it + 2, tile_hi));
+            __builtin_amdgcn_sched_barrier(0);
+            bool unset[QG];
+            record_unset(unset);
+            floatx16 sc[KT][QG];
+            qk(sc, Ks[cur], nref);
+            st2(kn, vn, cur ^ 1);                          // that buffer is free since the last barrier
+            fix_tile(sc, (tile_lo + it) * BN, unset);
+            softmax_pv(sc, Vs[cur]);
             __syncthreads();
-            floatx16 s0[KT][QG], s1[KT][QG];
-            bool un0[QG], un1[QG];
-            record_unset(un0);
-            qk(s0, Ks[0], nref);
-            fix_tile(s0, tile_lo * BN, un0);
-            __syncthreads();                               // K slot 0 is refilled in iteration 0
-            auto step = [&](int it, floatx16 (&sc)[KT][QG], floatx16 (&sn)[KT][QG], bool (&un_n)[QG])
-                __attribute__((always_inline)) {
-                load_k(min(tile_lo + it + 2, tile_hi));    // past the end: harmless repeats
-                load_v(min(tile_lo + it + 1, tile_hi));
-                __builtin_amdgcn_sched_barrier(0);         // keep the loads ahead of the compute
-                record_unset(un_n);
-                qk(sn, Ks[(it + 1) & 1], nref);            // the last iteration's is unused
-                softmax_pv(sc, Vs[it & 1]);
-                __builtin_amdgcn_sched_barrier(0);         // stores after the compute
-                store_k(it & 1);
-                store_v((it + 1) & 1);
-                __syncthreads();
-                if (it + 1 < ntiles) fix_tile(sn, (tile_lo + it + 1) * BN, un_n);
-            };
-            for (int it = 0; it < ntiles; it += 2) {
-                step(it, s0, s1, un1);
-                if (it + 1 < ntiles) step(it + 1, s1, s0, un0);
-            }
+        };
+        for (int it = 0; it < ntiles; it += 2) {
+            step(it, kb2, vb2, ka, va);
+            if (it + 1 < ntiles) step(it + 1, ka, va, kb2, vb2);
         }
 
         // an overflow anywhere shows up as a non-finite l or O
@@ -917,9 +823,9 @@ void prefill_group_kernel(AttnArgs a) {
 
 hipError_t launch_prefill(const AttnArgs& a, int dtype, hipStream_t stream) {
     if (dtype == 1)
-        hipLaunchKernelGGL((prefill_group_kernel<MUSE_PREFILL_QG, MUSE_PREFILL_WPB, MUSE_PREFILL_KT, MUSE_PREFILL_PIPE != 0>),
-                           dim3((unsigned)prefill_grid_group(a.n_seq, a.n_new, 32 * MUSE_PREFILL_QG, MUSE_PREFILL_WPB)),
-                           dim3(64 * MUSE_PREFILL_WPB), 0, stream, a);
+        hipLaunchKernelGGL((prefill_group_kernel<kGroupQG, kGroupWPB, kGroupKT>),
+                           dim3((unsigned)prefill_grid_group(a.n_seq, a.n_new, 32 * kGroupQG, kGroupWPB)),
+                           dim3(64 * kGroupWPB), 0, stream, a);
     else
         hipLaunchKernelGGL(prefill_kernel<float>, dim3((unsigned)prefill_grid(a.n_seq, a.n_new)), dim3(256), 0,
                            stream, a);

@@ -381,7 +381,7 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a) {
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)(a.n_seq * kKvHeads * a.nsplit)), block(512);
-    hipLaunchKernelGGL(verify_kernel<MUSE_VERIFY_DEPTH>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(verify_kernel<kVerifyDepth>, grid, block, 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return hipSuccess;
