@@ -107,44 +107,6 @@ __device__ __forceinline__ float sigmoid(float g) {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// ---------------------------------------------- handoffs between workgroups
-// Split partials cross workgroups (and XCDs): written and read with
-// agent-scope atomic accesses or the sc1 cache policy, both coherent per
-// access.  No agent-scope fence is used: on this GPU one writes back and
-// invalidates a whole XCD L2, which costs more than the attention.
-__device__ __forceinline__ void publish(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float observe(const float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Vector accesses with the same per-dword coherence (sc1).  The buffer
-// resource spans `bytes` from `base`; an access beyond it reads zeros.
-constexpr int kCoherent = 16;                          // sc1
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
-}
-// Count one arrival on a tagged word (tag << 32 | count; a word carrying
-// another tag counts as zero, so the word needs no clearing); true for the
-// arrival that completes n, which resets the word to (tag, 0) for a replay
-// with the same tag.  The first attempt assumes it completes n.
-__device__ __forceinline__ bool arrive_tagged(unsigned long long* word, uint32_t tag, int n) {
-    unsigned long long old = ((unsigned long long)tag << 32) | (unsigned int)(n - 1);
-    unsigned int arrived = 0;
-    for (;;) {                                         // retries only on contention
-        const unsigned int cnt = ((unsigned int)(old >> 32) == tag) ? (unsigned int)old : 0u;
-        const unsigned long long want = ((unsigned long long)tag << 32) | (cnt + 1);
-        if (__hip_atomic_compare_exchange_strong(word, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT)) {
-            arrived = cnt + 1;
-            break;
-        }
-    }
-    const bool done = arrived == (unsigned int)n;
-    if (done) __hip_atomic_store(word, (unsigned long long)tag << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return done;
-}
-
 // ----------------------------------------------------- QK-norm and RoPE
 // One head vector of 128 values per wave: lane i holds the adjacent pair
 // (x[2i], x[2i+1]), which is RoPE pair i.

@@ -63,9 +63,9 @@ struct AttnArgs {
     int32_t v_windowed;     // 1: cache_v row likewise (cache_v is then the V copy)
 };
 
-// Kernel (c): the whole decode step for one new token per sequence in one
-// launch -- QK-norm/RoPE of Q and K, the KV append, split-K attention, the
-// merge of the splits and the gate.
+// Kernel (c): the decode step for one new token per sequence -- QK-norm/RoPE
+// of Q and K, the KV append and split-K attention in one launch, then (with
+// more than one split) the merge of the splits and the gate in a second.
 struct DecodeArgs {
     const void* q;          // [S][32][128]
     const void* k;          // [S][2][128]
@@ -87,12 +87,9 @@ struct DecodeArgs {
     float scale_log2;       // attn_scale * log2(e)
     int32_t chunk;          // keys per split
     int32_t nsplit;         // splits per (sequence, KV head)
-    uint32_t tag;           // nonzero, distinct per call: marks this call's arrivals
     float* part_o;          // [S][32][nsplit][128] unnormalised partial outputs
     float* part_m;          // [S][32][nsplit] partial maxima (log2 domain)
     float* part_l;          // [S][32][nsplit] partial softmax denominators
-    unsigned long long* arrivals;  // [S][2][kArriveWords] (tag << 32 | arrivals): the pair, then groups
-    unsigned int* ready;    // [S][2][kReadyWords] tag of the call whose split (then group) partial is stored, 0 once merged
     float theta[64];        // f32 RoPE frequency table
 };
 
@@ -167,15 +164,11 @@ constexpr int kDecodeTile = 64;  // split granularity of the decode (keys)
 // that every key tile the attention kernel loads (tiles start at multiples of
 // their size, at most this) lies inside the copy.
 constexpr int kWindowAlign = 64;
-constexpr int kDecodeWaves = 8;  // waves per decode workgroup (two per SIMD)
+constexpr int kDecodeWaves = 4;  // waves per decode workgroup (two workgroups per CU)
 constexpr int kDecodeDepth = 3;  // 16-row sub-tiles of loads in flight per decode wave
 constexpr int kDecodeTargetBlocks = 256;   // decode workgroups a call aims for: one per CU
-constexpr int kDecodeMinSplitRows = 512;   // rows per decode split, at least (when the span allows)
-constexpr int kDecodeReadySpins = 1 << 20;  // polls of a ready word before the merge gives up
-constexpr int kMaxSplits = 128;  // decode splits per (sequence, KV head), at most
-constexpr int kArriveGroup = 8;   // decode splits per merge group (and group arrival word)
-constexpr int kArriveWords = 1 + kMaxSplits / kArriveGroup;  // arrival words per (sequence, KV head)
-constexpr int kReadyWords = kMaxSplits + kMaxSplits / kArriveGroup;  // ready words per (sequence, KV head): splits, groups
+constexpr int kDecodeMinSplitRows = 64;    // rows per decode split, at least (when the span allows)
+constexpr int kMaxSplits = 256;  // decode splits per (sequence, KV head), at most
 
 int prefill_grid(int n_seq, int n_new);
 

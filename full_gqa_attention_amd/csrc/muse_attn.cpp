@@ -5,7 +5,6 @@
 
 #include <hip/hip_runtime_api.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -105,8 +104,9 @@ muse_status check_sizes(int32_t n_seq, int32_t n_new, int32_t max_seq_len) {
 
 // Decode split: about kDecodeTargetBlocks workgroups in total, chunks a
 // multiple of the 64-row tile and (when the span allows) of at least
-// kDecodeMinSplitRows rows: a split costs a fixed few microseconds (its
-// first loads, its partial and the merge), which short splits do not repay.
+// kDecodeMinSplitRows rows: a CU streams only a few tens of GB/s, so a short
+// window is spread over many CUs, but each split also carries its first
+// loads and a partial for the merge.
 // The span of visible rows is at most window (sliding) or max_seq_len + 1
 // (full).
 void decode_split(const muse_attn_layer* l, int32_t n_seq, int32_t max_seq_len,
@@ -135,10 +135,10 @@ void decode_split(const muse_attn_layer* l, int32_t n_seq, int32_t max_seq_len,
 // max(0, seq_len - window + 1) rounded down to kWindowAlign (kq_capacity =
 // min(max_seq_len, window - 1 + kWindowAlign - 1) + N); on ring layers then a
 // copy of the same rows of V, laid out alike.
-// Decode: arrival words [S][2][kArriveWords] (u64), ready words [S][2][kReadyWords]
-// (u32), then the split partials O [S][32][nsplit][128], m and l [S][32][nsplit].
+// Decode: with more than one split per (sequence, KV head), the split partials
+// O [S][32][nsplit][128], m and l [S][32][nsplit]; with one split, nothing.
 struct WorkspaceLayout {
-    size_t qhat = 0, kq = 0, vq = 0, arrivals = 0, ready = 0, part_o = 0, part_m = 0, part_l = 0, total = 0;
+    size_t qhat = 0, kq = 0, vq = 0, part_o = 0, part_m = 0, part_l = 0, total = 0;
     int64_t kq_capacity = 0;
     int32_t chunk = 0, nsplit = 0;
     bool verify = false;
@@ -175,12 +175,8 @@ WorkspaceLayout layout_for(const muse_attn_layer* l, int32_t n_seq, int32_t n_ne
             }
         }
     } else {
-        w.arrivals = 0;
-        off = round_up((size_t)n_seq * kKvHeads * muse::kArriveWords * sizeof(unsigned long long), kAlign);
         decode_split(l, n_seq, max_seq_len, &w.chunk, &w.nsplit);
-        w.ready = off;
-        off += round_up((size_t)n_seq * kKvHeads * muse::kReadyWords * sizeof(unsigned int), kAlign);
-        const size_t parts = (size_t)n_seq * kHeads * w.nsplit;
+        const size_t parts = w.nsplit > 1 ? (size_t)n_seq * kHeads * w.nsplit : 0;
         w.part_o = off;
         off += round_up(parts * kHeadDim * sizeof(float), kAlign);
         w.part_m = off;
@@ -199,17 +195,6 @@ struct Range {
 };
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
-// A distinct nonzero 32-bit tag per decode call (see the arrival words in
-// decode.hip); process-wide, never repeats within 2^32 calls.
-uint32_t next_tag() {
-    static std::atomic<uint32_t> counter{0x6d757365u};
-    uint32_t t;
-    do {
-        t = counter.fetch_add(1, std::memory_order_relaxed) + 1;
-    } while (t == 0);
-    return t;
-}
-
 void rope_table(float theta, float* out64) {
     for (int i = 0; i < kHeadDim / 2; ++i)
         out64[i] = (float)std::pow((double)theta, -(2.0 * i) / (double)kHeadDim);
@@ -225,14 +210,17 @@ muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, cons
     if (!cache) return MUSE_ERR_NULL;
     if (cache->capacity < 0) return MUSE_ERR_CAPACITY;
     if (rows_needed(layer, max_seq_len, n_new) > cache->capacity) return MUSE_ERR_CAPACITY;
+    // a ring is addressed with 32-bit byte offsets
+    if (layer->kv_ring && cache->capacity * (int64_t)(kKvHeads * kHeadDim * elem_bytes(layer->dtype)) > INT32_MAX)
+        return MUSE_ERR_CAPACITY;
     if (n_seq == 0 || n_new == 0) return MUSE_OK;    // nothing to do
-    if (!seq_len || !q || !k || !v || !gate || !out || !cache->k || !cache->v || !workspace)
-        return MUSE_ERR_NULL;
+    if (!seq_len || !q || !k || !v || !gate || !out || !cache->k || !cache->v) return MUSE_ERR_NULL;
     if (timer && (!timer->start || !timer->stop)) return MUSE_ERR_NULL;
+    const WorkspaceLayout wl = layout_for(layer, n_seq, n_new, max_seq_len, decode);
+    if (wl.total > 0 && !workspace) return MUSE_ERR_NULL;      // a call that needs no workspace takes NULL
     const void* ptrs[] = {seq_len, q, k, v, gate, out, cache->k, cache->v, workspace};
     for (const void* p : ptrs)
         if (!aligned16(p)) return MUSE_ERR_ALIGN;
-    const WorkspaceLayout wl = layout_for(layer, n_seq, n_new, max_seq_len, decode);
     if (workspace_bytes < wl.total) return MUSE_ERR_WORKSPACE;
 
     const size_t es = elem_bytes(layer->dtype);
@@ -283,12 +271,9 @@ muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, cons
         da.scale_log2 = scale_log2;
         da.chunk = wl.chunk;
         da.nsplit = wl.nsplit;
-        da.tag = next_tag();
         da.part_o = (float*)(ws + wl.part_o);
         da.part_m = (float*)(ws + wl.part_m);
         da.part_l = (float*)(ws + wl.part_l);
-        da.arrivals = (unsigned long long*)(ws + wl.arrivals);
-        da.ready = (unsigned int*)(ws + wl.ready);
         if (rope) rope_table(layer->rope_theta, da.theta);
         if (timer && hipEventRecord(timer->start, stream) != hipSuccess) return MUSE_ERR_HIP;
         if (muse::launch_decode(da, dt, stream) != hipSuccess) return MUSE_ERR_HIP;

@@ -173,13 +173,15 @@ muse_status muse_attn_prefill(const muse_attn_layer* layer, int32_t n_seq, int32
 /*
  * Decode: exactly one new token per sequence (n_new = 1) at position
  * seq_len[s]; the same five steps as prefill, with the attention split over
- * the cache length (split-K) and merged on the device.  Arguments as for
- * muse_attn_prefill with n_new = 1 (q [n_seq][1][32][128], etc.).  The
- * splits of a call meet in the workspace (arrival counts, ready words and
- * partials, all tagged with the call): calls that may run at the same time
- * must not share a workspace.  A call replayed from a captured graph reuses
- * its tag, and each call leaves the workspace ready for that.  If a split's
- * partial never becomes ready (bounded wait), that output is NaN.
+ * the cache length (split-K).  Arguments as for muse_attn_prefill with
+ * n_new = 1 (q [n_seq][1][32][128], etc.).  With more than one split per
+ * (sequence, KV head) the splits store their partial (max, sum, output) in
+ * the workspace and a second kernel on the same stream merges them in split
+ * order and applies the gate; the timer then spans both kernels.  The
+ * workspace holds nothing between calls (contents on entry are ignored), but
+ * calls that may run at the same time must not share one.  When
+ * muse_attn_workspace_size reports 0 bytes (one split), workspace may be
+ * NULL.
  */
 muse_status muse_attn_decode(const muse_attn_layer* layer, int32_t n_seq,
                              const int32_t* seq_len, int32_t max_seq_len,

@@ -126,6 +126,12 @@ def _mut(attr, value):
     return f
 
 
+def _long_prefix(x):
+    """A prefix long enough that the call needs a workspace (several decode splits)."""
+    x.max_seq_len = 600
+    x.cache.capacity = 1024
+
+
 def _lay(attr, value):
     def f(x):
         setattr(x.layer, attr, value)
@@ -157,8 +163,8 @@ CASES = [
     ("q NULL", _mut("q", 0), NULL),
     ("gate NULL", _mut("gate", 0), NULL),
     ("seq_len NULL", _mut("seq_len", 0), NULL),
-    ("workspace NULL", _mut("ws", 0), NULL),
-    ("workspace too small", _mut("ws_bytes", 1024), WORKSPACE),
+    ("workspace NULL", lambda x: (_long_prefix(x), setattr(x, "ws", 0)), NULL),
+    ("workspace too small", lambda x: (_long_prefix(x), setattr(x, "ws_bytes", 1024)), WORKSPACE),
     ("q misaligned", _mut("q", BASE + 512 * MB * 1 + 8), ALIGN),
     ("out overlaps q", _mut("out", BASE + 512 * MB * 1 + 4096), ALIAS),
     ("workspace overlaps cache k", _mut("ws", BASE + 512 * MB * 7 + 4096), ALIAS),
@@ -168,6 +174,7 @@ CASES = [
 @pytest.mark.parametrize("decode", [False, True])
 @pytest.mark.parametrize("name,mutate,code", CASES, ids=[c[0] for c in CASES])
 def test_validation_fails_closed(lib, name, mutate, code, decode):
+    assert code != 0                 # fake pointers: every case must stop before a launch
     f = Fake(decode=decode)
     mutate(f)
     assert f.call(lib) == code
@@ -216,8 +223,8 @@ def test_validation_ring(lib, decode):
     # short sequences need only their positions, even on a ring layer
     f = Fake(decode=decode)
     f.layer.kv_ring = 1
-    f.cache.capacity = 200
-    f.max_seq_len = 100
+    f.cache.capacity = 700           # under the window, over the 600 + 64 positions
+    f.max_seq_len = 600
     f.ws = 0
     assert f.call(lib) == NULL       # passes the capacity check, stops at the NULL workspace
 
@@ -333,3 +340,14 @@ def test_out_proj_in_place_residual_and_empty(lib):
     # out == residual is the in-place stream update (validated, then nothing
     # enqueued for n == 0; with n > 0 the launch needs a GPU)
     assert _op_call(lib, n=0, out=0x50000000) == OK
+
+
+def test_decode_workspace_zero_for_one_split(lib):
+    """A decode whose keys fit one split per (sequence, KV head) needs no
+    workspace (the header allows a NULL workspace then); a longer one does."""
+    lay = fa.make_layer(fa.FULL_NOPE, dtype=fa.BF16)
+    n = ctypes.c_size_t()
+    assert lib.muse_attn_workspace_size(ctypes.byref(lay), 4, 1, 100, 1, ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.muse_attn_workspace_size(ctypes.byref(lay), 4, 1, 8192, 1, ctypes.byref(n)) == 0
+    assert n.value > 0

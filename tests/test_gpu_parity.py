@@ -112,12 +112,14 @@ def test_decode_ragged(spec, dtype):
 
 
 @pytest.mark.parametrize("dtype", [synth.BF16, synth.F32], ids=["bf16", "f32"])
-def test_decode_long_context_two_level_merge(dtype):
-    """Long contexts make many splits per (sequence, KV head), merged in
-    groups and then across groups: 40,000 cached rows (six groups, the last
-    partial), 9,000 (two) and 7,680 (a full group and a group of one split)."""
+@pytest.mark.parametrize("lens", [[40000, 9000, 7680], [60000]], ids=["3seq", "1seq"])
+def test_decode_long_context_many_splits(dtype, lens):
+    """Long contexts make many splits per (sequence, KV head), merged by the
+    merge kernel in batches of 16 rows: three sequences of 40,000, 9,000 and
+    7,680 cached rows (42 splits, fewer live in the shorter ones), and one of
+    60,000 (126 splits: the (m, l) slots past 64 sit in a second register
+    per lane)."""
     spec = synth.full()
-    lens = [40000, 9000, 7680]
     w = _custom("long_decode", dtype, len(lens), max(lens), 1, [spec])
     inp = _ragged_inputs(w, spec, lens, 1)
     _check_layer(w, spec, inp, decode=True)
@@ -217,9 +219,10 @@ def test_empty_inputs():
 
 
 def test_decode_workspace_reuse_and_garbage():
-    """The split-arrival words need no clearing: a workspace full of random
-    bytes, reused across calls of different batch sizes, gives the same
-    results as a fresh one."""
+    """A workspace full of random bytes, reused across calls of different
+    batch sizes, gives the same results as a fresh one: the merge reads every
+    partial slot of a call but uses only the live splits' (the slots of a
+    shorter sequence's missing splits hold whatever was there)."""
     spec = synth.full()
     w = _custom("ws", synth.BF16, 6, 3000, 1, [spec])
     inp = _ragged_inputs(w, spec, [3000, 2500, 100, 3000, 1, 2048], 1)
@@ -241,9 +244,9 @@ def test_decode_workspace_reuse_and_garbage():
 
 @pytest.mark.parametrize("spec", [synth.sliding(2048, 500000.0), synth.full()], ids=["w2048", "full"])
 def test_decode_graph_replays_match_eager(spec):
-    """A captured decode call replays with the same arrival tag every time;
-    every replay (with new inputs copied in and eager work in between) must
-    equal the eager result on the same inputs."""
+    """A captured decode call (split kernel, then merge kernel) replays with
+    new inputs copied in and eager work in between; every replay must equal
+    the eager result on the same inputs."""
     S, L = 4, 5000
     w = _custom("graph", synth.BF16, S, L, 1, [spec])
     inp = _ragged_inputs(w, spec, [L, 4000, 2999, 17], 1)
