@@ -1,20 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of the Muse Glimmer attention core on one MI355X.
 
-Default workload (one "step"): a decode step of 64 sequences x 8,192 cached
-tokens, bf16, on one sliding layer (RoPE, window 2,048) and one full NoPE
-layer -- QK-norm, RoPE, KV append, split-K attention and the gate, for both
-layers.  `value` is decode attention KV bytes per second over the whole step
-(the visible K/V rows, 1,024 B per row per sequence).  The 8 x 8,192 bf16
-prefill (both layer kinds) is timed in the same run and reported under
-"prefill" in TFLOP/s (16,384 flop per visible (query, key) pair over 32
-heads), so the line carries both halves of the metric.
+Default workload: the 52-layer attention schedule (layers l % 4 == 3 full
+NoPE, the others sliding RoPE with a 2,048-key window) for 4 sequences with
+32,768 cached rows per layer: a chunked prefill of 4,096 new tokens through
+all 52 layers, then decode steps.  One "step" is one decode step of all 52
+layers -- QK-norm, RoPE, KV append, split-K attention, merge and gate in
+every layer, then the device-side position increment -- replayed from a
+HIP graph.  `value` is the decode phase's attention KV bytes per second
+(the visible K/V rows, 1,024 B per row per sequence, summed over the timed
+steps and layers).  The chunked prefill is timed in the same run and
+reported under "prefill" in TFLOP/s (16,384 flop per visible (query, key)
+pair over 32 heads), so the line carries both halves of the metric.  The
+other workloads (the 1 x 512 f32 prefill, the 64 x 8,192 decode, the 8 x
+8,192 prefill, the 16 x 131,072 decode) are extra legs under "configs".
 
-Inputs are seeded synthetic tensors already resident in HBM.  Decode caches
-are rotated over enough copies that every step reads bytes the 256 MB
-Infinity Cache cannot still hold.  `roofline` uses the attention kernel's own
-launch time from HIP events recorded by the library around that kernel.
-`cpu_baseline` times the CPU oracle on the same step's inputs (rank 0, N=1).
+Inputs are seeded synthetic tensors already resident in HBM.  `roofline`
+uses the attention kernel's own launch time from HIP events the library
+records around it.  `cpu_baseline` times the CPU oracle on a bounded sample
+of the same workload (rank 0, N=1); each leg carries its own.
 """
 from __future__ import annotations
 
@@ -31,8 +35,10 @@ if ROOT not in sys.path:
 METRIC = "decode attn KV GB/s (% HBM peak) + prefill attn TFLOP/s (% MFMA peak)"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 / fp16 MFMA
+FP32_PEAK_TFLOPS = 157.3         # MI355X fp32 (the 1 x 512 f32 workload)
 FLOP_PER_PAIR = 32 * 4 * 128     # 32 heads x (2*128 for Q.K + 2*128 for P.V)
 MALL_BYTES = 256 << 20
+HEADLINE = "schedule_52x4_32768p4096_256d"
 
 
 def kv_row_bytes(dtype: int) -> int:
@@ -48,7 +54,7 @@ def prefill_pairs(spec, L: int, N: int) -> int:
 
 
 PROFILES = os.path.join(ROOT, "profiles")
-COUNTERS_FILE = os.path.join(PROFILES, "decode_64x8192_bf16_hbm_counters.md")
+COUNTERS_FILE = os.path.join(PROFILES, "decode_schedule_52x4_hbm_counters.md")
 DECODE_SOURCES = ["full_gqa_attention_amd/csrc/decode.hip", "full_gqa_attention_amd/csrc/device_common.h",
                   "full_gqa_attention_amd/csrc/kernels.h", "full_gqa_attention_amd/csrc/muse_attn.cpp"]
 MFMA_FILE = os.path.join(PROFILES, "prefill_8x8192_bf16_mfma_counters.md")
@@ -70,23 +76,6 @@ def sources_hash(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic():
-    """HBM bytes per decode-kernel launch from the committed counter summary,
-    or None when the decode kernel's sources changed since it was taken."""
-    try:
-        kv = {}
-        with open(COUNTERS_FILE) as f:
-            for line in f:
-                if line.startswith("    ") and ":" in line:
-                    k, v = line.strip().split(":", 1)
-                    kv[k.strip()] = v.strip()
-        if kv.get("decode_sources_sha256_16") != sources_hash(DECODE_SOURCES):
-            return None
-        return float(kv["hbm_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
-        return None
-
-
 def read_summary_values(path: str) -> dict:
     """The indented `key: value` lines of a committed counter summary."""
     kv = {}
@@ -101,6 +90,20 @@ def read_summary_values(path: str) -> dict:
     return kv
 
 
+def counter_traffic():
+    """HBM bytes per decode-kernel launch of the headline schedule (full and
+    sliding layers) from the committed counter summary, or None when the
+    decode kernel's sources changed since it was taken."""
+    kv = read_summary_values(COUNTERS_FILE)
+    if kv.get("decode_sources_sha256_16") != sources_hash(DECODE_SOURCES):
+        return None
+    try:
+        return {"all": float(kv["hbm_bytes_per_launch"]), "full": float(kv["hbm_bytes_per_launch_full"]),
+                "sliding": float(kv["hbm_bytes_per_launch_sliding"])}
+    except (KeyError, ValueError):
+        return None
+
+
 def prefill_counters():
     """MFMA utilisation of the prefill kernel per layer from the committed
     counter summary, or None when the prefill sources changed since."""
@@ -113,6 +116,487 @@ def prefill_counters():
                 "source": os.path.relpath(MFMA_FILE, ROOT)}
     except (KeyError, ValueError):
         return None
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, out: str, command: str):
+    """Write the decode kernels' HBM-traffic summary from two --pmc runs of
+    `bench.py --counters-run` (eager decode steps of the 52-layer schedule:
+    dispatches in layer order, layer l full NoPE iff l % 4 == 3)."""
+    import csv
+
+    def per_kernel(path):
+        copy, dec, merge = [], [], []
+        for r in csv.DictReader(open(path)):
+            v = float(r["Counter_Value"])
+            name = r["Kernel_Name"]
+            if "decode_merge_kernel" in name:
+                merge.append(v)
+            elif "decode_kernel" in name:
+                dec.append(v)
+            elif "copyBuffer" in name:
+                copy.append(v)
+        return copy, dec, merge
+
+    fc, fd, fm = per_kernel(fetch_csv)
+    wc, wd, wm = per_kernel(write_csv)
+    kinds = ["full" if i % 52 % 4 == 3 else "sliding" for i in range(len(fd))]
+
+    def avg(xs, kind):
+        v = [x for x, k in zip(xs, kinds) if kind in (k, "all")]
+        return sum(v) / len(v)
+
+    rows, vals = [], {}
+    for kind in ("sliding", "full", "all"):
+        fb = avg(fd, kind) * 1024 * FETCH_SCALE
+        wb = avg(wd, kind) * 1024 * WRITE_SCALE
+        vals[kind] = fb + wb
+        rows.append(f"| decode_kernel, {kind} | {avg(fd, kind):.1f} | {avg(wd, kind):.1f} | {fb / 1e6:.2f} | "
+                    f"{wb / 1e6:.3f} |")
+    mk = ["full" if i % 52 % 4 == 3 else "sliding" for i in range(len(fm))]
+    for kind in ("sliding", "full"):
+        v = [x for x, k in zip(fm, mk) if k == kind]
+        u = [x for x, k in zip(wm, mk) if k == kind]
+        if v:
+            rows.append(f"| decode_merge_kernel, {kind} | {sum(v) / len(v):.1f} | {sum(u) / len(u):.1f} | "
+                        f"{sum(v) / len(v) * 1024 * FETCH_SCALE / 1e6:.2f} | {sum(u) / len(u) * 1024 * WRITE_SCALE / 1e6:.3f} |")
+    lines = ["# HBM traffic of the decode kernels: 52-layer schedule, 4 sequences at 36,864 + step cached rows", "",
+             "Two counter runs (from /tmp, repository at $ROOT):", "", "```", command, "```", "",
+             f"Calibration: the first copy in each run is a 1 GiB device copy (`--calibrate-copy`); it read "
+             f"{fc[0]:.1f} KiB on FETCH_SIZE and {wc[0]:.1f} KiB on WRITE_SIZE, so FETCH_SIZE is scaled by "
+             f"{FETCH_SCALE} and WRITE_SIZE by {WRITE_SCALE}.  Algorithmic KV bytes per launch: sliding "
+             f"4 x 2,048 x 1,024 B = 8.39 MB; full 4 x (p + 1) x 1,024 B = 151.0 MB at p = 36,864.", "",
+             "| kernel, layers | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB |",
+             "|---|---|---|---|---|", *rows, "",
+             "Values read by bench.py (traffic is reported only while these sources are unchanged):", "",
+             f"    decode_sources_sha256_16: {sources_hash(DECODE_SOURCES)}",
+             f"    hbm_bytes_per_launch: {vals['all']:.0f}",
+             f"    hbm_bytes_per_launch_full: {vals['full']:.0f}",
+             f"    hbm_bytes_per_launch_sliding: {vals['sliding']:.0f}", ""]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64, help="timed decode steps of the schedule (at most 256)")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prefill-steps", type=int, default=3, help="timed chunked-prefill passes")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' legs")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timings")
+    ap.add_argument("--ring", action="store_true",
+                    help="sliding layers keep their window in a ring cache (kv_ring) in the schedule")
+    ap.add_argument("--verify", action="store_true",
+                    help="also time the 16-token verify call (64 x 8,192 cached rows, both layers)")
+    ap.add_argument("--out-proj", action="store_true",
+                    help="also time the block's tail (o_proj + post-attention norm) at 65,536 and 64 tokens")
+    ap.add_argument("--relocate", action="store_true",
+                    help="also time NoPE tile relocation (muse_kv_relocate) of a 64 x 8,192 full-layer cache")
+    ap.add_argument("--counters-run", action="store_true",
+                    help="only the schedule's chunk and 2 eager decode steps (for --pmc counter runs)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the 8 x 8,192 prefill and print its JSON object (for counter runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 1 GiB device copy first (scale for HBM byte counters)")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT", "COMMAND"),
+                    help="write a kernel-trace summary from rocprofv3 kernel_stats.csv and exit")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT", "COMMAND"),
+                    help="write the decode kernels' HBM-traffic summary from two --pmc runs and exit")
+    ap.add_argument("--summarize-mfma", nargs=4, metavar=("PMC1_CSV", "PMC2_CSV", "OUT", "COMMAND"),
+                    help="write the prefill kernel's MFMA-utilisation summary from two --pmc runs and exit")
+    return ap.parse_args()
+
+
+def percentiles(xs):
+    """p10, p50, p90 (nearest rank) of a list of launch times."""
+    v = sorted(xs)
+    return [v[min(len(v) - 1, int(q * len(v)))] for q in (0.1, 0.5, 0.9)]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _kind(spec, synth) -> str:
+    return "full" if spec.kind == synth.FULL_NOPE else "sliding"
+
+
+def kernel_roofline(kind_ms, kind_bytes, peak, unit, scale, kernel):
+    """Roofline of a kernel from per-launch times (ms) and algorithmic work per
+    launch, overall and per layer kind: achieved = average work per launch /
+    average launch time."""
+    per = {}
+    all_ms, all_w = [], []
+    for kind in kind_ms:
+        ms, wk = kind_ms[kind], kind_bytes[kind]
+        all_ms += ms
+        all_w += wk
+        a = (sum(wk) / len(wk)) / (sum(ms) / len(ms) * 1e-3) / scale
+        per[kind] = {"launches": len(ms), "avg_launch_us": round(1e3 * sum(ms) / len(ms), 2),
+                     "p10_p50_p90_us": [round(1e3 * x, 2) for x in percentiles(ms)],
+                     "algorithmic_per_launch": round(sum(wk) / len(wk)), "achieved": round(a, 1),
+                     "frac": round(a / peak, 4)}
+    a = (sum(all_w) / len(all_w)) / (sum(all_ms) / len(all_ms) * 1e-3) / scale
+    return {"achieved": round(a, 1), "peak": peak, "unit": unit, "frac": round(a / peak, 4), "kernel": kernel,
+            "launches": len(all_ms), "avg_launch_us": round(1e3 * sum(all_ms) / len(all_ms), 2),
+            "algorithmic_per_launch": round(sum(all_w) / len(all_w)), "per_kind": per}
+
+
+# ---------------------------------------------------------------- headline
+
+def bench_schedule(args, fa, synth, torch):
+    """The 52-layer schedule: the chunked prefill (eager calls, timed as a
+    phase and per attention kernel), then the decode phase: a few eager steps
+    with the library's kernel timer on every call (the roofline), and the
+    timed steps replayed from a captured HIP graph (`value`)."""
+    from full_gqa_attention_amd.schedule import Schedule
+    from full_gqa_attention_amd.timing import KernelTimers
+    w = synth.WORKLOADS[HEADLINE]
+    S, L0, N = w.n_seq, w.prefix, w.n_new
+    K = max(1, min(args.steps, w.decode_steps))
+    sch = Schedule(w, ring=args.ring)
+    kinds = [_kind(s, synth) for s in sch.specs]
+    log(f"schedule {w.name}: {len(sch.specs)} layers, cache {sch.cache_bytes() / 1e9:.2f} GB, ring={args.ring}")
+    torch.cuda.synchronize()
+    # ---- chunked prefill: one warm-up pass, then timed passes (each rewrites the same rows)
+    sch.prefill()
+    torch.cuda.synchronize()
+    P = max(1, args.prefill_steps)
+    timers = KernelTimers(P * len(sch.specs))
+    t0 = time.perf_counter()
+    for i in range(P):
+        sch.prefill(timers=[timers[i * len(sch.specs) + l] for l in range(len(sch.specs))])
+    torch.cuda.synchronize()
+    t_prefill = (time.perf_counter() - t0) / P
+    pms = {"sliding": [], "full": []}
+    pfl = {"sliding": [], "full": []}
+    for i in range(P):
+        for l, spec in enumerate(sch.specs):
+            pms[kinds[l]].append(timers.elapsed_ms(i * len(sch.specs) + l))
+            pfl[kinds[l]].append(FLOP_PER_PAIR * S * prefill_pairs(spec, L0, N))
+    timers.close()
+    flops = sum(FLOP_PER_PAIR * S * prefill_pairs(spec, L0, N) for spec in sch.specs)
+    prefill = {"workload": f"{w.name} (chunk of {N} tokens onto {L0} cached rows, 52 layers)",
+               "ms": round(t_prefill * 1e3, 3), "tflop": round(flops / 1e12, 3),
+               "tflops": round(flops / t_prefill / 1e12, 1),
+               "frac_mfma_peak": round(flops / t_prefill / 1e12 / MFMA_PEAK_TFLOPS, 4),
+               "launch": "eager calls, prep (K-hat, V append) and attention per layer",
+               "roofline": dict(bound="mfma", traffic=None, **kernel_roofline(
+                   pms, pfl, MFMA_PEAK_TFLOPS, "TFLOP/s", 1e12,
+                   "muse::prefill_group_kernel<1, 8, 1> (bf16)"))}
+    # ---- decode: eager steps with the kernel timer on every call
+    E = min(8, K)
+    sch.start_decode()
+    timers = KernelTimers(E * len(sch.specs))
+    for i in range(E):
+        sch.decode_step(timers=[timers[i * len(sch.specs) + l] for l in range(len(sch.specs))])
+    torch.cuda.synchronize()
+    dms = {"sliding": [], "full": []}
+    dby = {"sliding": [], "full": []}
+    for i in range(E):
+        for l, spec in enumerate(sch.specs):
+            dms[kinds[l]].append(timers.elapsed_ms(i * len(sch.specs) + l))
+            dby[kinds[l]].append(kv_row_bytes(w.dtype) * S * visible_rows(spec, L0 + N + i))
+    timers.close()
+    roof = dict(bound="hbm", **kernel_roofline(dms, dby, HBM_PEAK_GBS, "GB/s", 1e9, "muse::decode_kernel<bf16>"))
+    tr = counter_traffic() if not args.ring else None
+    roof["traffic"] = tr["all"] if tr else None
+    if tr:
+        for kind in ("full", "sliding"):
+            roof["per_kind"][kind]["traffic"] = tr[kind]
+    # ---- decode: the timed steps, replayed from one captured step
+    sch.start_decode()
+    graph = sch.capture_step()
+    for _ in range(args.warmup):
+        graph.replay()
+    sch.start_decode()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        graph.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del graph
+    kv = sum(kv_row_bytes(w.dtype) * S * visible_rows(spec, L0 + N + i) for i in range(K) for spec in sch.specs)
+    res = {"value": kv / wall / 1e9, "ms_per_step": wall * 1e3 / K, "kv_bytes": kv, "steps": K,
+           "roofline": roof, "prefill": prefill,
+           "config": {"workload": w.name, "layers": len(sch.specs), "full_layers": kinds.count("full"),
+                      "n_seq": S, "cached_tokens": L0, "chunk_tokens": N,
+                      "decode_positions": [L0 + N, L0 + N + K - 1], "q_heads": 32, "kv_heads": 2,
+                      "head_dim": 128, "window": 2048, "rope_theta": 500000.0, "kv_ring_sliding": bool(args.ring),
+                      "kv_cache_GB": round(sch.cache_bytes() / 1e9, 3),
+                      "decode_kv_bytes_per_step": round(kv / K)}}
+    return res, sch
+
+
+def oracle_layer_of(spec, dtype):
+    import oracle
+    return oracle.Layer(kind=spec.kind, window=spec.window, rope_theta=spec.rope_theta, rms_eps=spec.rms_eps,
+                        q_gain=spec.q_gain, k_gain=spec.k_gain, scale=spec.scale, dtype=dtype)
+
+
+def cpu_schedule_sample(sch, fa, synth, torch, n_steps: int = 4):
+    """The oracle on a bounded sample of the schedule, on the cache the GPU
+    holds: every layer's decode rows (all 4 sequences, all 32 heads) at the
+    first n_steps decode positions (the GPU's outputs there come from eager
+    decode steps run again here), and two rows of every layer's chunk
+    (sequence 0, tokens 0 and n_new - 1; linear caches only).  Returns the
+    oracle's times and work and the parity of the sampled GPU outputs."""
+    import numpy as np
+    import oracle
+    w = sch.w
+    S, L0, N = w.n_seq, w.prefix, w.n_new
+    sch.start_decode()
+    outs = []
+    for i in range(n_steps):
+        sch.decode_step()
+        torch.cuda.synchronize()
+        outs.append([d[4][:, 0].double().cpu().numpy() for d in sch.dec])
+    t_dec = t_pre = 0.0
+    kv = pairs = 0
+    worst, ok = 0.0, True
+    prows = np.array([(0, 0), (0, N - 1)], np.int32)
+
+    def check(got, ref):
+        nonlocal worst, ok
+        err = np.abs(got - ref)
+        worst = max(worst, float(err.max()))
+        ok = ok and bool(np.all(err <= 2e-2 + 1e-2 * np.abs(ref)))
+
+    for l, spec in enumerate(sch.specs):
+        inp = sch.inputs[l]
+        q, k, v, g, _ = sch.dec[l]
+        top = L0 + N + n_steps
+        ring = sch.is_ring(spec)
+        lo = 0 if spec.window == 0 else max(0, (L0 + N if ring else L0) - spec.window + 1)
+        ck = np.zeros((S, top, 2, 128), np.uint16)
+        cv = np.zeros_like(ck)
+        pos = torch.arange(lo, top, device=inp.cache_k.device)
+        rows = pos % spec.window if ring else pos
+        ck[:, lo:top] = synth.to_storage_numpy(inp.cache_k[:, rows])
+        cv[:, lo:top] = synth.to_storage_numpy(inp.cache_v[:, rows])
+        lay = oracle_layer_of(spec, w.dtype)
+        u16 = synth.to_storage_numpy
+        for i in range(n_steps):
+            p = L0 + N + i
+            args = (lay, np.full(S, p, np.int32), u16(k), u16(v), ck, cv, oracle.all_rows(S, 1),
+                    u16(q).reshape(S, 32, 128), u16(g).reshape(S, 4096))
+            t0 = time.perf_counter()
+            ref = oracle.attn_rows(*args)
+            t_dec += time.perf_counter() - t0
+            kv += kv_row_bytes(w.dtype) * S * visible_rows(spec, p)
+            check(outs[i][l], ref)
+        if not ring:                                   # a ring no longer holds the chunk's prefix
+            sel = (prows[:, 0], prows[:, 1])
+            args = (lay, np.full(S, L0, np.int32), u16(inp.k), u16(inp.v), ck, cv, prows,
+                    u16(inp.q)[sel], u16(inp.gate)[sel])
+            t0 = time.perf_counter()
+            ref = oracle.attn_rows(*args)
+            t_pre += time.perf_counter() - t0
+            pairs += sum(visible_rows(spec, L0 + int(t)) for t in prows[:, 1])
+            check(sch.outs[l][sel].double().cpu().numpy().reshape(len(prows), -1), ref)
+    return {"decode_s": t_dec, "decode_kv": kv, "prefill_s": t_pre, "prefill_pairs": pairs,
+            "parity": {"max_abs_err": worst, "within_tolerance": ok,
+                       "rows": f"{n_steps} decode steps x 52 layers x {S} sequences and 2 chunk rows per layer, "
+                               "all 32 heads, against the oracle"}}
+
+
+# ----------------------------------------------------------- other workloads
+
+class LayerRun:
+    """One layer of a decode or prefill workload with its inputs and caches
+    (decode: rotated over `copies` cache copies, so the 256 MB Infinity Cache
+    cannot serve a step from the previous one)."""
+
+    def __init__(self, w, spec, copies, decode, fa, synth):
+        import torch
+        self.spec = spec
+        self.inp = synth.layer_inputs(w, spec, device="cuda", backend="torch")
+        self.caches = [(self.inp.cache_k, self.inp.cache_v)]
+        for _ in range(1, copies):
+            self.caches.append((self.inp.cache_k.clone(), self.inp.cache_v.clone()))
+        self.layer = fa.make_layer(spec.kind, window=spec.window, rope_theta=spec.rope_theta,
+                                   rms_eps=spec.rms_eps, q_norm_gain=spec.q_gain,
+                                   k_norm_gain=spec.k_gain, attn_scale=spec.scale, dtype=w.dtype)
+        self.decode = decode
+        self.ws = fa.workspace(self.layer, w.n_seq, w.n_new, w.prefix, decode)
+        self.out = torch.empty_like(self.inp.gate)
+        self.max_seq_len = w.prefix
+
+    def call(self, fa, copy, timer=None):
+        ck, cv = self.caches[copy]
+        fn = fa.decode if self.decode else fa.prefill
+        fn(self.layer, self.inp.q, self.inp.k, self.inp.v, self.inp.gate, ck, cv, self.inp.seq_len,
+           self.out, max_seq_len=self.max_seq_len, workspace=self.ws, timer=timer)
+
+
+def run_timed(runs, steps, warmup, copies, fa, torch):
+    """W untimed steps, then K timed steps between synchronisations, with the
+    kernel timer on every call."""
+    from full_gqa_attention_amd.timing import KernelTimers
+    timers = KernelTimers(steps * len(runs))
+    for i in range(warmup):
+        for r in runs:
+            r.call(fa, i % copies)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for j, r in enumerate(runs):
+            r.call(fa, (warmup + i) % copies, timers[i * len(runs) + j])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch = [timers.elapsed_ms(i) for i in range(len(timers))]
+    timers.close()
+    return wall, per_launch
+
+
+def run_graphs(runs, steps, warmup, copies, fa, torch):
+    """The same steps replayed from HIP graphs (one captured step per cache copy)."""
+    graphs = []
+    for c in range(copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in runs:
+                r.call(fa, c)
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % copies].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[(warmup + i) % copies].replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del graphs
+    return wall
+
+
+def leg_decode(w, fa, synth, torch, steps=20, warmup=3, cpu=True):
+    """A decode workload (both layer kinds), graph-replayed; the kernel
+    timer on every call of an eager pass gives the per-kind roofline.  The CPU
+    oracle runs on the whole step and checks the GPU output."""
+    per_step = sum(kv_row_bytes(w.dtype) * w.n_seq * visible_rows(s, w.prefix) for s in w.layers)
+    copies = min(8, max(1, -(-(2 * MALL_BYTES) // max(per_step, 1)) + 1))
+    log(f"decode {w.name}: {copies} cache copies, {per_step / 1e6:.1f} MB KV per step")
+    runs = [LayerRun(w, spec, copies, True, fa, synth) for spec in w.layers]
+    torch.cuda.synchronize()
+    _, per_launch = run_timed(runs, steps, warmup, copies, fa, torch)
+    wall = run_graphs(runs, steps, warmup, copies, fa, torch)
+    ms = {"sliding": [], "full": []}
+    by = {"sliding": [], "full": []}
+    for j, r in enumerate(runs):
+        ms[_kind(r.spec, synth)] += per_launch[j::len(runs)]
+        by[_kind(r.spec, synth)] += [kv_row_bytes(w.dtype) * w.n_seq * visible_rows(r.spec, w.prefix)] * steps
+    res = {"metric": "decode attn KV GB/s", "value": round(per_step * steps / wall / 1e9, 1), "unit": "GB/s",
+           "ms_per_step": round(wall * 1e3 / steps, 5), "frac_hbm_peak": round(per_step * steps / wall / 1e9 / HBM_PEAK_GBS, 4),
+           "launch": "each step replayed from a HIP graph", "cache_copies": copies,
+           "roofline": dict(bound="hbm", traffic=None, **kernel_roofline(ms, by, HBM_PEAK_GBS, "GB/s", 1e9,
+                                                                         "muse::decode_kernel<bf16>"))}
+    if cpu:
+        res["cpu_baseline"], res["parity"] = cpu_decode_full(w, runs, synth, torch)
+    del runs
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_decode_full(w, runs, synth, torch):
+    """The oracle on every row of the decode step (all sequences, both layers)."""
+    import numpy as np
+    import oracle
+    rows = oracle.all_rows(w.n_seq, 1)
+    t_oracle, worst, ok = 0.0, 0.0, True
+    for r in runs:
+        ck, cv = r.caches[0]
+        args = (oracle_layer_of(r.spec, w.dtype), r.inp.seq_len.cpu().numpy(), synth.to_storage_numpy(r.inp.k),
+                synth.to_storage_numpy(r.inp.v), synth.to_storage_numpy(ck), synth.to_storage_numpy(cv), rows,
+                synth.to_storage_numpy(r.inp.q).reshape(-1, 32, 128),
+                synth.to_storage_numpy(r.inp.gate).reshape(-1, 4096))
+        t0 = time.perf_counter()
+        ref = oracle.attn_rows(*args)
+        t_oracle += time.perf_counter() - t0
+        err = np.abs(r.out.double().cpu().numpy().reshape(-1, 4096) - ref)
+        worst = max(worst, float(err.max()))
+        ok = ok and bool(np.all(err <= 2e-2 + 1e-2 * np.abs(ref)))
+    kv = sum(kv_row_bytes(w.dtype) * w.n_seq * visible_rows(r.spec, w.prefix) for r in runs)
+    return ({"value": round(kv / t_oracle / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+             "sample": f"the whole step: {w.n_seq} sequences x {len(runs)} layers, all 32 heads",
+             "seconds": round(t_oracle, 3)},
+            {"max_abs_err": worst, "within_tolerance": ok})
+
+
+def leg_prefill(w, fa, synth, torch, steps=5, warmup=2, cpu=True, cpu_rows=None, single_core=False):
+    """A prefill workload (both layer kinds), eager calls with the kernel
+    timer on each; the CPU oracle on every row (cpu_rows None) or a sample."""
+    log(f"prefill {w.name}")
+    runs = [LayerRun(w, spec, 1, False, fa, synth) for spec in w.layers]
+    torch.cuda.synchronize()
+    wall, per_launch = run_timed(runs, steps, warmup, 1, fa, torch)
+    flops = sum(FLOP_PER_PAIR * w.n_seq * prefill_pairs(s, w.prefix, w.n_new) for s in w.layers)
+    ms = {"sliding": [], "full": []}
+    fl = {"sliding": [], "full": []}
+    for j, r in enumerate(runs):
+        ms[_kind(r.spec, synth)] += per_launch[j::len(runs)]
+        fl[_kind(r.spec, synth)] += [FLOP_PER_PAIR * w.n_seq * prefill_pairs(r.spec, w.prefix, w.n_new)] * steps
+    bf16 = w.dtype == synth.BF16
+    peak = MFMA_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
+    kern = "muse::prefill_group_kernel<1, 8, 1> (bf16)" if bf16 else "muse::prefill_kernel<float> (f32)"
+    res = {"metric": "prefill attn TFLOP/s", "value": round(flops * steps / wall / 1e12, 2), "unit": "TFLOP/s",
+           "ms_per_step": round(wall * 1e3 / steps, 4), "frac_peak": round(flops * steps / wall / 1e12 / peak, 4),
+           "launch": "eager calls (prep and attention kernels per layer)",
+           "roofline": dict(bound="mfma", traffic=None, **kernel_roofline(ms, fl, peak, "TFLOP/s", 1e12, kern))}
+    if w.name == "prefill_8x8192_bf16":
+        res["roofline"]["counters"] = prefill_counters()
+    if cpu:
+        res["cpu_baseline"], res["parity"] = cpu_prefill(w, runs, synth, cpu_rows, single_core)
+    del runs
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_prefill(w, runs, synth, rows, single_core):
+    """The oracle on every row (rows None) or on the given (s, t) sample, in
+    pairs/s and rows/s; a sample reports the extrapolated full-run time."""
+    import numpy as np
+    import oracle
+    full = rows is None
+    rows = oracle.all_rows(w.n_seq, w.n_new) if full else np.asarray(rows, np.int32)
+    res, worst, ok = {}, 0.0, True
+    default_threads = oracle.num_threads()
+    for threads in ([1] if single_core else []) + [0]:
+        if threads:
+            oracle.set_num_threads(threads)
+        t_oracle, pairs = 0.0, 0
+        for r in runs:
+            sel = (rows[:, 0], rows[:, 1])
+            q = synth.to_storage_numpy(r.inp.q)[sel]
+            g = synth.to_storage_numpy(r.inp.gate)[sel]
+            args = (oracle_layer_of(r.spec, w.dtype), r.inp.seq_len.cpu().numpy(), synth.to_storage_numpy(r.inp.k),
+                    synth.to_storage_numpy(r.inp.v), None, None, rows, q, g)
+            t0 = time.perf_counter()
+            ref = oracle.attn_rows(*args)
+            t_oracle += time.perf_counter() - t0
+            pairs += sum(visible_rows(r.spec, w.prefix + int(t)) for t in rows[:, 1])
+            got = r.out.double().cpu().numpy()[sel].reshape(len(rows), -1)
+            err = np.abs(got - ref)
+            worst = max(worst, float(err.max()))
+            tol = 1e-4 if w.dtype == synth.F32 else 2e-2 + 1e-2 * np.abs(ref)
+            ok = ok and bool(np.all(err <= tol))
+        total_pairs = sum(w.n_seq * prefill_pairs(r.spec, w.prefix, w.n_new) for r in runs)
+        entry = {"value": round(pairs * FLOP_PER_PAIR / t_oracle / 1e12, 6), "unit": "TFLOP/s",
+                 "pairs_per_s": round(pairs / t_oracle), "rows_per_s": round(len(rows) * len(runs) / t_oracle, 1),
+                 "cores": oracle.num_threads(), "kind": "oracle", "seconds": round(t_oracle, 3),
+                 "sample": ("every row" if full else f"{len(rows)} (sequence, token) rows per layer (window and "
+                            f"tile edges), all 32 heads, both layers")}
+        if not full:
+            entry["extrapolated_full_run_s"] = round(t_oracle * total_pairs / pairs, 1)
+            entry["extrapolation"] = "full-run time = sample time x all visible pairs / sampled pairs"
+        res["single_core" if threads == 1 else "all_cores"] = entry
+        if threads:
+            oracle.set_num_threads(default_threads)
+    out = res["all_cores"]
+    if single_core:
+        out = dict(out, single_core=res["single_core"])
+    return out, {"max_abs_err": worst, "within_tolerance": ok}
 
 
 def summarize_mfma(pmc1_csv: str, pmc2_csv: str, out: str, command: str):
@@ -170,6 +654,7 @@ def summarize_mfma(pmc1_csv: str, pmc2_csv: str, out: str, command: str):
         f.write("\n".join(lines) + "\n")
 
 
+
 def summarize_trace(stats_csv: str, out: str, command: str):
     """Write a kernel-trace summary (text) from rocprofv3's kernel_stats.csv."""
     import csv
@@ -190,330 +675,6 @@ def summarize_trace(stats_csv: str, out: str, command: str):
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
-
-def summarize_counters(fetch_csv: str, write_csv: str, out: str, command: str):
-    """Write the decode kernel's HBM-traffic summary from two --pmc runs."""
-    import csv
-
-    def per_kernel(path):
-        copy, dec = [], []
-        for r in csv.DictReader(open(path)):
-            v = float(r["Counter_Value"])
-            if "decode_kernel" in r["Kernel_Name"]:
-                dec.append(v)
-            elif "copyBuffer" in r["Kernel_Name"]:
-                copy.append(v)
-        return copy, dec
-
-    fc, fd = per_kernel(fetch_csv)
-    wc, wd = per_kernel(write_csv)
-    # launches alternate sliding, full (the benchmark's layer order)
-    f_sl, f_fu = sum(fd[0::2]) / len(fd[0::2]), sum(fd[1::2]) / len(fd[1::2])
-    w_sl, w_fu = sum(wd[0::2]) / len(wd[0::2]), sum(wd[1::2]) / len(wd[1::2])
-    fetch_b = [x * 1024 * FETCH_SCALE for x in (f_sl, f_fu)]
-    write_b = [x * 1024 * WRITE_SCALE for x in (w_sl, w_fu)]
-    per_launch = (sum(fetch_b) + sum(write_b)) / 2
-    lines = ["# HBM traffic of the decode kernel: 64 x 8,192 bf16 decode step", "",
-             "Two counter runs (from /tmp, repository at $ROOT):", "", "```", command, "```", "",
-             f"Calibration: the first copy in each run is a 1 GiB device copy (`--calibrate-copy`); it read "
-             f"{fc[0]:.1f} KiB on FETCH_SIZE and {wc[0]:.1f} KiB on WRITE_SIZE, so FETCH_SIZE is scaled by "
-             f"{FETCH_SCALE} and WRITE_SIZE by {WRITE_SCALE}.", "",
-             "| launch | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB | algorithmic KV MB |",
-             "|---|---|---|---|---|---|",
-             f"| sliding (W 2048) | {f_sl:.1f} | {w_sl:.1f} | {fetch_b[0] / 1e6:.1f} | {write_b[0] / 1e6:.2f} | 134.2 |",
-             f"| full | {f_fu:.1f} | {w_fu:.1f} | {fetch_b[1] / 1e6:.1f} | {write_b[1] / 1e6:.2f} | 536.9 |",
-             "", "Values read by bench.py (traffic is reported only while these sources are unchanged):", "",
-             f"    decode_sources_sha256_16: {sources_hash(DECODE_SOURCES)}",
-             f"    hbm_bytes_per_launch: {per_launch:.0f}", ""]
-    with open(out, "w") as f:
-        f.write("\n".join(lines) + "\n")
-
-
-def parse():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode_64x8192_bf16")
-    ap.add_argument("--prefill-workload", default="prefill_8x8192_bf16")
-    ap.add_argument("--prefill-steps", type=int, default=10)
-    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
-    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--schedule", action="store_true",
-                    help="also time the 52-layer schedule workload (chunked prefill phase + 256 decode steps)")
-    ap.add_argument("--ring", action="store_true",
-                    help="sliding layers keep their window in a ring cache (kv_ring) in the decode and schedule runs")
-    ap.add_argument("--verify", action="store_true",
-                    help="also time the 16-token verify call (64 x 8,192 cached rows, both layers)")
-    ap.add_argument("--out-proj", action="store_true",
-                    help="also time the block's tail (o_proj + post-attention norm) at 65,536 and 64 tokens")
-    ap.add_argument("--relocate", action="store_true",
-                    help="also time NoPE tile relocation (muse_kv_relocate) of a 64 x 8,192 full-layer cache")
-    ap.add_argument("--eager", action="store_true",
-                    help="time decode steps as eager calls only (no HIP graph), e.g. under counter collection")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="run one 1 GiB device copy first (scale for HBM byte counters)")
-    ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT", "COMMAND"),
-                    help="write a kernel-trace summary from rocprofv3 kernel_stats.csv and exit")
-    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT", "COMMAND"),
-                    help="write the decode kernel's HBM-traffic summary from two --pmc runs and exit")
-    ap.add_argument("--prefill-only", action="store_true",
-                    help="time only the prefill workload and print its JSON object (for counter runs)")
-    ap.add_argument("--summarize-mfma", nargs=4, metavar=("PMC1_CSV", "PMC2_CSV", "OUT", "COMMAND"),
-                    help="write the prefill kernel's MFMA-utilisation summary from two --pmc runs and exit")
-    return ap.parse_args()
-
-
-def percentiles(xs):
-    """p10, p50, p90 (nearest rank) of a list of launch times."""
-    v = sorted(xs)
-    return [v[min(len(v) - 1, int(q * len(v)))] for q in (0.1, 0.5, 0.9)]
-
-
-def log(msg):
-    print(f"[bench] {msg}", file=sys.stderr, flush=True)
-
-
-def ring_of(cache, L: int, cap: int):
-    """A ring of `cap` rows holding positions [L - cap, L) of every sequence
-    at row p % cap (the same stored rows as the linear cache)."""
-    import torch
-    ring = torch.empty((cache.shape[0], cap) + tuple(cache.shape[2:]), dtype=cache.dtype, device=cache.device)
-    pos = torch.arange(max(0, L - cap), L, device=cache.device)
-    ring[:, pos % cap] = cache[:, pos]
-    if L < cap:
-        ring[:, L:] = 0
-    return ring
-
-
-def uses_ring(spec, ring: bool, synth) -> bool:
-    return ring and spec.kind == synth.SLIDING_ROPE
-
-
-class LayerRun:
-    def __init__(self, w, spec, copies, decode, fa, synth, ring=False):
-        import torch
-        self.spec = spec
-        self.inp = synth.layer_inputs(w, spec, device="cuda", backend="torch")
-        self.ring = uses_ring(spec, ring, synth) and decode
-        if self.ring:                                 # the window's rows only, as a ring
-            self.inp.cache_k = ring_of(self.inp.cache_k, w.prefix, spec.window)
-            self.inp.cache_v = ring_of(self.inp.cache_v, w.prefix, spec.window)
-        self.caches = [(self.inp.cache_k, self.inp.cache_v)]
-        for _ in range(1, copies):
-            self.caches.append((self.inp.cache_k.clone(), self.inp.cache_v.clone()))
-        self.layer = fa.make_layer(spec.kind, window=spec.window, rope_theta=spec.rope_theta,
-                                   rms_eps=spec.rms_eps, q_norm_gain=spec.q_gain,
-                                   k_norm_gain=spec.k_gain, attn_scale=spec.scale, dtype=w.dtype,
-                                   kv_ring=1 if self.ring else 0)
-        self.decode = decode
-        self.ws = fa.workspace(self.layer, w.n_seq, w.n_new, w.prefix, decode)
-        self.out = torch.empty_like(self.inp.gate)
-        self.max_seq_len = w.prefix
-
-    def call(self, fa, copy, timer=None):
-        ck, cv = self.caches[copy]
-        fn = fa.decode if self.decode else fa.prefill
-        fn(self.layer, self.inp.q, self.inp.k, self.inp.v, self.inp.gate, ck, cv, self.inp.seq_len,
-           self.out, max_seq_len=self.max_seq_len, workspace=self.ws, timer=timer)
-
-
-def run_timed(runs, steps, warmup, copies, fa, torch):
-    """W untimed steps, then K timed steps between synchronisations."""
-    from full_gqa_attention_amd.timing import KernelTimers
-    timers = KernelTimers(steps * len(runs))
-    for i in range(warmup):
-        for r in runs:
-            r.call(fa, i % copies)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        for j, r in enumerate(runs):
-            r.call(fa, (warmup + i) % copies, timers[i * len(runs) + j])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_launch = [timers.elapsed_ms(i) for i in range(len(timers))]
-    timers.close()
-    return wall, per_launch
-
-
-def run_graphs(runs, steps, warmup, copies, fa, torch):
-    """The same steps replayed from HIP graphs (one captured step per cache
-    copy): W untimed replays, then K timed ones between synchronisations.
-    Every kernel of every step still runs; the graph only removes the host's
-    per-call Python/ctypes cost from between the launches."""
-    graphs = []
-    for c in range(copies):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for r in runs:
-                r.call(fa, c)
-        graphs.append(g)
-    for i in range(warmup):
-        graphs[i % copies].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        graphs[(warmup + i) % copies].replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    del graphs
-    return wall
-
-
-def bench_decode(w, args, fa, synth, torch):
-    per_step_unique = sum(kv_row_bytes(w.dtype) * w.n_seq * visible_rows(s, w.prefix) for s in w.layers)
-    copies = max(1, -(-(2 * MALL_BYTES) // max(per_step_unique, 1)) + 1)
-    copies = min(copies, 8)
-    log(f"decode {w.name}: {len(w.layers)} layers, {copies} cache copies, "
-        f"{per_step_unique / 1e6:.1f} MB KV per step")
-    runs = [LayerRun(w, spec, copies, True, fa, synth, ring=args.ring) for spec in w.layers]
-    torch.cuda.synchronize()
-    wall_eager, per_launch = run_timed(runs, args.steps, args.warmup, copies, fa, torch)
-    wall = wall_eager if args.eager else run_graphs(runs, args.steps, args.warmup, copies, fa, torch)
-    kv_per_step = per_step_unique
-    ms_per_step = wall * 1e3 / args.steps
-    launches = len(per_launch)
-    avg_launch_ms = sum(per_launch) / launches
-    bytes_per_launch = kv_per_step / len(runs)
-    achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
-    per_layer = {}
-    for j, r in enumerate(runs):
-        lt = per_launch[j::len(runs)]
-        b = kv_row_bytes(w.dtype) * w.n_seq * visible_rows(r.spec, w.prefix)
-        per_layer[r.spec.name] = {"kernel_us": round(1e3 * sum(lt) / len(lt), 2),
-                                  "kv_MB": round(b / 1e6, 3),
-                                  "kernel_GBps": round(b / (sum(lt) / len(lt) * 1e-3) / 1e9, 1),
-                                  "p10_p50_p90_us": [round(1e3 * x, 2) for x in percentiles(lt)]}
-    res = {
-        "value": kv_per_step / (ms_per_step * 1e-3) / 1e9,
-        "ms_per_step": ms_per_step,
-        "eager": {"value": round(kv_per_step * args.steps / wall_eager / 1e9, 1),
-                  "ms_per_step": round(wall_eager * 1e3 / args.steps, 5),
-                  "note": "same steps launched one call at a time from Python, with per-kernel events"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": counter_traffic() if w.name == "decode_64x8192_bf16" else None,
-                     "kernel": "muse::decode_kernel<bf16>" if w.dtype == 1 else "muse::decode_kernel<f32>",
-                     "launches": launches, "avg_launch_us": round(avg_launch_ms * 1e3, 2),
-                     "algorithmic_bytes_per_launch": int(bytes_per_launch),
-                     "per_layer": per_layer},
-        "config": {"workload": w.name, "n_seq": w.n_seq, "cached_tokens": w.prefix, "new_tokens": 1,
-                   "layers": [f"{s.name}" + (f"_w{s.window}_theta{int(s.rope_theta)}" if s.window else "_nope")
-                              for s in w.layers],
-                   "q_heads": 32, "kv_heads": 2, "head_dim": 128, "cache_copies": copies,
-                   "kv_bytes_per_step": kv_per_step, "kv_ring_sliding": bool(args.ring)},
-    }
-    return res, runs
-
-
-def bench_prefill(w, steps, warmup, fa, synth, torch):
-    log(f"prefill {w.name}: {len(w.layers)} layers")
-    runs = [LayerRun(w, spec, 1, False, fa, synth) for spec in w.layers]
-    torch.cuda.synchronize()
-    wall, per_launch = run_timed(runs, steps, warmup, 1, fa, torch)
-    flops_step = sum(FLOP_PER_PAIR * w.n_seq * prefill_pairs(s, w.prefix, w.n_new) for s in w.layers)
-    ms_per_step = wall * 1e3 / steps
-    per_layer = {}
-    for j, r in enumerate(runs):
-        lt = per_launch[j::len(runs)]
-        f = FLOP_PER_PAIR * w.n_seq * prefill_pairs(r.spec, w.prefix, w.n_new)
-        avg = sum(lt) / len(lt)
-        per_layer[r.spec.name] = {"kernel_ms": round(avg, 4), "tflop": round(f / 1e12, 4),
-                                  "kernel_TFLOPs": round(f / (avg * 1e-3) / 1e12, 1),
-                                  "p10_p50_p90_ms": [round(x, 4) for x in percentiles(lt)]}
-    kern = sum(per_launch) / len(per_launch)
-    achieved = flops_step / len(runs) / (kern * 1e-3) / 1e12
-    return {
-        "workload": w.name,
-        "tflops": round(flops_step / (ms_per_step * 1e-3) / 1e12, 2),
-        "ms_per_step": round(ms_per_step, 4),
-        "frac_mfma_peak": round(flops_step / (ms_per_step * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "muse::prefill_group_kernel<1, 8, 1, false> (bf16)", "avg_launch_ms": round(kern, 4),
-                     "per_layer": per_layer,
-                     "counters": prefill_counters() if w.name == "prefill_8x8192_bf16" else None},
-        "flop_per_step": flops_step, "steps": steps, "warmup": warmup,
-    }
-
-
-def bench_schedule(w, fa, synth, torch, ring=False):
-    """The 52-layer schedule workload: 4 sequences with 32,768 cached rows per
-    layer, a 4,096-token chunked prefill through all 52 layers (timed as one
-    phase, eager calls), then 256 decode steps of all 52 layers (one step =
-    52 decode calls and the seq_len increment, replayed from a HIP graph).
-    ring: the sliding layers keep their window in a ring of `window` rows."""
-    S, L0, N, steps = w.n_seq, w.prefix, w.n_new, w.decode_steps
-    extra = 4                                          # warm-up decode steps, rows overwritten later
-    cap = L0 + N + steps + extra
-    max_dec = L0 + N + steps + extra - 1
-    log(f"schedule {w.name}: {len(w.layers)} layers, capacity {cap}")
-    layers, inputs, outs, dec_in = [], [], [], []
-    for spec in w.layers:
-        r = uses_ring(spec, ring, synth)
-        inp = synth.layer_inputs(w, spec, device="cuda", backend="torch",
-                                 capacity=L0 if r else cap)
-        if r:
-            inp.cache_k = ring_of(inp.cache_k, L0, spec.window)
-            inp.cache_v = ring_of(inp.cache_v, L0, spec.window)
-        layers.append(fa.make_layer(spec.kind, window=spec.window, rope_theta=spec.rope_theta,
-                                    rms_eps=spec.rms_eps, q_norm_gain=spec.q_gain,
-                                    k_norm_gain=spec.k_gain, attn_scale=spec.scale, dtype=w.dtype,
-                                    kv_ring=1 if r else 0))
-        inputs.append(inp)
-        outs.append(torch.empty_like(inp.gate))
-        d = synth.layer_inputs(w, spec, device="cuda", backend="torch", n_new=1, prefix=0,
-                               step=1, with_cache=False)
-        dec_in.append((d.q, d.k, d.v, d.gate, torch.empty_like(d.gate)))
-    seq_len = torch.full((S,), L0, dtype=torch.int32, device="cuda")
-    ws_p = torch.empty(max(fa.workspace_size(lay, S, N, L0, False) for lay in layers),
-                       dtype=torch.uint8, device="cuda")
-    ws_d = torch.empty(max(fa.workspace_size(lay, S, 1, max_dec, True) for lay in layers),
-                       dtype=torch.uint8, device="cuda")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for lay, inp, out in zip(layers, inputs, outs):
-        fa.prefill(lay, inp.q, inp.k, inp.v, inp.gate, inp.cache_k, inp.cache_v, seq_len, out,
-                   max_seq_len=L0, workspace=ws_p)
-    torch.cuda.synchronize()
-    t_prefill = time.perf_counter() - t0
-    flops = sum(FLOP_PER_PAIR * S * prefill_pairs(spec, L0, N) for spec in w.layers)
-    seq_len.fill_(L0 + N)
-
-    def one_step():
-        for lay, inp, (q, k, v, g, o) in zip(layers, inputs, dec_in):
-            fa.decode(lay, q, k, v, g, inp.cache_k, inp.cache_v, seq_len, o, max_seq_len=max_dec,
-                      workspace=ws_d)
-        seq_len.add_(1)
-
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        one_step()
-    for _ in range(extra):
-        graph.replay()
-    torch.cuda.synchronize()
-    seq_len.fill_(L0 + N)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    t_decode = time.perf_counter() - t0
-    kv = sum(kv_row_bytes(w.dtype) * S * visible_rows(spec, L0 + N + i)
-             for i in range(steps) for spec in w.layers)
-    del graph
-    cache_bytes = sum(2 * inp.cache_k.numel() * inp.cache_k.element_size() for inp in inputs)
-    return {"workload": w.name, "layers": len(w.layers), "n_seq": S,
-            "kv_ring_sliding": bool(ring), "kv_cache_GB": round(cache_bytes / 1e9, 3),
-            "prefill": {"tokens_per_seq": N, "at_position": L0, "ms": round(t_prefill * 1e3, 2),
-                        "tflop": round(flops / 1e12, 3), "TFLOPs": round(flops / t_prefill / 1e12, 1),
-                        "frac_mfma_peak": round(flops / t_prefill / 1e12 / MFMA_PEAK_TFLOPS, 4),
-                        "launch": "eager"},
-            "decode": {"steps": steps, "ms": round(t_decode * 1e3, 2), "kv_GB": round(kv / 1e9, 2),
-                       "GBps": round(kv / t_decode / 1e9, 1),
-                       "frac_hbm_peak": round(kv / t_decode / 1e9 / HBM_PEAK_GBS, 4),
-                       "launch": "each step (52 decode calls + seq_len increment) replayed from a HIP graph"}}
 
 
 def bench_verify(fa, synth, torch, steps=20, warmup=3, n_new=16):
@@ -554,6 +715,7 @@ def bench_verify(fa, synth, torch, steps=20, warmup=3, n_new=16):
                          "kernel": "muse::verify_kernel + muse::verify_merge_kernel (bf16)",
                          "per_layer": per_layer},
             "steps": steps, "warmup": warmup}
+
 
 
 def bench_out_proj(fa, synth, torch, steps=10, warmup=3):
@@ -601,6 +763,7 @@ def bench_out_proj(fa, synth, torch, steps=10, warmup=3):
     return res
 
 
+
 def bench_relocate(fa, synth, torch, steps=10):
     """NoPE tile relocation ("Chapter 14 - QK-norm and RoPE" 14.6): the whole
     cache of a full layer of the 64 x 8,192 decode workload, moved as 512-row
@@ -638,40 +801,6 @@ def bench_relocate(fa, synth, torch, steps=10):
             "frac_hbm_peak": round(2 * moved / dt / 1e9 / HBM_PEAK_GBS, 4), "bytes_checked": ok}
 
 
-def cpu_baseline_decode(w, runs, synth, torch):
-    """Time the CPU oracle on this step's inputs (all rows of both layers) and
-    check the benchmarked GPU output against it."""
-    import numpy as np
-    import oracle
-    rows = oracle.all_rows(w.n_seq, 1)
-    t_oracle = 0.0
-    worst = 0.0
-    ok = True
-    for r in runs:
-        ck, cv = r.caches[0]
-        pk, pv = synth.to_storage_numpy(ck), synth.to_storage_numpy(cv)   # rows < seq_len untouched
-        lay = oracle.Layer(kind=r.spec.kind, window=r.spec.window, rope_theta=r.spec.rope_theta,
-                           rms_eps=r.spec.rms_eps, q_gain=r.spec.q_gain, k_gain=r.spec.k_gain,
-                           scale=r.spec.scale, dtype=w.dtype)
-        args = (lay, r.inp.seq_len.cpu().numpy(), synth.to_storage_numpy(r.inp.k),
-                synth.to_storage_numpy(r.inp.v), pk, pv, rows,
-                synth.to_storage_numpy(r.inp.q).reshape(-1, 32, 128),
-                synth.to_storage_numpy(r.inp.gate).reshape(-1, 4096))
-        t0 = time.perf_counter()
-        ref = oracle.attn_rows(*args)
-        t_oracle += time.perf_counter() - t0
-        got = r.out.double().cpu().numpy().reshape(-1, 4096)
-        err = np.abs(got - ref)
-        worst = max(worst, float(err.max()))
-        ok = ok and bool(np.all(err <= 2e-2 + 1e-2 * np.abs(ref)))
-    kv = sum(kv_row_bytes(w.dtype) * w.n_seq * visible_rows(r.spec, w.prefix) for r in runs)
-    return {"value": round(kv / t_oracle / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"the whole step: {w.n_seq} sequences x {len(runs)} layers, all 32 heads "
-                      f"({t_oracle:.2f} s)",
-            "seconds": round(t_oracle, 3)}, {"max_abs_err": worst, "within_tolerance": ok}
-
-
 def main():
     args = parse()
     if args.summarize_trace:
@@ -701,35 +830,69 @@ def main():
         torch.cuda.synchronize()
         del a, b
     if args.prefill_only:
-        pw = synth.WORKLOADS[args.prefill_workload]
-        print(json.dumps({"prefill": bench_prefill(pw, args.prefill_steps, 2, fa, synth, torch)}), flush=True)
+        pw = synth.WORKLOADS["prefill_8x8192_bf16"]
+        print(json.dumps({"prefill": leg_prefill(pw, fa, synth, torch, steps=5, cpu=False)}), flush=True)
         return
-    w = synth.WORKLOADS[args.workload]
-    if not w.is_decode:
-        print(f"--workload must be a decode workload, got {w.name}", file=sys.stderr)
-        sys.exit(2)
-    res, runs = bench_decode(w, args, fa, synth, torch)
+    if args.counters_run:
+        from full_gqa_attention_amd.schedule import Schedule
+        sch = Schedule(synth.WORKLOADS[HEADLINE], ring=args.ring)
+        sch.prefill()
+        sch.start_decode()
+        for _ in range(2):
+            sch.decode_step()
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_run": HEADLINE, "decode_steps": 2}), flush=True)
+        return
+
+    res, sch = bench_schedule(args, fa, synth, torch)
+    K = res["steps"]
     line = {
         "metric": METRIC, "value": round(res["value"], 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == 1 else "f32",
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic: seeded N(0,1) inputs and cache prefixes, resident in HBM",
         "config": res["config"], "roofline": res["roofline"],
         "frac_hbm_peak": round(res["value"] / HBM_PEAK_GBS, 4),
-        "launch": "eager calls" if args.eager else "each step replayed from a HIP graph of its kernel launches",
-        "eager": res["eager"],
+        "launch": "each decode step (52 layers' decode calls, then the seq_len increment) replayed from a HIP graph",
+        "prefill": res["prefill"],
     }
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on the same step")
-        cb, parity = cpu_baseline_decode(w, runs, synth, torch)
-        line["cpu_baseline"] = cb
-        line["parity"] = parity
-    del runs
+    if not args.no_cpu_baseline and not args.ring:
+        import oracle
+        log("timing the CPU oracle on a sample of the schedule")
+        cs = cpu_schedule_sample(sch, fa, synth, torch)
+        w = sch.w
+        total_pairs = sum(w.n_seq * prefill_pairs(s, w.prefix, w.n_new) for s in sch.specs)
+        total_kv = sum(kv_row_bytes(w.dtype) * w.n_seq * visible_rows(s, w.prefix + w.n_new + i)
+                       for i in range(w.decode_steps) for s in sch.specs)
+        line["cpu_baseline"] = {
+            "value": round(cs["decode_kv"] / cs["decode_s"] / 1e9, 4), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "decode: the first 4 decode steps of all 52 layers, 4 sequences, all 32 heads "
+                      f"({cs['decode_kv'] / 1e9:.2f} GB of KV rows, {cs['decode_s']:.2f} s); prefill: 2 chunk rows "
+                      f"per layer ({cs['prefill_pairs']} visible pairs, {cs['prefill_s']:.2f} s)",
+            "seconds": round(cs["decode_s"] + cs["prefill_s"], 3),
+            "prefill_tflops": round(cs["prefill_pairs"] * FLOP_PER_PAIR / max(cs["prefill_s"], 1e-9) / 1e12, 6),
+            "extrapolated_full_run_s": {
+                "chunked_prefill": round(cs["prefill_s"] * total_pairs / max(cs["prefill_pairs"], 1), 1),
+                "decode_256_steps": round(cs["decode_s"] * total_kv / cs["decode_kv"], 1),
+                "note": "extrapolation: sample time x the workload's visible pairs (or KV bytes) / the sample's"}}
+        line["parity"] = cs["parity"]
+    del sch
     torch.cuda.empty_cache()
-    if not args.no_prefill:
-        pw = synth.WORKLOADS[args.prefill_workload]
-        line["prefill"] = bench_prefill(pw, args.prefill_steps, 2, fa, synth, torch)
+    if not args.no_configs:
+        cpu = not args.no_cpu_baseline
+        legs = {}
+        import numpy as np
+        w1 = synth.WORKLOADS["prefill_1x512_f32"]
+        legs[w1.name] = leg_prefill(w1, fa, synth, torch, steps=20, cpu=cpu, single_core=True)
+        legs["decode_64x8192_bf16"] = leg_decode(synth.WORKLOADS["decode_64x8192_bf16"], fa, synth, torch, cpu=cpu)
+        w3 = synth.WORKLOADS["prefill_8x8192_bf16"]
+        edges = sorted({0, 1, 63, 64, 127, 128, 2046, 2047, 2048, 2049, 4095, 8191})
+        rows3 = np.array([(s, t) for s in (0, 7) for t in edges], np.int32)
+        legs[w3.name] = leg_prefill(w3, fa, synth, torch, steps=5, cpu=cpu, cpu_rows=rows3)
+        legs["decode_16x131072_bf16"] = leg_decode(synth.WORKLOADS["decode_16x131072_bf16"], fa, synth, torch,
+                                                   steps=10, cpu=cpu)
+        line["configs"] = legs
     if args.verify:
         torch.cuda.empty_cache()
         line["verify"] = bench_verify(fa, synth, torch)
@@ -739,10 +902,6 @@ def main():
     if args.relocate:
         torch.cuda.empty_cache()
         line["relocate"] = bench_relocate(fa, synth, torch)
-    if args.schedule:
-        torch.cuda.empty_cache()
-        line["schedule"] = bench_schedule(synth.WORKLOADS["schedule_52x4_32768p4096_256d"], fa, synth, torch,
-                                          ring=args.ring)
     print(json.dumps(line), flush=True)
 
 

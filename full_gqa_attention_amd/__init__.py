@@ -154,11 +154,15 @@ def workspace_size(layer: Layer, n_seq: int, n_new: int, max_seq_len: int, decod
     return n.value
 
 
+def workspace_buffer(nbytes: int, device="cuda") -> torch.Tensor:
+    """A byte tensor of at least `nbytes` (never empty, so it has an address)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
 def workspace(layer: Layer, n_seq: int, n_new: int, max_seq_len: int, decode: bool,
               device="cuda") -> torch.Tensor:
     """A byte tensor large enough for one call."""
-    return torch.empty(max(workspace_size(layer, n_seq, n_new, max_seq_len, decode), 1),
-                       dtype=torch.uint8, device=device)
+    return workspace_buffer(workspace_size(layer, n_seq, n_new, max_seq_len, decode), device)
 
 
 # ------------------------------------------------------------------ calls

@@ -553,7 +553,7 @@ void decode_kernel(DecodeArgs a) {
 // order, so the result does not depend on how the split workgroups were
 // scheduled.
 constexpr int kMergeWaves = 4;                         // heads per merge workgroup
-constexpr int kMergeBatch = 16;                        // O rows in flight per lane
+constexpr int kMergeBatch = 16;                        // O rows in flight per lane (16 measured faster than 32 or 64)
 template <typename T>
 __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeArgs a) {
     constexpr int D = kHeadDim, B = kMergeBatch, R = kMaxSplits / 64;
@@ -640,13 +640,15 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream) {
         hipLaunchKernelGGL((decode_kernel<bf16_t, kDecodeDepth, kDecodeWaves>), grid, block, 0, stream, a);
     else
         hipLaunchKernelGGL((decode_kernel<float, 2, kDecodeWaves>), grid, block, 0, stream, a);
-    if (a.nsplit > 1) {
-        const dim3 mgrid((unsigned)(a.n_seq * kHeads / kMergeWaves)), mblock(64 * kMergeWaves);
-        if (dtype == 1)
-            hipLaunchKernelGGL(decode_merge_kernel<bf16_t>, mgrid, mblock, 0, stream, a);
-        else
-            hipLaunchKernelGGL(decode_merge_kernel<float>, mgrid, mblock, 0, stream, a);
-    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const DecodeArgs& a, int dtype, hipStream_t stream) {
+    const dim3 grid((unsigned)(a.n_seq * kHeads / kMergeWaves)), block(64 * kMergeWaves);
+    if (dtype == 1)
+        hipLaunchKernelGGL(decode_merge_kernel<bf16_t>, grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL(decode_merge_kernel<float>, grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

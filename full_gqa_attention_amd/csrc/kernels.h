@@ -175,6 +175,7 @@ int prefill_grid(int n_seq, int n_new);
 hipError_t launch_prep(const PrepArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_prefill(const AttnArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeArgs& a, int dtype, hipStream_t stream);   // when nsplit > 1
 hipError_t launch_relocate(const RelocArgs& a, hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_verify_merge(const VerifyArgs& a, hipStream_t stream);

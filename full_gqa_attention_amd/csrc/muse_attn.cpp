@@ -278,6 +278,7 @@ muse_status run(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new, cons
         if (timer && hipEventRecord(timer->start, stream) != hipSuccess) return MUSE_ERR_HIP;
         if (muse::launch_decode(da, dt, stream) != hipSuccess) return MUSE_ERR_HIP;
         if (timer && hipEventRecord(timer->stop, stream) != hipSuccess) return MUSE_ERR_HIP;
+        if (da.nsplit > 1 && muse::launch_decode_merge(da, dt, stream) != hipSuccess) return MUSE_ERR_HIP;
         return MUSE_OK;
     }
 

@@ -177,7 +177,7 @@ muse_status muse_attn_prefill(const muse_attn_layer* layer, int32_t n_seq, int32
  * n_new = 1 (q [n_seq][1][32][128], etc.).  With more than one split per
  * (sequence, KV head) the splits store their partial (max, sum, output) in
  * the workspace and a second kernel on the same stream merges them in split
- * order and applies the gate; the timer then spans both kernels.  The
+ * order and applies the gate (the timer brackets the first kernel only).  The
  * workspace holds nothing between calls (contents on entry are ignored), but
  * calls that may run at the same time must not share one.  When
  * muse_attn_workspace_size reports 0 bytes (one split), workspace may be

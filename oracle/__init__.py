@@ -90,6 +90,8 @@ def _load():
         lib.oracle_layer_kind.argtypes = [ctypes.c_int]
         lib.oracle_layer_kind.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
         lib.oracle_round_bf16.argtypes = [ctypes.c_double]
         lib.oracle_round_bf16.restype = ctypes.c_double
         lib.oracle_round_store.argtypes = [ctypes.c_double, ctypes.c_int]
@@ -135,6 +137,11 @@ def layer_kind(layer: int) -> int:
 
 def num_threads() -> int:
     return _load().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's later calls use (OpenMP)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def round_bf16(x: float) -> float:

@@ -66,6 +66,15 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads the following calls use (n >= 1; for timing the oracle on one core). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Value of a bf16 bit pattern (bf16 is the top half of an IEEE f32). */
 static double bf16_bits_to_double(uint16_t b) {
     uint32_t u = ((uint32_t)b) << 16;

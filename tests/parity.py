@@ -89,27 +89,31 @@ def bf16_neighbours_ok(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
     return np.abs((g >> 16) - (r >> 16)) <= 1
 
 
+def check_rows(gk: np.ndarray, gv: np.ndarray, kst: np.ndarray, vst: np.ndarray, dtype: int, what: str):
+    """Stored cache rows (gk, gv: the GPU's, as float64) against the oracle's
+    K-hat and V rows (kst, vst): V bit-exact, K as the module docstring says."""
+    assert np.array_equal(gv, vst), f"{what}: V rows differ"
+    scale = np.max(np.abs(kst), axis=-1, keepdims=True)
+    if dtype == synth.F32:
+        # a few f32 roundings of values bounded by the head's largest entry
+        assert np.all(np.abs(gk - kst) <= 1e-6 * scale), f"{what}: K rows differ"
+        return
+    # one bf16 ulp apart, or (entries that rotation cancels towards zero,
+    # where an ulp is tiny) within the f32 pipeline's absolute error of 2e-6
+    # of the head vector's largest entry
+    ok = bf16_neighbours_ok(gk, kst) | (np.abs(gk - kst) <= 2e-6 * scale)
+    if not np.all(ok):
+        i = tuple(np.argwhere(~ok)[0])
+        raise AssertionError(f"{what}: {int((~ok).sum())} K entries off, first at {i}: gpu {gk[i]!r} "
+                             f"oracle {kst[i]!r} row max {scale[i[:-1]]}")
+
+
 def check_appended(inp: synth.LayerInputs, kst, vst, seq_len, dtype: int, n_new: int):
     """The cache rows [L_s, L_s + n_new) hold the oracle's stored K-hat and V."""
     for s in range(kst.shape[0]):
         L = int(seq_len[s])
-        gk = to_f64(inp.cache_k[s, L:L + n_new])
-        gv = to_f64(inp.cache_v[s, L:L + n_new])
-        assert np.array_equal(gv, vst[s]), f"V rows of sequence {s} differ"
-        if dtype == synth.F32:
-            # a few f32 roundings of values bounded by the head's largest entry
-            scale = np.max(np.abs(kst[s]), axis=-1, keepdims=True)
-            assert np.all(np.abs(gk - kst[s]) <= 1e-6 * scale), f"K rows of {s}"
-        else:
-            # one bf16 ulp apart, or (entries that rotation cancels towards
-            # zero, where an ulp is tiny) within the f32 pipeline's absolute
-            # error of 2e-6 of the head vector's largest entry
-            scale = np.max(np.abs(kst[s]), axis=-1, keepdims=True)
-            ok = bf16_neighbours_ok(gk, kst[s]) | (np.abs(gk - kst[s]) <= 2e-6 * scale)
-            if not np.all(ok):
-                i = tuple(np.argwhere(~ok)[0])
-                raise AssertionError(f"K rows of sequence {s}: {int((~ok).sum())} entries off, first "
-                                     f"at {i}: gpu {gk[i]!r} oracle {kst[s][i]!r} row max {scale[i[:-1]]}")
+        check_rows(to_f64(inp.cache_k[s, L:L + n_new]), to_f64(inp.cache_v[s, L:L + n_new]),
+                   kst[s], vst[s], dtype, f"appended rows of sequence {s}")
 
 
 def host_cache(inp: synth.LayerInputs, seqs=None):
