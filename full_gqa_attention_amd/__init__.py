@@ -29,7 +29,7 @@ STATUS = {0: "MUSE_OK", 1: "MUSE_ERR_NULL", 2: "MUSE_ERR_SHAPE", 3: "MUSE_ERR_LA
           4: "MUSE_ERR_CAPACITY", 5: "MUSE_ERR_WORKSPACE", 6: "MUSE_ERR_DTYPE",
           7: "MUSE_ERR_HIP", 8: "MUSE_ERR_ALIGN", 9: "MUSE_ERR_ALIAS"}
 
-EXPORTS = ("muse_attn_prefill", "muse_attn_decode", "muse_attn_workspace_size",
+EXPORTS = ("muse_attn_prefill", "muse_attn_decode", "muse_attn_decode_noalloc", "muse_attn_workspace_size",
            "muse_attn_layer_init", "muse_layer_kind_for", "muse_rope_theta_table",
            "muse_status_str", "muse_kv_relocate", "muse_out_proj", "muse_out_proj_workspace_size")
 
@@ -87,6 +87,9 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(KvCache), vp, vp, sz, vp,
                                        ctypes.POINTER(KernelTimer)]
         L.muse_attn_decode.restype = ctypes.c_int
+        L.muse_attn_decode_noalloc.argtypes = [lp, i32, vp, i32, vp, vp, vp, vp,
+                                               ctypes.POINTER(KvCache), vp, vp, ctypes.POINTER(KernelTimer)]
+        L.muse_attn_decode_noalloc.restype = ctypes.c_int
         L.muse_attn_workspace_size.argtypes = [lp, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.muse_attn_workspace_size.restype = ctypes.c_int
         L.muse_attn_layer_init.argtypes = [lp, i32, i32]
@@ -255,6 +258,41 @@ def decode(layer: Layer, q, k, v, gate, cache_k, cache_v, seq_len, out=None, *,
         max_seq_len = cache_k.shape[1] - 1
     return _call(True, layer, q, k, v, gate, cache_k, cache_v, seq_len, out, max_seq_len,
                  workspace, stream, timer)
+
+
+def decode_noalloc(layer: Layer, q, k, v, gate, cache_k, cache_v, seq_len, out=None, *,
+                   max_seq_len: Optional[int] = None, stream=None,
+                   timer: Optional[KernelTimer] = None) -> torch.Tensor:
+    """muse_attn_decode_noalloc on torch tensors: muse_attn_decode with the
+    library's static scratch instead of a workspace argument."""
+    dt = _TORCH.get(layer.dtype)
+    if dt is None:
+        raise MuseError(6, "layer.dtype")
+    S = q.shape[0]
+    if out is None:
+        out = torch.empty(gate.shape, dtype=gate.dtype, device=gate.device)
+    if max_seq_len is None:
+        if layer.kv_ring:
+            raise ValueError("a kv_ring layer needs max_seq_len (positions outgrow the ring)")
+        max_seq_len = cache_k.shape[1] - 1
+    _expect(q, "q", (S, 1, N_HEADS, HEAD_DIM), dt)
+    _expect(k, "k", (S, 1, N_KV_HEADS, HEAD_DIM), dt)
+    _expect(v, "v", (S, 1, N_KV_HEADS, HEAD_DIM), dt)
+    _expect(gate, "gate", (S, 1, ATTN_DIM), dt)
+    _expect(out, "out", (S, 1, ATTN_DIM), dt)
+    _expect(cache_k, "cache_k", None, dt)
+    _expect(cache_v, "cache_v", tuple(cache_k.shape), dt)
+    if cache_k.dim() != 4 or cache_k.shape[0] != S or tuple(cache_k.shape[2:]) != (N_KV_HEADS, HEAD_DIM):
+        raise ValueError("cache_k/cache_v must be [n_seq, capacity, 2, 128]")
+    _expect(seq_len, "seq_len", (S,), torch.int32)
+    cache = KvCache(cache_k.data_ptr(), cache_v.data_ptr(), cache_k.shape[1])
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    tptr = ctypes.byref(timer) if timer is not None else None
+    rc = lib().muse_attn_decode_noalloc(ctypes.byref(layer), S, _ptr(seq_len), max_seq_len, _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(gate), ctypes.byref(cache), _ptr(out), ctypes.c_void_p(stream), tptr)
+    _check(rc, "muse_attn_decode_noalloc")
+    return out
 
 
 def kv_tiles(tiles):

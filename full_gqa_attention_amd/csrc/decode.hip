@@ -38,6 +38,7 @@
 // output; otherwise each split stores its partial and decode_merge_kernel,
 // the next launch on the stream, merges the splits in split order.  Splits
 // that would cover no row of a shorter sequence exit at once.
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
@@ -632,6 +633,32 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeAr
     const float inv = 1.0f / den;
     out[0] = from_f32<T>(acc0 * inv * sigmoid(g0));
     out[1] = from_f32<T>(acc1 * inv * sigmoid(g1));
+}
+
+// The allocation-free decode's scratch: split partials in a file-scope
+// device array (each GPU the library runs on holds its own copy until the
+// process ends).  Host code never passes `scratch` itself to a kernel (on the
+// host the name is only a stand-in): its device address is resolved once per
+// device with hipGetSymbolAddress and that address is used.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* per_device[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!per_device[dev]) {                            // first call on this device, which is current
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        per_device[dev] = p;
+    }
+    *ptr = per_device[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream) {

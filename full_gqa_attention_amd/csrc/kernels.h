@@ -175,6 +175,10 @@ int prefill_grid(int n_seq, int n_new);
 hipError_t launch_prep(const PrepArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_prefill(const AttnArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
+// Device address of the allocation-free decode's scratch on the current
+// device (kDecodeScratchBytes), resolved on the first call per device.
+constexpr size_t kDecodeScratchBytes = (size_t)4 << 20;
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_decode_merge(const DecodeArgs& a, int dtype, hipStream_t stream);   // when nsplit > 1
 hipError_t launch_relocate(const RelocArgs& a, hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);

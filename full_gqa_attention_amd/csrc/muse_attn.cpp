@@ -408,6 +408,22 @@ muse_status muse_attn_decode(const muse_attn_layer* layer, int32_t n_seq,
                workspace_bytes, stream, timer, true);
 }
 
+muse_status muse_attn_decode_noalloc(const muse_attn_layer* layer, int32_t n_seq,
+                                     const int32_t* seq_len, int32_t max_seq_len,
+                                     const void* q, const void* k, const void* v, const void* gate,
+                                     const muse_kv_cache* cache, void* out,
+                                     hipStream_t stream, const muse_kernel_timer* timer) {
+    muse_status st = check_layer(layer);
+    if (st != MUSE_OK) return st;
+    if ((st = check_sizes(n_seq, 1, max_seq_len)) != MUSE_OK) return st;
+    if (layout_for(layer, n_seq, 1, max_seq_len, true).total > muse::kDecodeScratchBytes)
+        return MUSE_ERR_WORKSPACE;                     // the split partials exceed the library's scratch
+    void* ws = nullptr;
+    if (n_seq > 0 && muse::decode_scratch(&ws) != hipSuccess) return MUSE_ERR_HIP;
+    return run(layer, n_seq, 1, seq_len, max_seq_len, q, k, v, gate, cache, out, ws, muse::kDecodeScratchBytes,
+               stream, timer, true);
+}
+
 muse_status muse_attn_workspace_size(const muse_attn_layer* layer, int32_t n_seq, int32_t n_new,
                                      int32_t max_seq_len, int32_t is_decode, size_t* bytes) {
     if (!bytes) return MUSE_ERR_NULL;

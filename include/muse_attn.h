@@ -190,6 +190,24 @@ muse_status muse_attn_decode(const muse_attn_layer* layer, int32_t n_seq,
                              void* workspace, size_t workspace_bytes,
                              hipStream_t stream, const muse_kernel_timer* timer);
 
+/*
+ * Decode without a caller-supplied workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The same computation and kernels as
+ * muse_attn_decode; the split partials go to a static device array of the
+ * library, 4 MiB per GPU (every decode of up to 126 sequences fits; a call
+ * whose muse_attn_workspace_size exceeds 4 MiB returns MUSE_ERR_WORKSPACE
+ * and enqueues nothing).  Allocates nothing: its first call on a device (the
+ * current one) looks up that device's copy of the array.  All calls on one
+ * GPU share the array, so calls that may overlap on a GPU (other streams,
+ * other threads) race and must not be issued.
+ */
+muse_status muse_attn_decode_noalloc(const muse_attn_layer* layer, int32_t n_seq,
+                                     const int32_t* seq_len, int32_t max_seq_len,
+                                     const void* q, const void* k, const void* v, const void* gate,
+                                     const muse_kv_cache* cache, void* out,
+                                     hipStream_t stream, const muse_kernel_timer* timer);
+
 /* One tile of cache rows to relocate: rows [src_pos, src_pos + n_rows) of
  * sequence src_seq go to rows [dst_pos, dst_pos + n_rows) of sequence
  * dst_seq. */

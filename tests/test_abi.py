@@ -351,3 +351,25 @@ def test_decode_workspace_zero_for_one_split(lib):
     assert n.value == 0
     assert lib.muse_attn_workspace_size(ctypes.byref(lay), 4, 1, 8192, 1, ctypes.byref(n)) == 0
     assert n.value > 0
+
+
+def test_decode_noalloc_refuses_beyond_its_scratch(lib):
+    """The allocation-free decode keeps its split partials in a 4 MiB static
+    array: a call needing more (127 sequences, 2 splits each: 4.23 MB) is
+    refused before anything is enqueued; 126 sequences would fit."""
+    lay = fa.make_layer(fa.FULL_NOPE, dtype=fa.BF16)
+    n = ctypes.c_size_t()
+    assert lib.muse_attn_workspace_size(ctypes.byref(lay), 127, 1, 200, 1, ctypes.byref(n)) == 0
+    assert n.value > 4 << 20
+    assert lib.muse_attn_workspace_size(ctypes.byref(lay), 126, 1, 200, 1, ctypes.byref(n)) == 0
+    assert n.value <= 4 << 20
+    f = Fake(decode=True, kind=fa.FULL_NOPE)
+    f.n_seq, f.max_seq_len = 127, 200
+    vp = ctypes.c_void_p
+    rc = lib.muse_attn_decode_noalloc(ctypes.byref(f.layer), f.n_seq, vp(f.seq_len), f.max_seq_len, vp(f.q),
+                                      vp(f.k), vp(f.v), vp(f.gate), ctypes.byref(f.cache), vp(f.out), None, None)
+    assert rc == WORKSPACE
+    f.layer.n_heads = 16                               # and the layer checks come first
+    rc = lib.muse_attn_decode_noalloc(ctypes.byref(f.layer), f.n_seq, vp(f.seq_len), f.max_seq_len, vp(f.q),
+                                      vp(f.k), vp(f.v), vp(f.gate), ctypes.byref(f.cache), vp(f.out), None, None)
+    assert rc == SHAPE
