@@ -145,20 +145,23 @@ def summarize_counters(fetch_csv: str, write_csv: str, out: str, command: str):
         v = [x for x, k in zip(xs, kinds) if kind in (k, "all")]
         return sum(v) / len(v)
 
+    mk = ["full" if i % 52 % 4 == 3 else "sliding" for i in range(len(fm))]
+
+    def mavg(xs, kind):
+        v = [x for x, k in zip(xs, mk) if kind in (k, "all")]
+        return sum(v) / len(v)
+
     rows, vals = [], {}
     for kind in ("sliding", "full", "all"):
         fb = avg(fd, kind) * 1024 * FETCH_SCALE
         wb = avg(wd, kind) * 1024 * WRITE_SCALE
-        vals[kind] = fb + wb
         rows.append(f"| decode_kernel, {kind} | {avg(fd, kind):.1f} | {avg(wd, kind):.1f} | {fb / 1e6:.2f} | "
                     f"{wb / 1e6:.3f} |")
-    mk = ["full" if i % 52 % 4 == 3 else "sliding" for i in range(len(fm))]
-    for kind in ("sliding", "full"):
-        v = [x for x, k in zip(fm, mk) if k == kind]
-        u = [x for x, k in zip(wm, mk) if k == kind]
-        if v:
-            rows.append(f"| decode_merge_kernel, {kind} | {sum(v) / len(v):.1f} | {sum(u) / len(u):.1f} | "
-                        f"{sum(v) / len(v) * 1024 * FETCH_SCALE / 1e6:.2f} | {sum(u) / len(u) * 1024 * WRITE_SCALE / 1e6:.3f} |")
+        mf = mavg(fm, kind) * 1024 * FETCH_SCALE
+        mw = mavg(wm, kind) * 1024 * WRITE_SCALE
+        rows.append(f"| decode_merge_kernel, {kind} | {mavg(fm, kind):.1f} | {mavg(wm, kind):.1f} | "
+                    f"{mf / 1e6:.2f} | {mw / 1e6:.3f} |")
+        vals[kind] = fb + wb + mf + mw                 # one decode call: the split kernel and the merge kernel
     lines = ["# HBM traffic of the decode kernels: 52-layer schedule, 4 sequences at 36,864 + step cached rows", "",
              "Two counter runs (from /tmp, repository at $ROOT):", "", "```", command, "```", "",
              f"Calibration: the first copy in each run is a 1 GiB device copy (`--calibrate-copy`); it read "
@@ -167,7 +170,8 @@ def summarize_counters(fetch_csv: str, write_csv: str, out: str, command: str):
              f"4 x 2,048 x 1,024 B = 8.39 MB; full 4 x (p + 1) x 1,024 B = 151.0 MB at p = 36,864.", "",
              "| kernel, layers | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB |",
              "|---|---|---|---|---|", *rows, "",
-             "Values read by bench.py (traffic is reported only while these sources are unchanged):", "",
+             "Values read by bench.py: HBM bytes per decode call, split and merge kernels together (traffic is "
+             "reported only while these sources are unchanged):", "",
              f"    decode_sources_sha256_16: {sources_hash(DECODE_SOURCES)}",
              f"    hbm_bytes_per_launch: {vals['all']:.0f}",
              f"    hbm_bytes_per_launch_full: {vals['full']:.0f}",
@@ -198,8 +202,8 @@ def parse():
                     help="time only the 8 x 8,192 prefill and print its JSON object (for counter runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device copy first (scale for HBM byte counters)")
-    ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT", "COMMAND"),
-                    help="write a kernel-trace summary from rocprofv3 kernel_stats.csv and exit")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_CSV", "OUT", "COMMAND"),
+                    help="write a kernel-trace summary from rocprofv3 kernel_trace.csv and exit")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT", "COMMAND"),
                     help="write the decode kernels' HBM-traffic summary from two --pmc runs and exit")
     ap.add_argument("--summarize-mfma", nargs=4, metavar=("PMC1_CSV", "PMC2_CSV", "OUT", "COMMAND"),
@@ -284,26 +288,54 @@ def bench_schedule(args, fa, synth, torch):
                "roofline": dict(bound="mfma", traffic=None, **kernel_roofline(
                    pms, pfl, MFMA_PEAK_TFLOPS, "TFLOP/s", 1e12,
                    "muse::prefill_group_kernel<1, 8, 1> (bf16)"))}
-    # ---- decode: eager steps with the kernel timer on every call
-    E = min(8, K)
-    sch.start_decode()
-    timers = KernelTimers(E * len(sch.specs))
-    for i in range(E):
-        sch.decode_step(timers=[timers[i * len(sch.specs) + l] for l in range(len(sch.specs))])
-    torch.cuda.synchronize()
+    # ---- decode roofline: per layer kind, a HIP graph of that kind's decode
+    # calls at the first decode position (split kernel + merge kernel each),
+    # replayed between HIP events on the stream it runs on
+    R = 8
     dms = {"sliding": [], "full": []}
     dby = {"sliding": [], "full": []}
-    for i in range(E):
-        for l, spec in enumerate(sch.specs):
-            dms[kinds[l]].append(timers.elapsed_ms(i * len(sch.specs) + l))
-            dby[kinds[l]].append(kv_row_bytes(w.dtype) * S * visible_rows(spec, L0 + N + i))
-    timers.close()
-    roof = dict(bound="hbm", **kernel_roofline(dms, dby, HBM_PEAK_GBS, "GB/s", 1e9, "muse::decode_kernel<bf16>"))
+    sch.start_decode()
+    for kind in ("sliding", "full"):
+        idx = [l for l in range(len(sch.specs)) if kinds[l] == kind]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for l in idx:
+                sch.decode_layer(l)
+        g.replay()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R)]
+        for a, b in ev:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        for a, b in ev:
+            dms[kind] += [a.elapsed_time(b) / len(idx)] * len(idx)
+            dby[kind] += [kv_row_bytes(w.dtype) * S * visible_rows(sch.specs[l], L0 + N) for l in idx]
+        del g
+    roof = dict(bound="hbm", **kernel_roofline(
+        dms, dby, HBM_PEAK_GBS, "GB/s", 1e9,
+        "one decode call: muse::decode_kernel<bf16> (split) + muse::decode_merge_kernel<bf16> (merge)"))
+    roof["measured"] = ("per layer kind, a graph of that kind's decode calls replayed between HIP events; "
+                        "the trace's per-call time is the two kernels' averages added")
     tr = counter_traffic() if not args.ring else None
     roof["traffic"] = tr["all"] if tr else None
     if tr:
         for kind in ("full", "sliding"):
             roof["per_kind"][kind]["traffic"] = tr[kind]
+    # the split kernel alone, from the library's timer on eager calls (the
+    # events' own cost is a few microseconds of these times)
+    E = min(4, K)
+    sch.start_decode()
+    timers = KernelTimers(E * len(sch.specs))
+    for i in range(E):
+        sch.decode_step(timers=[timers[i * len(sch.specs) + l] for l in range(len(sch.specs))])
+    torch.cuda.synchronize()
+    split = {"sliding": [], "full": []}
+    for i in range(E):
+        for l in range(len(sch.specs)):
+            split[kinds[l]].append(1e3 * timers.elapsed_ms(i * len(sch.specs) + l))
+    timers.close()
+    roof["split_kernel_eager_event_us"] = {k: round(sum(v) / len(v), 2) for k, v in split.items()}
     # ---- decode: the timed steps, replayed from one captured step
     sch.start_decode()
     graph = sch.capture_step()
@@ -655,26 +687,71 @@ def summarize_mfma(pmc1_csv: str, pmc2_csv: str, out: str, command: str):
 
 
 
-def summarize_trace(stats_csv: str, out: str, command: str):
-    """Write a kernel-trace summary (text) from rocprofv3's kernel_stats.csv."""
+def summarize_trace(trace_csv: str, out: str, command: str):
+    """Write a kernel-trace summary (text) from rocprofv3's kernel_trace.csv of
+    a default run: the schedule phase (every dispatch before the first f32
+    kernel, which starts the other workloads' legs), its decode and
+    prefill kernels by layer kind (the calls run in layer order, layer l full
+    iff l % 4 == 3), then the legs by kernel."""
     import csv
-    rows = [r for r in csv.DictReader(open(stats_csv)) if "muse" in r["Name"]]
-    lines = ["# Kernel trace summary", "", "Command (from /tmp, repository at $ROOT):", "", "```",
-             command, "```", "", "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
     import re
-    for r in rows:
-        name = r["Name"]
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+
+    def short(name):
         m = re.match(r"_ZN4muse(\d+)", name)
         if m:
             n = int(m.group(1))
             kname = name[m.end():m.end() + n]
-            dt = "bf16" if "DF16b" in name[m.end() + n:] else "f32"
-            name = f"muse::{kname}<{dt}>"
-        lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+            return f"muse::{kname}<{'bf16' if 'DF16b' in name[m.end() + n:] else 'f32'}>"
+        return name.split("(")[0].replace("void ", "")
+
+    import collections
+    legs_at = next((i for i, r in enumerate(rows) if "muse" in r["Kernel_Name"] and short(r["Kernel_Name"]).endswith(
+        ("<f32>", "<float>(muse::AttnArgs)", "<float>(muse::PrepArgs)")) or "<float>" in r["Kernel_Name"]), len(rows))
+    # in the schedule phase the split kernel's grid tells the layer kind (the
+    # 39 sliding layers' grid is the more frequent one), a merge kernel takes
+    # the kind of the split before it, and prefill calls run in layer order
+    grids = collections.Counter(r["Grid_Size_X"] if "Grid_Size_X" in r else r["Grid_Size"]
+                                for r in rows[:legs_at] if "decode_kernel" in r["Kernel_Name"])
+    sliding_grid = grids.most_common(1)[0][0] if grids else None
+    groups = {}
+    counters = {}
+    last_kind = "sliding"
+    for i, r in enumerate(rows):
+        name = r["Kernel_Name"]
+        if "muse" not in name:
+            continue
+        k = short(name)
+        phase = "schedule" if i < legs_at else "legs"
+        if phase == "schedule":
+            kind = None
+            if "decode_merge_kernel" in k:
+                kind = last_kind
+            elif "decode_kernel" in k:
+                kind = "sliding" if (r.get("Grid_Size_X") or r.get("Grid_Size")) == sliding_grid else "full"
+                last_kind = kind
+            elif "prefill_group_kernel" in k or "prep_kernel" in k:
+                c = counters.get(k, 0)
+                counters[k] = c + 1
+                kind = "full" if c % 52 % 4 == 3 else "sliding"
+            if kind:
+                k = f"{k}, {kind} layers"
+        groups.setdefault((phase, k), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# Kernel trace summary", "", "Command (from /tmp, repository at $ROOT):", "", "```", command, "```", "",
+             "Per kernel: the 52-layer schedule phase of the run (chunked prefill, eager and graph-replayed decode "
+             "steps), with layer kinds, then the other workloads' legs.", "",
+             "| phase | kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    for (phase, k), v in sorted(groups.items(), key=lambda x: (x[0][0] != "schedule", -sum(x[1]))):
+        lines.append(f"| {phase} | {k} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    lines += ["", "One decode call of the schedule (split kernel + merge kernel, the unit of the bench line's "
+              "roofline), from the averages above:", ""]
+    for kind in ("sliding", "full"):
+        a = groups.get(("schedule", f"muse::decode_kernel<bf16>, {kind} layers"))
+        b = groups.get(("schedule", f"muse::decode_merge_kernel<bf16>, {kind} layers"))
+        if a and b:
+            lines.append(f"    decode_call_us_{kind}: {sum(a) / len(a) + sum(b) / len(b):.2f}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
-
 
 
 def bench_verify(fa, synth, torch, steps=20, warmup=3, n_new=16):

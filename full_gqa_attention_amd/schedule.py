@@ -93,13 +93,18 @@ class Schedule:
         """Position the sequences after the chunk: the first decode step is at prefix + n_new."""
         self.seq_len.fill_(self.w.prefix + self.w.n_new)
 
+    def decode_layer(self, l: int, timer=None):
+        """Layer l's decode call at the current position (seq_len unchanged)."""
+        q, k, v, g, o = self.dec[l]
+        inp = self.inputs[l]
+        fa.decode(self.layers[l], q, k, v, g, inp.cache_k, inp.cache_v, self.seq_len, o,
+                  max_seq_len=self.max_decode_pos, workspace=self.ws_decode, timer=timer)
+
     def decode_step(self, timers=None):
         """Every layer's decode call at the current position, then seq_len += 1
         on the device.  timers: optional per-layer muse_kernel_timer values."""
-        for l, (lay, inp, (q, k, v, g, o)) in enumerate(zip(self.layers, self.inputs, self.dec)):
-            fa.decode(lay, q, k, v, g, inp.cache_k, inp.cache_v, self.seq_len, o,
-                      max_seq_len=self.max_decode_pos, workspace=self.ws_decode,
-                      timer=timers[l] if timers else None)
+        for l in range(len(self.layers)):
+            self.decode_layer(l, timers[l] if timers else None)
         self.seq_len.add_(1)
 
     def capture_step(self) -> "torch.cuda.CUDAGraph":
