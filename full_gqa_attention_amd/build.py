@@ -68,5 +68,50 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+SAN_LIB_PATH = os.path.join(PKG, "libmuse_attn_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def build_sanitized() -> str:
+    """libmuse_attn_san.so: the host code (argument checks, workspace layout,
+    launch set-up) built with AddressSanitizer and UndefinedBehaviorSanitizer,
+    linked with the kernels of the regular build (GPU code is not
+    instrumented).  A process that loads it must preload clang's ASan runtime
+    (``asan_runtime()``)."""
+    if not all(os.path.exists(os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")) for src in SOURCES):
+        build()
+    san_dir = os.path.join(BUILD_DIR, "san")
+    os.makedirs(san_dir, exist_ok=True)
+    host_obj = os.path.join(san_dir, "muse_attn.o")
+    cmd = [hipcc()] + common_flags() + SAN_FLAGS + ["-c", os.path.join(CSRC, "muse_attn.cpp"), "-o", host_obj]
+    out = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if out.returncode != 0:
+        sys.stderr.write(out.stdout.decode(errors="replace"))
+        raise RuntimeError("hipcc failed on the sanitized muse_attn.cpp")
+    objs = [host_obj] + [os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o") for src in SOURCES
+                         if src != "muse_attn.cpp"]
+    tmp = SAN_LIB_PATH + ".tmp"
+    subprocess.run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-fsanitize=address,undefined",
+                    "-shared-libasan", *objs, "-o", tmp], check=True)
+    os.replace(tmp, SAN_LIB_PATH)
+    return SAN_LIB_PATH
+
+
+def asan_runtime() -> str:
+    """clang's shared ASan runtime (it carries the UBSan handlers too)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    out = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE, check=True)
+    path = out.stdout.decode().strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang's shared ASan runtime was not found")
+    return path
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized())
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -596,7 +596,7 @@ muse_status muse_out_proj(int32_t n_tokens, const void* attn, const void* w, con
     return MUSE_OK;
 }
 
-const char* muse_status_str(muse_status s) {
+const char* muse_status_str(int s) {
     switch (s) {
         case MUSE_OK: return "MUSE_OK";
         case MUSE_ERR_NULL: return "MUSE_ERR_NULL: a required pointer is NULL";

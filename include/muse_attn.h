@@ -266,8 +266,10 @@ int32_t muse_layer_kind_for(int32_t layer_index, int32_t n_layers);
  * ["Chapter 14" 14.4.1]  MUSE_ERR_LAYER unless theta is finite and > 0. */
 muse_status muse_rope_theta_table(float theta, float* out_host64);
 
-/* Static string naming a status code (never NULL). */
-const char* muse_status_str(muse_status status);
+/* Static string naming a status code (never NULL).  Takes the code as an int
+ * so that any value, a muse_status or not, is a valid argument; values that
+ * name no status give "unknown muse_status". */
+const char* muse_status_str(int status);
 
 /* ------------------------------------------------ the block's tail (next step)
  *

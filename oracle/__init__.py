@@ -30,6 +30,9 @@ ANGLE_F32, ANGLE_EXACT = 0, 1
 HEAD_DIM, N_HEADS, N_KV_HEADS = 128, 32, 2
 
 
+_SAN_LIB_PATH = os.path.join(_HERE, "liboracle_san.so")
+
+
 def build(force: bool = True) -> str:
     """Compile oracle.c into liboracle.so with gcc (-O2, OpenMP, no fast-math)."""
     if force or not os.path.exists(_LIB_PATH):
@@ -40,6 +43,27 @@ def build(force: bool = True) -> str:
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
+
+
+def build_sanitized(clang: str = "/opt/rocm/llvm/bin/clang") -> str:
+    """liboracle_san.so: oracle.c with AddressSanitizer and
+    UndefinedBehaviorSanitizer, built with clang so that it shares one ASan
+    runtime with the sanitized HIP library in a test process."""
+    tmp = _SAN_LIB_PATH + ".tmp"
+    cmd = [clang, "-O1", "-g", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+           "-ffp-contract=off", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fno-omit-frame-pointer", "-shared-libasan", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _SAN_LIB_PATH)
+    return _SAN_LIB_PATH
+
+
+def use_sanitized_build() -> None:
+    """Load liboracle_san.so instead of liboracle.so (before the first call)."""
+    global _LIB_PATH
+    if _lib is not None:
+        raise RuntimeError("the oracle library is already loaded")
+    _LIB_PATH = _SAN_LIB_PATH
 
 
 class _Layer(ctypes.Structure):
