@@ -194,6 +194,10 @@ def parse():
                     help="also time the 16-token verify call (64 x 8,192 cached rows, both layers)")
     ap.add_argument("--out-proj", action="store_true",
                     help="also time the block's tail (o_proj + post-attention norm) at 65,536 and 64 tokens")
+    ap.add_argument("--summarize-legs", nargs=5, metavar=("TRACE_CSV", "FETCH_CSV", "WRITE_CSV", "OUT", "COMMAND"),
+                    help="write the per-kernel summary of the verify / o_proj / relocate legs")
+    ap.add_argument("--only-next", action="store_true",
+                    help="run only the legs asked for with --verify / --out-proj / --relocate (no schedule, no configs)")
     ap.add_argument("--relocate", action="store_true",
                     help="also time NoPE tile relocation (muse_kv_relocate) of a 64 x 8,192 full-layer cache")
     ap.add_argument("--counters-run", action="store_true",
@@ -687,6 +691,79 @@ def summarize_mfma(pmc1_csv: str, pmc2_csv: str, out: str, command: str):
 
 
 
+def summarize_legs(trace_csv: str, fetch_csv: str, write_csv: str, out: str, command: str):
+    """Per-kernel summary of `bench.py --only-next ...` (verify, o_proj,
+    relocate legs): average duration from the kernel trace, and FETCH_SIZE /
+    WRITE_SIZE (medians over the dispatches, scaled by the 1 GiB copy of
+    `--calibrate-copy`) from two counter runs.  Verify launches of the sliding
+    and the full layer share a grid; they are told apart by duration (the
+    full layer's calls take about three times longer)."""
+    import csv
+    import statistics
+
+    def rows_of(path, value):
+        out = []
+        for r in csv.DictReader(open(path)):
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            out.append((int(r["Start_Timestamp"]), r["Kernel_Name"], int(r.get("Grid_Size") or r.get("Grid_Size_X") or 0),
+                        dur, value(r)))
+        return [x[1:] for x in sorted(out)]                # dispatch order
+
+    def keys(lst, cut):
+        # a verify merge belongs to the layer of the verify launch before it
+        out, last = [], ""
+        for n, g, d, v in lst:
+            short = n.split("(")[0].replace("void ", "")
+            if "verify_kernel" in short and cut is not None:
+                last = ", full layer" if d > cut else ", sliding layer"
+                out.append(short + last)
+            elif "verify_merge" in short:
+                out.append(short + last)
+            else:
+                out.append(short)
+        return out
+
+    trace = rows_of(trace_csv, lambda r: 0.0)
+    fetch = rows_of(fetch_csv, lambda r: float(r["Counter_Value"]))
+    write = rows_of(write_csv, lambda r: float(r["Counter_Value"]))
+    vd = sorted(d for n, g, d, v in trace if "verify_kernel" in n)
+    cut = (vd[0] + vd[-1]) / 2 if vd else None
+    copy_f = [v for n, g, d, v in fetch if "copyBuffer" in n]
+    copy_w = [v for n, g, d, v in write if "copyBuffer" in n]
+    fs = FETCH_SCALE if not copy_f else round((1 << 30) / (copy_f[0] * 1024), 2)
+    ws = WRITE_SCALE if not copy_w else round((1 << 30) / (copy_w[0] * 1024), 2)
+    groups = {}
+    for (n, g, d, v), k in zip(trace, keys(trace, cut)):
+        if "muse::" in n:
+            groups.setdefault(k, {"dur": [], "f": [], "w": []})["dur"].append(d)
+    for lst, tag in ((fetch, "f"), (write, "w")):
+        fd = sorted(d for n, g, d, v in lst if "verify_kernel" in n)
+        fcut = (fd[0] + fd[-1]) / 2 if fd else None
+        for (n, g, d, v), k in zip(lst, keys(lst, fcut)):
+            if "muse::" in n and k in groups:
+                groups[k][tag].append(v)
+    lines = ["# Kernel trace and HBM traffic of the verify, o_proj and relocate legs", "",
+             "Commands (from /tmp, repository at $ROOT): the trace, then the two counter runs:", "", "```",
+             command, "```", "",
+             f"FETCH_SIZE is scaled by {fs} and WRITE_SIZE by {ws} (a 1 GiB device copy, `--calibrate-copy`, "
+             f"read {copy_f[0] if copy_f else 0:.1f} KiB and wrote {copy_w[0] if copy_w else 0:.1f} KiB on them). "
+             "FETCH_SIZE counts what the L2s fetch from memory, Infinity Cache hits included.  Counter values "
+             "are medians over the dispatches.", "",
+             "Algorithmic bytes per launch: verify reads every visible cache row once (64 x 8,208 x 1,024 B = "
+             "537.9 MB full; 64 x 2,063 x 1,024 B = 135.2 MB sliding) and writes 35.7 MB of f32 partials (2 splits); "
+             "relocate moves up to 120 tiles of 512 rows per launch (62.9 MB of K and V read, the same written); "
+             "o_proj: W (54.5 MB) and the attention rows once, f32 projection written.", "",
+             "| kernel | dispatches | avg us | min us | read MB | write MB |", "|---|---|---|---|---|---|"]
+    for k in sorted(groups):
+        gd = groups[k]
+        fmb = statistics.median(gd["f"]) * 1024 * fs / 1e6 if gd["f"] else float("nan")
+        wmb = statistics.median(gd["w"]) * 1024 * ws / 1e6 if gd["w"] else float("nan")
+        lines.append(f"| `{k}` | {len(gd['dur'])} | {sum(gd['dur']) / len(gd['dur']):.2f} | {min(gd['dur']):.2f} | "
+                     f"{fmb:.2f} | {wmb:.2f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def summarize_trace(trace_csv: str, out: str, command: str):
     """Write a kernel-trace summary (text) from rocprofv3's kernel_trace.csv of
     a default run: the schedule phase (every dispatch before the first f32
@@ -856,23 +933,35 @@ def bench_relocate(fa, synth, torch, steps=10):
     tiles = fa.kv_tiles([(s, i * T, (s + 1) % S, (L // T - 1 - i) * T, T) for s in range(S) for i in range(L // T)])
     fa.kv_relocate(lay, a_k, a_v, b_k, b_v, tiles)
     torch.cuda.synchronize()
-    # GPU time of one pass between events (the host builds and checks the
-    # tile list before enqueueing; that is timed separately)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    gpu_ms = []
+    # The host checks the tile list and splits it into launches on every call
+    # (timed here on its own).  The GPU time of a pass comes from a HIP graph
+    # of one call: the tile descriptors travel as kernel arguments, so the
+    # replays run the copy kernels only.
     host = 0.0
     for _ in range(steps):
         t0 = time.perf_counter()
-        e0.record()
         fa.kv_relocate(lay, a_k, a_v, b_k, b_v, tiles)
-        e1.record()
         host += time.perf_counter() - t0
+        torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fa.kv_relocate(lay, a_k, a_v, b_k, b_v, tiles)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gpu_ms = []
+    for _ in range(steps):
+        e0.record()
+        graph.replay()
+        e1.record()
         torch.cuda.synchronize()
         gpu_ms.append(e0.elapsed_time(e1))
     dt = sorted(gpu_ms)[len(gpu_ms) // 2] * 1e-3
     moved = 2 * a_k.numel() * a_k.element_size()           # K and V bytes per pass
     ok = bool(torch.equal(b_k[1, (L // T - 1) * T:], a_k[0, :T]))
-    return {"tiles": tiles[1], "tile_rows": T, "MB_moved": round(moved / 1e6, 1), "gpu_ms": round(dt * 1e3, 3),
+    del graph
+    return {"tiles": tiles[1], "tile_rows": T, "MB_moved": round(moved / 1e6, 1),
+            "gpu_ms": round(dt * 1e3, 3), "gpu_ms_measured": "one pass replayed from a HIP graph, between events",
             "host_ms_per_call": round(host / steps * 1e3, 3),
             "GBps_read_plus_write": round(2 * moved / dt / 1e9, 1),
             "frac_hbm_peak": round(2 * moved / dt / 1e9 / HBM_PEAK_GBS, 4), "bytes_checked": ok}
@@ -880,6 +969,9 @@ def bench_relocate(fa, synth, torch, steps=10):
 
 def main():
     args = parse()
+    if args.summarize_legs:
+        summarize_legs(*args.summarize_legs)
+        return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
         return
@@ -909,6 +1001,18 @@ def main():
     if args.prefill_only:
         pw = synth.WORKLOADS["prefill_8x8192_bf16"]
         print(json.dumps({"prefill": leg_prefill(pw, fa, synth, torch, steps=5, cpu=False)}), flush=True)
+        return
+    if args.only_next:
+        extra = {}
+        if args.verify:
+            extra["verify"] = bench_verify(fa, synth, torch)
+            torch.cuda.empty_cache()
+        if args.out_proj:
+            extra["out_proj"] = bench_out_proj(fa, synth, torch)
+            torch.cuda.empty_cache()
+        if args.relocate:
+            extra["relocate"] = bench_relocate(fa, synth, torch)
+        print(json.dumps(extra), flush=True)
         return
     if args.counters_run:
         from full_gqa_attention_amd.schedule import Schedule
