@@ -359,6 +359,24 @@ void prefill_kernel(AttnArgs a) {
 // the Q.K MFMAs start from -ref instead of 0, so no subtraction is left
 // either.  Row sums are taken from the bf16 P values that enter the P.V
 // product (v_dot2 against (1, 1)).
+// One direct load: every lane fetches 16 bytes at `src` (its own address) and
+// the active lanes' pieces land at the LDS address `dst` + 16 x lane (`dst`
+// uniform).  Issued as inline asm, so the compiler neither counts it nor
+// guards LDS accesses with waits for it (the builtin made the RoPE table
+// wait for every load in flight): the caller waits (s_waitcnt vmcnt) before
+// it reads that LDS.  M0 holds the LDS address, with a wait state before the
+// load; nothing else in this file's kernels uses M0 (checked in their gfx950
+// assembly: no s_movrel/v_movrel, GWS, LDS-direct or s_sendmsg), so the
+// clobber loses nothing.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* src, void* dst) {
+    const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(m0) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 template <int QG> struct GroupTraits {
     static constexpr int WAVES = QG == 1 ? 2 : 1;      // waves per SIMD the registers allow
 };
@@ -391,6 +409,9 @@ void prefill_group_kernel(AttnArgs a) {
     constexpr int NCH = BN * CPR / NT;                 // chunks per thread per tile
     __shared__ __attribute__((aligned(16))) TQ Ks[2][BN * LDK];
     __shared__ __attribute__((aligned(16))) T Vs[2][BN * LDV];
+    constexpr int LDE = D + 8;                         // epilogue rows: 272 bytes = 17 slots of 16 bytes
+    static_assert(QG == 1, "the epilogue buffer holds one 32-row group per wave");
+    __shared__ __attribute__((aligned(16))) T ebuf[WPB][32 * LDE];
 
     // ---- work item: block b runs head group (b >> 3) % HQ of unit (b >> 3) / HQ * 8 + (b & 7),
     // so the workgroups of a unit (its 16 heads) share an XCD
@@ -451,8 +472,33 @@ void prefill_group_kernel(AttnArgs a) {
     // writing Q-hat to HBM and reading it back.  The workgroup's rows share one
     // (cos, sin) table in LDS.
     __shared__ float2 rot[BMW][kHeadDim / 2 + 1];       // padded: rows start 2 banks apart
-    // the raw Q rows and the first K/V tile go out before the (cos, sin)
-    // table is built, so that both memory round trips overlap it
+    // The epilogue's gate rows (32 rows x 256 bytes of head h) go straight to
+    // the wave's epilogue buffer first of all, so the epilogue does not wait
+    // for them.  They are requested before every load the compiler counts:
+    // vector loads complete in issue order, so the compiler's waits (which do
+    // not know of these) still wait exactly for what they name.
+    // Slot k (16 bytes) of the buffer is row k / 17, chunk k % 17; chunk 16 is
+    // the row's padding and takes a copy of chunk 15.  Nine loads of 64 slots
+    // cover the 544 slots; the last one only with lanes 0-31.
+    {
+        const char* grow = (const char*)a.gate + ((int64_t)s * N * kHeads + h) * D * ES;
+        char* eb0 = (char*)ebuf[wave];
+#pragma unroll
+        for (int j = 0; j < 9; ++j) {
+            const int slot = 64 * j + lane, r = slot / 17, c = min(slot % 17, 15);
+            const int t = min(q0 + r, N - 1);
+            if (j < 8 || lane < 32)
+                lds_dma16(grow + (int64_t)t * kHeads * D * ES + 16 * c, eb0 + 1024 * j);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // This lane's RoPE frequency is requested next, then the raw Q rows and
+    // the first K/V tile, all before the (cos, sin) table is built: the table
+    // waits for the frequency alone, and the Q and tile round trips overlap it.
+    // (Requested after them, the frequency made the table wait for every load
+    // in flight: 3.4 us per sliding workgroup instead of 0.6.)
+    const float th = a.rope ? theta_of_lane<AttnArgs>(lane) : 0.0f;
+    __builtin_amdgcn_sched_barrier(0);
     bf16x8 qraw[QG][NST];
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
@@ -469,7 +515,6 @@ void prefill_group_kernel(AttnArgs a) {
         va0[u] = *(const u32x4*)(vbase + off);
     }
     if (a.rope) {
-        const float th = theta_of_lane<AttnArgs>(lane);
         for (int row = wave; row < BMW; row += WPB) {
             float sn, cs;
             sincos_rope((float)((int64_t)L + q0 + row) * th, &sn, &cs);
@@ -772,22 +817,12 @@ void prefill_group_kernel(AttnArgs a) {
     // bytes in each.)  Only this wave touches its buffer, and a wave's LDS
     // accesses complete in order, so the phases need no barrier; the wave
     // barriers keep the compiler from moving accesses across phases.
-    constexpr int LDE = D + 8;                         // 272-byte rows
-    __shared__ __attribute__((aligned(16))) T ebuf[WPB][32 * LDE];
     T* eb = ebuf[wave];
     const int er = lane >> 4, ec = lane & 15;          // whole-row phases: row 4u + er, 16-byte chunk ec
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
         const int t0 = q0 + 32 * qg;
-        u32x4 graw[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int t = min(t0 + 4 * u + er, N - 1);
-            graw[u] = *(const u32x4*)((const T*)a.gate + (((int64_t)s * N + t) * kHeads + h) * D + 8 * ec);
-        }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int u = 0; u < 8; ++u) *(u32x4*)(eb + (4 * u + er) * LDE + 8 * ec) = graw[u];
+        __builtin_amdgcn_s_waitcnt(0);                 // the gate rows loaded into eb at the start
         __builtin_amdgcn_wave_barrier();
         const float inv = 1.0f / sum_halves(l_run[qg]);
 #pragma unroll
