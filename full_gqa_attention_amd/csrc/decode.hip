@@ -129,9 +129,13 @@ void decode_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) T qs_lo[kBf16 ? HG * LDQ : 4];
     __shared__ float2 rot_all[NW][kHeadDim / 2];       // per-wave (cos, sin) of the 64 RoPE pairs
 
+    // workgroup b takes pair b mod (2 n_seq) and split b / (2 n_seq): with
+    // dispatch round-robin over the 8 XCDs, all splits of a pair share an
+    // XCD when the pair count is a multiple of 8 (so does the pair's merge)
     const int b = blockIdx.x;
-    const int c = b % a.nsplit;
-    const int sg = b / a.nsplit;
+    const int npair = 2 * a.n_seq;
+    const int c = b / npair;
+    const int sg = b % npair;
     const int s = sg >> 1, g = sg & 1;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
@@ -560,7 +564,11 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeAr
     constexpr int D = kHeadDim, B = kMergeBatch, R = kMaxSplits / 64;
     static_assert(kMaxSplits % 64 == 0 && kHeads % kMergeWaves == 0, "whole lanes and workgroups");
     const int lane = threadIdx.x & 63;
-    const int sh = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);   // (sequence, head)
+    // workgroup b takes heads 4 q .. 4 q + 3 of pair b mod (2 n_seq), q = b / (2 n_seq)
+    // (the XCD of that pair's splits)
+    const int npair = 2 * a.n_seq;
+    const int mpair = blockIdx.x % npair, mq = blockIdx.x / npair;
+    const int sh = (mpair >> 1) * kHeads + (mpair & 1) * kHeadsPerKv + kMergeWaves * mq + (threadIdx.x >> 6);   // (sequence, head)
     const int s = sh / kHeads;
     const int nsplit = a.nsplit;
     const int64_t row0 = (int64_t)sh * nsplit;

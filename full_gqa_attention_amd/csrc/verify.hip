@@ -45,9 +45,13 @@ void verify_kernel(VerifyArgs a) {
     __shared__ __attribute__((aligned(16))) T Vs[2][BN * LDV];
     __shared__ float2 rot[kVerifyTokens][kHeadDim / 2 + 1];
 
+    // workgroup b takes pair b mod (2 n_seq) and split b / (2 n_seq): with
+    // dispatch round-robin over the 8 XCDs, all splits of a pair share an
+    // XCD when the pair count is a multiple of 8 (so do the pair's merges)
     const int b = blockIdx.x;
-    const int c = b % a.nsplit;
-    const int sg = b / a.nsplit;
+    const int npair = 2 * a.n_seq;
+    const int c = b / npair;
+    const int sg = b % npair;
     const int s = sg >> 1, g = sg & 1;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, gl = lane >> 5;
@@ -312,10 +316,11 @@ void verify_kernel(VerifyArgs a) {
 template <int MC>
 __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a) {
     const int tid = threadIdx.x, hg = tid >> 4, dq = tid & 15;
-    const int blk = blockIdx.x;                        // (s * N + t) * 2 + g
-    const int g = blk & 1, st = blk >> 1;
+    const int blk = blockIdx.x;                        // t * (2 n_seq) + 2 s + g: the XCD of the pair's splits
+    const int npair = 2 * a.n_seq;
     const int N = a.n_new;
-    const int t = st % N, s = st / N;
+    const int g = (blk % npair) & 1, s = (blk % npair) >> 1, t = blk / npair;
+    const int st = s * N + t;
     const int h = g * kHeadsPerKv + hg;
     const int64_t obase = ((int64_t)st * kHeads + h) * kHeadDim + 8 * dq;
     const u32x4 graw = *(const u32x4*)((const bf16_t*)a.gate + obase);
