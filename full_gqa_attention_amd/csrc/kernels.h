@@ -96,7 +96,7 @@ struct DecodeArgs {
 // Short bf16 chunks (at most kVerifyTokens new tokens per sequence): split-K
 // attention with all 16 heads x 16 token rows of a KV head per workgroup,
 // then a merge of the splits with the gate.
-constexpr int kVerifyDepth = 4;     // key tiles in flight per verify workgroup (register slots)
+constexpr int kVerifyDepth = 2;     // key tiles in flight per verify workgroup (register slots)
 constexpr int kVerifyBlocks = 256;  // verify workgroups a call aims for (splits = this / (2 n_seq))
 constexpr int kVerifyTokens = 16;
 constexpr int kVerifyTile = 32;     // keys per tile
