@@ -1,6 +1,6 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark times: every row where the oracle finishes in seconds (the 64 x
-8,192 decode step), sampled rows elsewhere.  A sample always includes the
+8,192 and 16 x 131,072 decode steps), sampled rows of every sequence elsewhere.  A sample always includes the
 window and tile edges; each attention row depends only on its own query and
 the cache, so checking a row checks it exactly.  Every appended cache row is
 checked in all cases.
@@ -35,21 +35,22 @@ def test_prefill_8x8192_sampled(li):
     w = synth.WORKLOADS["prefill_8x8192_bf16"]
     spec = w.layers[li]
     inp = synth.layer_inputs(w, spec, device=DEV, backend="torch")
+    # every sequence: the window and tile edges and 16 rows of its own
     rng = np.random.default_rng(7)
-    extra = tuple(int(x) for x in rng.integers(0, w.n_new, 6))
-    rows = np.concatenate([edge_rows(w.n_new, spec.window, extra, seqs=(s,)) for s in (0, 3, 7)])
+    rows = np.concatenate([edge_rows(w.n_new, spec.window, tuple(int(x) for x in rng.integers(0, w.n_new, 16)),
+                                     seqs=(s,)) for s in range(w.n_seq)])
     check_layer(w, spec, inp, decode=False, rows=rows, untouched=False)
 
 
 @pytest.mark.parametrize("li", [0, 1], ids=["full", "sliding"])
 def test_decode_16x131072_sampled(li):
-    """Long-context decode: 16 sequences x 131,072 cached rows; 4 sequences'
-    rows checked against the oracle (all 32 heads), every appended row checked."""
+    """Long-context decode: 16 sequences x 131,072 cached rows; every
+    sequence's row checked against the oracle (all 32 heads), every appended
+    row checked."""
     w = synth.WORKLOADS["decode_16x131072_bf16"]
     spec = w.layers[li]
     inp = synth.layer_inputs(w, spec, device=DEV, backend="torch")
-    rows = np.array([(s, 0) for s in (0, 5, 10, 15)], dtype=np.int32)
-    check_layer(w, spec, inp, decode=True, rows=rows, max_seq_len=w.prefix, untouched=False)
+    check_layer(w, spec, inp, decode=True, max_seq_len=w.prefix, untouched=False)
 
 
 def _bf16_from_f64(x: np.ndarray) -> torch.Tensor:
@@ -70,7 +71,7 @@ def test_schedule_chunk_then_decode(layer_index):
     seq = inp.seq_len.cpu().numpy()
     pk, pv = host_cache(inp)                           # the oracle's own cache copy
     out = run_gpu(spec, w.dtype, inp, decode=False, max_seq_len=w.prefix)
-    rows = np.concatenate([edge_rows(w.n_new, spec.window, (1000, 3000), seqs=(s,)) for s in (0, 3)])
+    rows = np.concatenate([edge_rows(w.n_new, spec.window, (1000, 3000), seqs=(s,)) for s in range(w.n_seq)])
     ref, kst, vst = run_oracle(spec, w.dtype, inp, rows, pk, pv, seq)
     got = to_f64(out[torch.as_tensor(rows[:, 0], device=DEV).long(), torch.as_tensor(rows[:, 1], device=DEV).long()])
     assert_close(got, ref, w.dtype, f"chunk l{layer_index}")
