@@ -21,6 +21,8 @@ ARCH = "gfx950"
 # The prefill kernels keep their Q.K and P.V accumulators in VGPRs: the scores
 # feed the VALU softmax directly, and the AGPRs serve as spill space.
 EXTRA_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# hipBLASLt computes the o_proj GEMM for more than a few tokens
+LINK_LIBS = ["-lhipblaslt"]
 
 
 def hipcc() -> str:
@@ -62,7 +64,7 @@ def build(verbose: bool = False) -> str:
     if failed:
         raise RuntimeError(f"hipcc failed on {failed}")
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, *LINK_LIBS, "-o", tmp]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
@@ -93,7 +95,7 @@ def build_sanitized() -> str:
                          if src != "muse_attn.cpp"]
     tmp = SAN_LIB_PATH + ".tmp"
     subprocess.run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-fsanitize=address,undefined",
-                    "-shared-libasan", *objs, "-o", tmp], check=True)
+                    "-shared-libasan", *objs, *LINK_LIBS, "-o", tmp], check=True)
     os.replace(tmp, SAN_LIB_PATH)
     return SAN_LIB_PATH
 

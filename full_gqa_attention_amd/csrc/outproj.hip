@@ -4,143 +4,22 @@
 // post-attention RMSNorm (its own epsilon, 1e-8 in the model) scales each
 // token's projection, and the result joins the residual stream.
 //
-// Two kernels.  The projection is a plain GEMM, proj = attn . W^T, on
-// v_mfma_f32_32x32x16_bf16 with f32 accumulation, written in f32 to the
-// workspace.  The norm needs a whole 6,656-wide row, which no GEMM tile holds,
+// Two steps.  The projection is a plain GEMM, proj = attn . W^T, with f32
+// accumulation, written in f32 to the workspace: for a few tokens (a decode
+// step) a kernel of this file that streams W across every CU, for more tokens
+// hipBLASLt.  The norm needs a whole 6,656-wide row, which no GEMM tile holds,
 // so a second, memory-bound kernel takes one row per workgroup: sum of
 // squares, 1 / sqrt(mean + eps), times the gain, plus the residual, rounded
 // once to bf16.
+#include <map>
+#include <mutex>
+
+#include <hipblaslt/hipblaslt.h>
+
 #include "device_common.h"
 #include "kernels.h"
 
 namespace muse {
-
-// ---- GEMM: a workgroup computes a kOpBM x kOpBN tile of proj with 8 waves
-// (kOpWM along the tokens x kOpWN along the channels, each 32 kOpTM x 32 kOpTN:
-// kOpTM x kOpTN MFMA tiles).  256 x 256 tiles of 64 x 128 per wave (4 x 2
-// waves) measured 15% faster than 256 x 128 tiles of 64 x 64: each operand
-// read from LDS feeds more MFMAs.
-// K advances 64 at a time through two LDS buffers; global loads run two
-// k-steps ahead in alternating register sets.  Both operands are K-contiguous
-// (attn rows and W rows), so every MFMA operand is one 16-byte LDS read.
-#ifndef MUSE_OP_TM
-#define MUSE_OP_TM 2
-#endif
-#ifndef MUSE_OP_TN
-#define MUSE_OP_TN 4
-#endif
-#ifndef MUSE_OP_WM
-#define MUSE_OP_WM 4
-#endif
-constexpr int kOpTM = MUSE_OP_TM, kOpTN = MUSE_OP_TN, kOpWM = MUSE_OP_WM, kOpWN = 8 / kOpWM;
-constexpr int kOpBM = 32 * kOpTM * kOpWM, kOpBN = 32 * kOpTN * kOpWN, kOpBK = 64;
-constexpr int kOpLds = kOpBK + 8;                      // 144-byte rows: b128 reads conflict-free
-constexpr int kOpThreads = 512;
-constexpr int kOpAChunks = kOpBM * kOpBK * 2 / 16 / kOpThreads;   // 16-byte chunks per thread (4)
-constexpr int kOpBChunks = kOpBN * kOpBK * 2 / 16 / kOpThreads;   // (2)
-static_assert(kModelDim % kOpBN == 0 && kAttnDim % kOpBK == 0, "tile sizes divide the shapes");
-
-__global__ __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void out_proj_gemm_kernel(OutProjArgs a) {
-    using MP = Mma32<bf16_t>;
-    constexpr int K = kAttnDim, N = kModelDim, NK = K / kOpBK;
-    __shared__ __attribute__((aligned(16))) bf16_t As[2][kOpBM * kOpLds];
-    __shared__ __attribute__((aligned(16))) bf16_t Bs[2][kOpBN * kOpLds];
-
-    const int nblk = N / kOpBN;
-    const int nb = blockIdx.x % nblk, mb = blockIdx.x / nblk;   // the channel blocks of a token block run together
-    const int m0 = mb * kOpBM, n0 = nb * kOpBN;
-    const int M = a.m;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, gl = lane >> 5;
-    const int wm = wave / kOpWN, wn = wave % kOpWN;
-
-    // staging: chunk c = tid + 512 u is row c / 8, 16-byte piece c % 8 of a 64-wide k slice
-    const bf16_t* A = (const bf16_t*)a.attn;
-    const bf16_t* B = (const bf16_t*)a.w;
-    auto load = [&](u32x4 (&ra)[kOpAChunks], u32x4 (&rb)[kOpBChunks], int ks) __attribute__((always_inline)) {
-        const int k0 = min(ks, NK - 1) * kOpBK;                  // past the end: harmless repeats
-#pragma unroll
-        for (int u = 0; u < kOpAChunks; ++u) {
-            const int c = tid + kOpThreads * u, r = c >> 3, p = c & 7;
-            const int row = min(m0 + r, M - 1);                  // rows past the last token repeat it
-            ra[u] = *(const u32x4*)(A + (int64_t)row * K + k0 + 8 * p);
-        }
-#pragma unroll
-        for (int u = 0; u < kOpBChunks; ++u) {
-            const int c = tid + kOpThreads * u, r = c >> 3, p = c & 7;
-            rb[u] = *(const u32x4*)(B + (int64_t)(n0 + r) * K + k0 + 8 * p);
-        }
-    };
-    auto store = [&](const u32x4 (&ra)[kOpAChunks], const u32x4 (&rb)[kOpBChunks], int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < kOpAChunks; ++u) {
-            const int c = tid + kOpThreads * u, r = c >> 3, p = c & 7;
-            *(u32x4*)(As[buf] + r * kOpLds + 8 * p) = ra[u];
-        }
-#pragma unroll
-        for (int u = 0; u < kOpBChunks; ++u) {
-            const int c = tid + kOpThreads * u, r = c >> 3, p = c & 7;
-            *(u32x4*)(Bs[buf] + r * kOpLds + 8 * p) = rb[u];
-        }
-    };
-
-    floatx16 acc[kOpTM][kOpTN];
-#pragma unroll
-    for (int i = 0; i < kOpTM; ++i)
-#pragma unroll
-        for (int j = 0; j < kOpTN; ++j) acc[i][j] = floatx16{};
-    // C[m][n] += A[m][k] W[n][k]: lane (l32, gl) gives A row l32 and W row l32
-    // (the B column), k = 8 gl .. 8 gl + 7 of each 16-wide step
-    auto compute = [&](int buf) __attribute__((always_inline)) {
-        const bf16_t* Ab = As[buf] + (32 * kOpTM * wm + l32) * kOpLds + 8 * gl;
-        const bf16_t* Bb = Bs[buf] + (32 * kOpTN * wn + l32) * kOpLds + 8 * gl;
-#pragma unroll
-        for (int kk = 0; kk < kOpBK / 16; ++kk) {
-            bf16x8 af[kOpTM], bfr[kOpTN];
-#pragma unroll
-            for (int i = 0; i < kOpTM; ++i) af[i] = *(const bf16x8*)(Ab + 32 * i * kOpLds + 16 * kk);
-#pragma unroll
-            for (int j = 0; j < kOpTN; ++j) bfr[j] = *(const bf16x8*)(Bb + 32 * j * kOpLds + 16 * kk);
-#pragma unroll
-            for (int i = 0; i < kOpTM; ++i)
-#pragma unroll
-                for (int j = 0; j < kOpTN; ++j) acc[i][j] = MP::mma(af[i], bfr[j], acc[i][j]);
-        }
-    };
-
-    u32x4 ra0[kOpAChunks], rb0[kOpBChunks], ra1[kOpAChunks], rb1[kOpBChunks];
-    load(ra0, rb0, 0);
-    store(ra0, rb0, 0);
-    load(ra1, rb1, 1);
-    __syncthreads();
-    // step ks: buffer ks & 1 holds k-slice ks, (rn, bn) holds slice ks + 1,
-    // (rf, bf) receives slice ks + 2
-    auto step = [&](int ks, u32x4 (&rn)[kOpAChunks], u32x4 (&bn)[kOpBChunks],
-                    u32x4 (&rf)[kOpAChunks], u32x4 (&bf)[kOpBChunks]) __attribute__((always_inline)) {
-        load(rf, bf, ks + 2);
-        compute(ks & 1);
-        store(rn, bn, (ks + 1) & 1);                   // free since the last barrier
-        __syncthreads();
-    };
-    static_assert(NK % 2 == 0, "k-steps come in pairs");
-    for (int ks = 0; ks < NK; ks += 2) {
-        step(ks, ra1, rb1, ra0, rb0);
-        step(ks + 1, ra0, rb0, ra1, rb1);
-    }
-
-    // ---- proj rows m0 + 32 (kOpTM wm + i) + 8 (e / 4) + 4 gl + e % 4, channel
-    // n0 + 32 (kOpTN wn + j) + l32: 32 lanes store 128 contiguous bytes per item
-#pragma unroll
-    for (int i = 0; i < kOpTM; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int m = m0 + 32 * (kOpTM * wm + i) + 8 * (e / 4) + 4 * gl + (e % 4);
-            if (m >= M) continue;
-#pragma unroll
-            for (int j = 0; j < kOpTN; ++j) a.proj[(int64_t)m * N + n0 + 32 * (kOpTN * wn + j) + l32] = acc[i][j][e];
-        }
-}
 
 // ---- GEMM for a few tokens (a decode step: at most 64).  Reading W's 54.5
 // MB is the whole cost, so every CU must stream an equal share with as much
@@ -305,6 +184,78 @@ __global__ __launch_bounds__(THREADS) void out_proj_norm_kernel(OutProjArgs a) {
     }
 }
 
+// ---- the projection of more tokens through hipBLASLt.  Column-major, as the
+// library sees it: D (f32 6656 x m, ld 6656; proj row-major [m][6656]) =
+// op(A) x B with A = W read as 4096 x 6656 (ld 4096) and op(A) its transpose,
+// B = attn read as 4096 x m (ld 4096).  One library handle per device, made on
+// the first such call there (it allocates: capture graphs only after one
+// eager call).  The algorithm is the library's heuristic choice among those
+// that need no workspace (the call passes none: an algorithm that wanted one
+// wrote through the missing buffer), kept per token count, so repeated calls
+// run the same kernels and give the same bits.
+namespace {
+struct BlasDevice {
+    hipblasLtHandle_t handle = nullptr;
+    std::map<int32_t, hipblasLtMatmulAlgo_t> algo;
+};
+std::mutex g_blas_mu;
+std::map<int, BlasDevice> g_blas;
+
+hipError_t launch_out_proj_blas(const OutProjArgs& a, hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorUnknown;
+    std::lock_guard<std::mutex> lock(g_blas_mu);
+    BlasDevice& bd = g_blas[dev];
+    if (!bd.handle && hipblasLtCreate(&bd.handle) != HIPBLAS_STATUS_SUCCESS) {
+        bd.handle = nullptr;
+        return hipErrorUnknown;
+    }
+    hipblasLtMatmulDesc_t desc = nullptr;
+    hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
+    hipblasLtMatmulPreference_t pref = nullptr;
+    hipError_t err = hipErrorUnknown;
+    const hipblasOperation_t opA = HIPBLAS_OP_T, opB = HIPBLAS_OP_N;
+    const float alpha = 1.0f, beta = 0.0f;
+    const auto ok = [](hipblasStatus_t st) { return st == HIPBLAS_STATUS_SUCCESS; };
+    do {
+        if (!ok(hipblasLtMatmulDescCreate(&desc, HIPBLAS_COMPUTE_32F, HIP_R_32F)) ||
+            !ok(hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opA, sizeof(opA))) ||
+            !ok(hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opB, sizeof(opB))))
+            break;
+        if (!ok(hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, kAttnDim, kModelDim, kAttnDim)) ||
+            !ok(hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, kAttnDim, (uint64_t)a.m, kAttnDim)) ||
+            !ok(hipblasLtMatrixLayoutCreate(&lc, HIP_R_32F, kModelDim, (uint64_t)a.m, kModelDim)))
+            break;
+        auto it = bd.algo.find(a.m);
+        if (it == bd.algo.end()) {
+            const uint64_t no_workspace = 0;
+            if (!ok(hipblasLtMatmulPreferenceCreate(&pref)) ||
+                !ok(hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES,
+                                                          &no_workspace, sizeof(no_workspace))))
+                break;
+            hipblasLtMatmulHeuristicResult_t res[8];
+            int n = 0;
+            if (!ok(hipblasLtMatmulAlgoGetHeuristic(bd.handle, desc, la, lb, lc, lc, pref, 8, res, &n))) break;
+            int pick = -1;
+            for (int i = 0; i < n && pick < 0; ++i)
+                if (ok(res[i].state) && res[i].workspaceSize == 0) pick = i;
+            if (pick < 0) break;
+            it = bd.algo.emplace(a.m, res[pick].algo).first;
+        }
+        if (!ok(hipblasLtMatmul(bd.handle, desc, &alpha, a.w, la, a.attn, lb, &beta, a.proj, lc, a.proj, lc,
+                                &it->second, nullptr, 0, stream)))
+            break;
+        err = hipSuccess;
+    } while (false);
+    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+    if (lc) hipblasLtMatrixLayoutDestroy(lc);
+    if (lb) hipblasLtMatrixLayoutDestroy(lb);
+    if (la) hipblasLtMatrixLayoutDestroy(la);
+    if (desc) hipblasLtMatmulDescDestroy(desc);
+    return err;
+}
+}  // namespace
+
 hipError_t launch_out_proj_gemm(const OutProjArgs& a, hipStream_t stream) {
     if (a.m <= kSkinnyMaxM) {
         const dim3 sgrid(kSkinnySlices * kSkinnyBlocks), sblock(512);
@@ -316,10 +267,7 @@ hipError_t launch_out_proj_gemm(const OutProjArgs& a, hipStream_t stream) {
         }
         return hipGetLastError();
     }
-    const int64_t mblk = (a.m + kOpBM - 1) / kOpBM;
-    hipLaunchKernelGGL(out_proj_gemm_kernel, dim3((unsigned)(mblk * (kModelDim / kOpBN))), dim3(kOpThreads), 0,
-                       stream, a);
-    return hipGetLastError();
+    return launch_out_proj_blas(a, stream);
 }
 
 hipError_t launch_out_proj_norm(const OutProjArgs& a, hipStream_t stream) {

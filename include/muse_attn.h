@@ -301,13 +301,18 @@ const char* muse_status_str(int status);
  *               in time must not share one
  *   timer       optional: brackets the projection (GEMM) kernel
  * The projection accumulates in f32 from the bf16 operands; the norm reads
- * the f32 projection; hidden is rounded to nearest even into bf16.
+ * the f32 projection; hidden is rounded to nearest even into bf16.  Up to 64
+ * tokens the projection is a kernel of this library; for more it is a
+ * hipBLASLt GEMM, whose library handle the first such call on a device
+ * creates (it allocates device memory: capture such calls in a graph only
+ * after one eager call on that device).
  * Fails closed, before anything is enqueued: NULL pointer MUSE_ERR_NULL;
  * n_tokens < 0 or above 2^24 MUSE_ERR_SHAPE; eps not positive and finite
  * MUSE_ERR_LAYER; a misaligned pointer MUSE_ERR_ALIGN; hidden_out partly
  * overlapping residual, or overlapping attn, w, gamma or the workspace, or
  * the workspace overlapping an input MUSE_ERR_ALIAS; workspace too small
- * MUSE_ERR_WORKSPACE; a failed launch MUSE_ERR_HIP.  Asynchronous on stream.
+ * MUSE_ERR_WORKSPACE; a failed launch, or no hipBLASLt algorithm for the
+ * shape, MUSE_ERR_HIP.  Asynchronous on stream.
  */
 #define MUSE_ATTN_DIM 4096
 #define MUSE_MODEL_DIM 6656

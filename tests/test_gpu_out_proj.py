@@ -6,8 +6,8 @@ seeded synthetic weights.
 Tolerance: the bf16 bound, |gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise (the
 GPU accumulates the bf16 products in f32 and rounds the output to bf16; the
 oracle is double throughout).  Token counts cover the few-token kernel (1 to
-64 rows: one to four 16-row tiles, full and ragged), the tiled kernel (65, a
-full 256-row tile, a ragged tile edge), and a prefill-sized batch checked on
+64 rows: one to four 16-row tiles, full and ragged), the hipBLASLt GEMM above
+64 tokens (65, 256, 257, 300, 513), and a prefill-sized batch checked on
 sampled rows (rows are independent, so a sample is exact for its rows).
 """
 import numpy as np
@@ -49,7 +49,7 @@ def test_out_proj_all_rows(M):
 
 def test_out_proj_prefill_sized_sampled_rows():
     """8 x 8,192 tokens (the prefill workload's batch) on sampled rows,
-    including both ends of every 256-row tile edge near the sample."""
+    including the first and last rows and rows around 256-row boundaries."""
     M = 65536
     rows = np.unique(np.concatenate([[0, 1, 255, 256, 257, 4095, 4096, 32767, 65279, 65280, 65535],
                                      np.random.default_rng(3).integers(0, M, 21)]))
