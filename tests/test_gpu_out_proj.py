@@ -56,6 +56,16 @@ def test_out_proj_prefill_sized_sampled_rows():
     run_case(M, rows=rows, config=71)
 
 
+@pytest.mark.parametrize("M", [1024, 4096, 16384])
+def test_out_proj_mid_sized_sampled_rows(M):
+    """Token counts where the GEMM library picks other algorithms than at
+    65,536 (at 16,384 its first pick needs a workspace, which the call does
+    not pass: only algorithms that need none may run), on sampled rows."""
+    rows = np.unique(np.concatenate([[0, 1, M // 2, M - 2, M - 1],
+                                     np.random.default_rng(M).integers(0, M, 16)]))
+    run_case(M, rows=rows, config=76)
+
+
 def test_out_proj_in_place_residual():
     run_case(300, in_place=True, config=72)
 
