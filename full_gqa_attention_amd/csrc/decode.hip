@@ -487,11 +487,18 @@ void decode_kernel(DecodeArgs a) {
         if (k < my_cnt) process(t, k);
         issue(t, k + DEPTH);
     };
-    for (int k0 = 0; k0 < my_cnt; k0 += DEPTH) {
-        stage(b0, k0);
-        if constexpr (DEPTH > 1) stage(b1, k0 + 1);
-        if constexpr (DEPTH > 2) stage(b2, k0 + 2);
-        if constexpr (DEPTH > 3) stage(b3, k0 + 3);
+    if (my_cnt <= DEPTH) {                             // every sub-tile of the wave is in flight already
+        if (my_cnt > 0) process(b0, 0);
+        if constexpr (DEPTH > 1) if (my_cnt > 1) process(b1, 1);
+        if constexpr (DEPTH > 2) if (my_cnt > 2) process(b2, 2);
+        if constexpr (DEPTH > 3) if (my_cnt > 3) process(b3, 3);
+    } else {
+        for (int k0 = 0; k0 < my_cnt; k0 += DEPTH) {
+            stage(b0, k0);
+            if constexpr (DEPTH > 1) stage(b1, k0 + 1);
+            if constexpr (DEPTH > 2) stage(b2, k0 + 2);
+            if constexpr (DEPTH > 3) stage(b3, k0 + 3);
+        }
     }
 
     // ---- merge the waves: LDS holds per wave [16 heads][128 + 2] floats
@@ -546,24 +553,28 @@ void decode_kernel(DecodeArgs a) {
 }
 
 // ---- the merge of the split partials: one wave per (sequence, query head),
-// four heads per workgroup, lane i holding dims 2i and 2i + 1.  With M the
-// largest partial maximum, split j weighs w_j = 2^(m_j - M); the output is
+// four heads per workgroup.  Lane (h, q) = (lane / 32, lane % 32) holds dims
+// 4q .. 4q + 3 of the splits j with j % 2 == h, so one 16-byte load per lane
+// and split pair brings in 32 splits' O rows at once.  With M the largest
+// partial maximum, split j weighs w_j = 2^(m_j - M); the output is
 // sum_j w_j O_j / sum_j w_j l_j, times sigma(gate) ("Chapter 9 - The Muse
-// Glimmer architecture" 9.8): the softmax over the union of the splits'
-// keys, an exact reformulation.  Every load (the partials of all nsplit
-// slots, the gate, seq_len) goes out at once, so the merge costs one memory
+// Glimmer architecture" 9.8): the softmax over the union of the splits' keys,
+// an exact reformulation.  Every load (the partials of the first 32 slots,
+// the gate, seq_len) goes out at once, so up to 32 splits cost one memory
 // round trip; slots at or past the sequence's live splits are read but not
-// used.  Lane j holds split j's (m, l) (and j + 64, ...); the reductions
-// leave the same bits in every lane, and the O rows are added in split
-// order, so the result does not depend on how the split workgroups were
-// scheduled.
+// used.  Lane j holds split j's (m, l) (and j + 64, ...); the reductions leave
+// the same bits in every lane, each half adds its O rows in split order and
+// the two halves are then added, so the result does not depend on how the
+// split workgroups were scheduled.
 constexpr int kMergeWaves = 4;                         // heads per merge workgroup
-constexpr int kMergeBatch = 16;                        // O rows in flight per lane (16 measured faster than 32 or 64)
+constexpr int kMergeBatch = 16;                        // O rows in flight per lane: 32 splits per round trip
 template <typename T>
 __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeArgs a) {
     constexpr int D = kHeadDim, B = kMergeBatch, R = kMaxSplits / 64;
     static_assert(kMaxSplits % 64 == 0 && kHeads % kMergeWaves == 0, "whole lanes and workgroups");
+    static_assert(D == 4 * 32, "32 lanes of 4 dims cover a head");
     const int lane = threadIdx.x & 63;
+    const int h = lane >> 5, dq = 4 * (lane & 31);
     // workgroup b takes heads 4 q .. 4 q + 3 of pair b mod (2 n_seq), q = b / (2 n_seq)
     // (the XCD of that pair's splits)
     const int npair = 2 * a.n_seq;
@@ -572,7 +583,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeAr
     const int s = sh / kHeads;
     const int nsplit = a.nsplit;
     const int64_t row0 = (int64_t)sh * nsplit;
-    const float* po = a.part_o + row0 * D + 2 * lane;
+    const float* po = a.part_o + row0 * D + dq;
     // (m, l) of slots lane, lane + 64, ...
     float mj[R], lj[R];
 #pragma unroll
@@ -581,25 +592,44 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeAr
         mj[r] = j < nsplit ? a.part_m[row0 + j] : kNegInf;
         lj[r] = j < nsplit ? a.part_l[row0 + j] : 0.0f;
     }
-    // the first batch of O rows
-    float2 ov[B];
+    // the O rows of slots h, h + 2, ..., h + 2 (B - 1)
+    floatx4 ov[B];
 #pragma unroll
-    for (int i = 0; i < B; ++i) ov[i] = i < nsplit ? *(const float2*)(po + (int64_t)i * D) : make_float2(0.0f, 0.0f);
-    const int64_t obase = (int64_t)sh * D + 2 * lane;
-    float g0, g1;
+    for (int i = 0; i < B; ++i) {
+        const int j = 2 * i + h;
+        ov[i] = j < nsplit ? *(const floatx4*)(po + (int64_t)j * D) : floatx4{};
+    }
+    const int64_t obase = (int64_t)sh * D + dq;
+    float gv[4];
     if constexpr (std::is_same<T, bf16_t>::value) {
-        const unsigned w = *(const unsigned*)((const bf16_t*)a.gate + obase);
-        g0 = __uint_as_float(w << 16);
-        g1 = __uint_as_float(w & 0xffff0000u);
+        const uint2 w = *(const uint2*)((const bf16_t*)a.gate + obase);
+        gv[0] = __uint_as_float(w.x << 16);
+        gv[1] = __uint_as_float(w.x & 0xffff0000u);
+        gv[2] = __uint_as_float(w.y << 16);
+        gv[3] = __uint_as_float(w.y & 0xffff0000u);
     } else {
-        const float2 gv = *(const float2*)((const float*)a.gate + obase);
-        g0 = gv.x;
-        g1 = gv.y;
+        const floatx4 g4 = *(const floatx4*)((const float*)a.gate + obase);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) gv[x] = g4[x];
     }
     const int L = a.seq_len[s];
     T* out = (T*)a.out + obase;
+    auto store4 = [&](const float (&v)[4]) __attribute__((always_inline)) {   // dims dq .. dq + 3, from half 0
+        if (h != 0) return;
+        if constexpr (std::is_same<T, bf16_t>::value) {
+            unsigned w[2];
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+                w[x] = (unsigned)__builtin_bit_cast(unsigned short, from_f32<bf16_t>(v[2 * x])) |
+                       ((unsigned)__builtin_bit_cast(unsigned short, from_f32<bf16_t>(v[2 * x + 1])) << 16);
+            *(uint2*)out = make_uint2(w[0], w[1]);
+        } else {
+            *(floatx4*)out = floatx4{v[0], v[1], v[2], v[3]};
+        }
+    };
     if (L < 0 || L > a.max_seq_len) {                  // refused on the device
-        out[0] = out[1] = from_f32<T>(__builtin_nanf(""));
+        const float nan = __builtin_nanf("");
+        store4({nan, nan, nan, nan});
         return;
     }
     const int lo = (a.window > 0) ? max(0, L - a.window + 1) : 0;
@@ -618,29 +648,39 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeAr
         den += live ? lj[r] * wj[r] : 0.0f;
     }
     den = group_sum<64>(den);
-    float acc0 = 0.0f, acc1 = 0.0f;
-    for (int jb = 0; jb < n; jb += B) {
+    floatx4 acc = floatx4{};
+    for (int jb = 0; jb < n; jb += 2 * B) {
         if (jb > 0) {                                  // later batches
 #pragma unroll
-            for (int i = 0; i < B; ++i)
-                ov[i] = jb + i < n ? *(const float2*)(po + (int64_t)(jb + i) * D) : make_float2(0.0f, 0.0f);
+            for (int i = 0; i < B; ++i) {
+                const int j = jb + 2 * i + h;
+                ov[i] = j < nsplit ? *(const floatx4*)(po + (int64_t)j * D) : floatx4{};
+            }
         }
+        // the batch's 32 weights sit in lanes jb % 64 .. jb % 64 + 31 of wj[jb / 64]
+        float wb = wj[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r)
+            if (jb / 64 == r) wb = wj[r];
+        const int lb = jb % 64;
 #pragma unroll
         for (int i = 0; i < B; ++i) {
-            const int j = jb + i;                      // wave-uniform
-            if (j < n) {
-                float w = 0.0f;                        // split j's weight, from lane j % 64
+            const int j0 = jb + 2 * i;                 // the pair's even split (wave-uniform)
+            if (j0 < n) {
+                const float we = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wb), lb + 2 * i));
+                const float wo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wb), lb + 2 * i + 1));
+                const bool live = j0 + h < n;          // split j0 + 1 may be past the live ones
+                const floatx4 c = ov[i] * (h ? wo : we);
 #pragma unroll
-                for (int r = 0; r < R; ++r)
-                    if (j / 64 == r) w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj[r]), j % 64));
-                acc0 += ov[i].x * w;
-                acc1 += ov[i].y * w;
+                for (int x = 0; x < 4; ++x) acc[x] += live ? c[x] : 0.0f;
             }
         }
     }
     const float inv = 1.0f / den;
-    out[0] = from_f32<T>(acc0 * inv * sigmoid(g0));
-    out[1] = from_f32<T>(acc1 * inv * sigmoid(g1));
+    float res[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) res[x] = sum_halves(acc[x]) * inv * sigmoid(gv[x]);
+    store4(res);
 }
 
 // The allocation-free decode's scratch: split partials in a file-scope
