@@ -141,7 +141,10 @@ void decode_kernel(DecodeArgs a) {
     const int l16 = lane & 15, q4 = lane >> 4;
     const int64_t obase = ((int64_t)s * kHeads + g * HG) * D;     // out/gate/q of head 16g
 
-    // ---- loads that do not depend on the sequence's length go out first.
+    // ---- loads that do not depend on the sequence's length go out first:
+    // the lane's RoPE frequency (pair = lane) before Q, so that the (cos, sin)
+    // table, which does not need Q, is made while Q is on its way.
+    const float th = theta_of_lane<DecodeArgs>(lane);
     // This wave's share of the raw Q: HPW heads, LPH lanes per head, DPL
     // consecutive dims per lane.
     constexpr int HPW = HG / NW, LPH = 64 / HPW, DPL = D / LPH;
@@ -184,7 +187,6 @@ void decode_kernel(DecodeArgs a) {
     // with one split per sequence this workgroup applies the gate (else the
     // merge kernel does, or a short sequence's only live split loads it late)
     if (a.nsplit == 1) load_gate();
-    const float th = theta_of_lane<DecodeArgs>(lane); // this lane's RoPE frequency (pair = lane)
     // The exits below use those loads too (an empty asm that takes them):
     // otherwise the compiler moves the loads past the exits, behind the wait
     // for seq_len, and the two round trips no longer overlap.
@@ -552,8 +554,8 @@ void decode_kernel(DecodeArgs a) {
     }
 }
 
-// ---- the merge of the split partials: one wave per (sequence, query head),
-// four heads per workgroup.  Lane (h, q) = (lane / 32, lane % 32) holds dims
+// ---- the merge of the split partials: one wave per (sequence, query head)
+// and workgroup.  Lane (h, q) = (lane / 32, lane % 32) holds dims
 // 4q .. 4q + 3 of the splits j with j % 2 == h, so one 16-byte load per lane
 // and split pair brings in 32 splits' O rows at once.  With M the largest
 // partial maximum, split j weighs w_j = 2^(m_j - M); the output is
@@ -566,7 +568,7 @@ void decode_kernel(DecodeArgs a) {
 // the same bits in every lane, each half adds its O rows in split order and
 // the two halves are then added, so the result does not depend on how the
 // split workgroups were scheduled.
-constexpr int kMergeWaves = 4;                         // heads per merge workgroup
+constexpr int kMergeWaves = 1;                         // heads per merge workgroup (one wave: its loads use a CU of their own)
 constexpr int kMergeBatch = 16;                        // O rows in flight per lane: 32 splits per round trip
 template <typename T>
 __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeArgs a) {
@@ -575,7 +577,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeAr
     static_assert(D == 4 * 32, "32 lanes of 4 dims cover a head");
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5, dq = 4 * (lane & 31);
-    // workgroup b takes heads 4 q .. 4 q + 3 of pair b mod (2 n_seq), q = b / (2 n_seq)
+    // workgroup b takes head q (of the pair's 16) of pair b mod (2 n_seq), q = b / (2 n_seq)
     // (the XCD of that pair's splits)
     const int npair = 2 * a.n_seq;
     const int mpair = blockIdx.x % npair, mq = blockIdx.x / npair;
