@@ -210,6 +210,9 @@ def parse():
                     help="write a kernel-trace summary from rocprofv3 kernel_trace.csv and exit")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT", "COMMAND"),
                     help="write the decode kernels' HBM-traffic summary from two --pmc runs and exit")
+    ap.add_argument("--decode-timeline", nargs="?", const="", metavar="OUT_MD",
+                    help="per-phase decode timelines from the profiling build (build it with "
+                         "`python full_gqa_attention_amd/build.py --timeline`); optional markdown summary path")
     ap.add_argument("--summarize-mfma", nargs=4, metavar=("PMC1_CSV", "PMC2_CSV", "OUT", "COMMAND"),
                     help="write the prefill kernel's MFMA-utilisation summary from two --pmc runs and exit")
     return ap.parse_args()
@@ -834,6 +837,123 @@ def summarize_trace(trace_csv: str, out: str, command: str):
         f.write("\n".join(lines) + "\n")
 
 
+TL_PHASES = ["seq_len read", "raw Q rows arrived", "Q-hat shared (barrier)", "sub-tiles done",
+             "partials merged in LDS", "stores complete"]
+
+
+def timeline_summary(split, merge):
+    """Phase times of one decode call from the profiling build's records
+    (10 ns units): per split workgroup, the medians (p10, p90) of each phase's
+    duration after the previous one; the call's critical path from the first
+    split workgroup's start to the last merge workgroup's end."""
+    import numpy as np
+    d = split[split[:, 6] > 0]
+    m = merge[merge[:, 2] > 0]
+    k0 = int(d[:, 0].min())
+    ph = np.diff(d[:, :7], axis=1) / 100.0
+    res = {"split_workgroups": int(len(d)), "sub_tiles_per_wave_p50": float(np.median(d[:, 7])),
+           "start_spread_us": round(float(d[:, 0].max() - k0) / 100.0, 2),
+           "phases_us": {n: [round(float(np.percentile(ph[:, i], q)), 2) for q in (50, 10, 90)]
+                         for i, n in enumerate(TL_PHASES)},
+           "workgroup_total_us_p50": round(float(np.median(d[:, 6] - d[:, 0])) / 100.0, 2),
+           "last_split_end_us": round(float(d[:, 6].max() - k0) / 100.0, 2)}
+    if len(m):
+        res["merge"] = {"workgroups": int(len(m)),
+                        "first_start_after_last_split_us": round(float(m[:, 0].min() - d[:, 6].max()) / 100.0, 2),
+                        "loads_arrived_us_p50": round(float(np.median(m[:, 1] - m[:, 0])) / 100.0, 2),
+                        "stores_complete_us_p50": round(float(np.median(m[:, 2] - m[:, 1])) / 100.0, 2),
+                        "last_end_us": round(float(m[:, 2].max() - k0) / 100.0, 2)}
+    return res
+
+
+def decode_timeline(fa, synth, torch, out_path=None, command=""):
+    """Per-phase decode timelines from the profiling build
+    (libmuse_attn_timeline.so): the 52-layer schedule's sliding and full
+    layers (a graph of that kind's calls, as the roofline times them) and the
+    64 x 8,192 and 16 x 131,072 decode layers (a graph of one call per cache
+    copy, as their legs time them); the records are those of the graph's last
+    call.  Prints one JSON object; writes a markdown summary to out_path."""
+    from full_gqa_attention_amd.schedule import Schedule
+    fa.use_timeline_library()
+
+    def capture(calls):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in calls:
+                c()
+        return g
+
+    def run(g, n_calls):
+        g.replay()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for a, b in ev:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) for a, b in ev)[2] * 1e3 / n_calls
+        fa.decode_timeline_read(clear=True)
+        g.replay()
+        split, merge = fa.decode_timeline_read(clear=True)
+        return round(us, 2), timeline_summary(split, merge)
+
+    cases = {}
+    w = synth.WORKLOADS[HEADLINE]
+    sch = Schedule(w)
+    sch.prefill()
+    sch.start_decode()
+    kinds = [_kind(s, synth) for s in sch.specs]
+    for kind in ("sliding", "full"):
+        idx = [l for l in range(len(sch.specs)) if kinds[l] == kind]
+        g = capture([(lambda l=l: sch.decode_layer(l)) for l in idx])
+        us, tl = run(g, len(idx))
+        cases[f"{w.name} {kind}"] = dict(graph=f"{len(idx)} calls ({kind} layers), records of the last",
+                                         us_per_call=us, **tl)
+        del g
+    del sch
+    torch.cuda.empty_cache()
+    for name in ("decode_64x8192_bf16", "decode_16x131072_bf16"):
+        wl = synth.WORKLOADS[name]
+        for spec in wl.layers:
+            per = kv_row_bytes(wl.dtype) * wl.n_seq * visible_rows(spec, wl.prefix)
+            copies = min(8, max(1, -(-(2 * MALL_BYTES) // max(per, 1)) + 1))
+            r = LayerRun(wl, spec, copies, True, fa, synth)
+            g = capture([(lambda c=c: r.call(fa, c)) for c in range(copies)])
+            us, tl = run(g, copies)
+            cases[f"{name} {_kind(spec, synth)}"] = dict(graph=f"{copies} calls (one per cache copy), records of the last",
+                                                          us_per_call=us, **tl)
+            del g, r
+            torch.cuda.empty_cache()
+    print(json.dumps({"decode_timeline": cases}), flush=True)
+    if out_path:
+        lines = ["# Decode phase timeline (profiling build): 52-layer schedule, 64 x 8,192 and 16 x 131,072 decode", "",
+                 "Command (repository root, one MI355X):", "", "```", command, "```", "",
+                 "The profiling build (`libmuse_attn_timeline.so`, `include/muse_attn_timeline.h`) is the regular "
+                 "library with per-workgroup stamps (`s_memrealtime`, 10 ns) in the decode split and merge kernels. "
+                 "Each phase is the median time (p10, p90) a split workgroup spends after the previous one; "
+                 "the stores phase waits for the workgroup's stores to complete. "
+                 "`us per call` is the graph-replayed call of the profiling build (split + merge).", ""]
+        for cname, c in cases.items():
+            lines += [f"## {cname}", "", f"{c['graph']}; {c['us_per_call']} us per call; {c['split_workgroups']} split "
+                      f"workgroups, {c['sub_tiles_per_wave_p50']:.0f} sub-tiles per wave (median), starts spread over "
+                      f"{c['start_spread_us']} us", "", "| split phase | us p50 | p10 | p90 |", "|---|---|---|---|"]
+            for n, (a, lo, hi) in c["phases_us"].items():
+                lines.append(f"| {n} | {a} | {lo} | {hi} |")
+            lines += ["", f"Split workgroup total (p50) {c['workgroup_total_us_p50']} us; last split workgroup done at "
+                      f"{c['last_split_end_us']} us after the first started."]
+            if "merge" in c:
+                mg = c["merge"]
+                lines.append(f"Merge: {mg['workgroups']} workgroups, the first starting {mg['first_start_after_last_split_us']} us "
+                             f"after the last split ended; loads in after {mg['loads_arrived_us_p50']} us, output stores "
+                             f"complete {mg['stores_complete_us_p50']} us later (p50); last merge workgroup done at "
+                             f"{mg['last_end_us']} us.")
+            lines.append("")
+        with open(out_path, "w") as f:
+            f.write("\n".join(lines))
+    return cases
+
+
 def bench_verify(fa, synth, torch, steps=20, warmup=3, n_new=16):
     """Multi-token verify: 16 drafted tokens per sequence scored against the
     64 x 8,192 cached rows (the drafting-and-verifying section of "How Muse
@@ -995,6 +1115,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.decode_timeline is not None:
+        decode_timeline(fa, synth, torch, out_path=args.decode_timeline or None,
+                        command="python bench.py --decode-timeline " + (args.decode_timeline or ""))
+        return
     fa.lib()                                  # fails loudly when the HIP library is missing
     if args.calibrate_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

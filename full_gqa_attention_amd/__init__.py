@@ -112,6 +112,43 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
+TIMELINE_LIB_PATH = _build.TIMELINE_LIB_PATH
+TIMELINE_EXPORTS = ("muse_decode_timeline_read",)
+TL_SPLIT_WORKGROUPS, TL_SPLIT_SLOTS, TL_MERGE_WORKGROUPS, TL_MERGE_SLOTS = 4096, 8, 4096, 4
+
+
+def use_timeline_library() -> ctypes.CDLL:
+    """Send this process's later calls to the profiling build
+    (libmuse_attn_timeline.so, include/muse_attn_timeline.h): the same C ABI,
+    whose decode kernels also record per-workgroup phase times.  Raises if
+    the profiling build is missing."""
+    global _lib, LIB_PATH
+    if not os.path.exists(TIMELINE_LIB_PATH):
+        raise RuntimeError(f"{TIMELINE_LIB_PATH} is missing: build it with "
+                           "`python full_gqa_attention_amd/build.py --timeline`")
+    _lib = None
+    LIB_PATH = TIMELINE_LIB_PATH
+    L = lib()
+    L.muse_decode_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_int32]
+    L.muse_decode_timeline_read.restype = ctypes.c_int
+    return L
+
+
+def decode_timeline_read(clear: bool = True):
+    """The profiling build's per-workgroup decode records (numpy int64
+    arrays [4096][8] for the split kernel and [4096][4] for the merge kernel,
+    10 ns units, zero rows for workgroups that did not record); clears them
+    afterwards unless clear is False."""
+    import numpy as np
+    split = np.zeros(TL_SPLIT_WORKGROUPS * TL_SPLIT_SLOTS, dtype=np.uint64)
+    merge = np.zeros(TL_MERGE_WORKGROUPS * TL_MERGE_SLOTS, dtype=np.uint64)
+    _check(lib().muse_decode_timeline_read(split.ctypes.data, split.size, merge.ctypes.data, merge.size,
+                                           1 if clear else 0), "muse_decode_timeline_read")
+    return (split.reshape(TL_SPLIT_WORKGROUPS, TL_SPLIT_SLOTS).astype(np.int64),
+            merge.reshape(TL_MERGE_WORKGROUPS, TL_MERGE_SLOTS).astype(np.int64))
+
+
 def _check(code: int, where: str):
     if code != 0:
         raise MuseError(code, where)

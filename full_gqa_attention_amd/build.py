@@ -100,6 +100,31 @@ def build_sanitized() -> str:
     return SAN_LIB_PATH
 
 
+TIMELINE_LIB_PATH = os.path.join(PKG, "libmuse_attn_timeline.so")
+
+
+def build_timeline() -> str:
+    """libmuse_attn_timeline.so: the regular library with decode.hip built
+    with MUSE_DECODE_TIMELINE, whose decode kernels record per-workgroup
+    phase times (include/muse_attn_timeline.h).  For profiling only."""
+    if not all(os.path.exists(os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")) for src in SOURCES):
+        build()
+    tl_dir = os.path.join(BUILD_DIR, "timeline")
+    os.makedirs(tl_dir, exist_ok=True)
+    obj = os.path.join(tl_dir, "decode.o")
+    cmd = [hipcc()] + common_flags() + ["-DMUSE_DECODE_TIMELINE", "-c", os.path.join(CSRC, "decode.hip"), "-o", obj]
+    out = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if out.returncode != 0:
+        sys.stderr.write(out.stdout.decode(errors="replace"))
+        raise RuntimeError("hipcc failed on the timeline decode.hip")
+    objs = [obj] + [os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o") for src in SOURCES
+                    if src != "decode.hip"]
+    tmp = TIMELINE_LIB_PATH + ".tmp"
+    subprocess.run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, *LINK_LIBS, "-o", tmp], check=True)
+    os.replace(tmp, TIMELINE_LIB_PATH)
+    return TIMELINE_LIB_PATH
+
+
 def asan_runtime() -> str:
     """clang's shared ASan runtime (it carries the UBSan handlers too)."""
     clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
@@ -115,5 +140,7 @@ def asan_runtime() -> str:
 if __name__ == "__main__":
     if "--sanitize" in sys.argv:
         print(build_sanitized())
+    elif "--timeline" in sys.argv:
+        print(build_timeline())
     else:
         print(build(verbose="-v" in sys.argv))

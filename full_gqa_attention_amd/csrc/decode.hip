@@ -44,7 +44,29 @@
 #include "device_common.h"
 #include "kernels.h"
 
+// Profiling build only (-DMUSE_DECODE_TIMELINE, libmuse_attn_timeline.so):
+// every split and merge workgroup records when it reaches each phase of its
+// work (s_memrealtime, a 100 MHz clock common to the whole GPU), for
+// muse_decode_timeline_read.  The stamps wait for what they name (the data
+// of a phase, the completion of the final stores); nothing else changes.  In
+// the regular build the macros are empty.
+#ifdef MUSE_DECODE_TIMELINE
+#include "muse_attn_timeline.h"
+#define MUSE_TL_STAMP(var) const unsigned long long var = __builtin_amdgcn_s_memrealtime()
+#define MUSE_TL_HOLD(...) asm volatile("" ::__VA_ARGS__)
+#define MUSE_TL_DRAIN() __builtin_amdgcn_s_waitcnt(0)
+#else
+#define MUSE_TL_STAMP(var)
+#define MUSE_TL_HOLD(...)
+#define MUSE_TL_DRAIN()
+#endif
+
 namespace muse {
+
+#ifdef MUSE_DECODE_TIMELINE
+__device__ unsigned long long decode_tl_split[MUSE_TL_SPLIT_WORKGROUPS * MUSE_TL_SPLIT_SLOTS];
+__device__ unsigned long long decode_tl_merge[MUSE_TL_MERGE_WORKGROUPS * MUSE_TL_MERGE_SLOTS];
+#endif
 
 template <typename T> struct DecodeTraits;
 // bf16: K and V rows loaded alike, 4 rows x 256 B per load instruction (16
@@ -132,6 +154,7 @@ void decode_kernel(DecodeArgs a) {
     // workgroup b takes pair b mod (2 n_seq) and split b / (2 n_seq): with
     // dispatch round-robin over the 8 XCDs, all splits of a pair share an
     // XCD when the pair count is a multiple of 8 (so does the pair's merge)
+    MUSE_TL_STAMP(tl0);
     const int b = blockIdx.x;
     const int npair = 2 * a.n_seq;
     const int c = b / npair;
@@ -204,6 +227,8 @@ void decode_kernel(DecodeArgs a) {
     }
     // positions are below 2^24 (checked on the host): 32-bit arithmetic
     const int p = L;
+    MUSE_TL_HOLD("s"(p));
+    MUSE_TL_STAMP(tl1);
     const int lo = (W > 0) ? max(0, p - W + 1) : 0;
     const int cs = lo + c * a.chunk;
     if (cs > p) {                                      // split beyond this sequence's rows
@@ -281,6 +306,8 @@ void decode_kernel(DecodeArgs a) {
     // ---- (cos, sin) of the 64 pairs at position p in the wave's own table,
     // then Q-hat of the wave's HPW heads: RMS norm with gain, RoPE on sliding
     // layers ("Chapter 14 - QK-norm and RoPE" 14.3-14.5)
+    MUSE_TL_HOLD("v"(qraw[0]));
+    MUSE_TL_STAMP(tl2);
     float2* rot = rot_all[wave];
     if (a.rope) {
         float sn, cs_;
@@ -328,6 +355,7 @@ void decode_kernel(DecodeArgs a) {
         if constexpr (kBf16) __builtin_memcpy(qs_lo + qh * LDQ + qd0, lv, sizeof lv);
     }
     __syncthreads();
+    MUSE_TL_STAMP(tl3);
     constexpr int NSTQ = kBf16 ? 4 : 32;               // 16x16x32 bf16 / 16x16x4 f32 steps
     using MW = Mma16Wide<T>;
     using MN = Mma16Narrow<T>;
@@ -504,6 +532,8 @@ void decode_kernel(DecodeArgs a) {
     }
 
     // ---- merge the waves: LDS holds per wave [16 heads][128 + 2] floats
+    MUSE_TL_HOLD("v"(o[0]), "v"(o[D / 16 - 1]));
+    MUSE_TL_STAMP(tl4);
     l_run = sum_halves(sum_rows16(l_run));
     __syncthreads();
     float* mg = (float*)lds;
@@ -533,12 +563,28 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int x = 0; x < DPT; ++x) own_o[x] += row[d0 + x] * e;
     }
+    MUSE_TL_HOLD("v"(own_l), "v"(own_o[0]));
+    MUSE_TL_STAMP(tl5);
+#ifdef MUSE_DECODE_TIMELINE
+    auto tl_record = [&]() __attribute__((always_inline)) {
+        MUSE_TL_DRAIN();
+        MUSE_TL_STAMP(tl6);
+        if (tid == 0 && b < MUSE_TL_SPLIT_WORKGROUPS) {
+            unsigned long long* d = decode_tl_split + (size_t)b * MUSE_TL_SPLIT_SLOTS;
+            d[0] = tl0; d[1] = tl1; d[2] = tl2; d[3] = tl3; d[4] = tl4; d[5] = tl5; d[6] = tl6;
+            d[7] = (unsigned long long)my_cnt;
+        }
+    };
+#endif
     if (n_live == 1) {                                 // the only split: finish here
         if (a.nsplit > 1) load_gate();                 // a short sequence of a split call
         T* out = (T*)a.out + obase;
         const float inv = 1.0f / own_l;
 #pragma unroll
         for (int x = 0; x < DPT; ++x) out[hh * D + d0 + x] = from_f32<T>(own_o[x] * inv * gate_sig(x));
+#ifdef MUSE_DECODE_TIMELINE
+        tl_record();
+#endif
         return;
     }
     // ---- several splits: store this split's partial (m, l, O) for the merge
@@ -552,6 +598,9 @@ void decode_kernel(DecodeArgs a) {
         a.part_m[head_row] = own_m;
         a.part_l[head_row] = own_l;
     }
+#ifdef MUSE_DECODE_TIMELINE
+    tl_record();
+#endif
 }
 
 // ---- the merge of the split partials: one wave per (sequence, query head)
@@ -572,6 +621,7 @@ constexpr int kMergeWaves = 1;                         // heads per merge workgr
 constexpr int kMergeBatch = 16;                        // O rows in flight per lane: 32 splits per round trip
 template <typename T>
 __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeArgs a) {
+    MUSE_TL_STAMP(tm0);
     constexpr int D = kHeadDim, B = kMergeBatch, R = kMaxSplits / 64;
     static_assert(kMaxSplits % 64 == 0 && kHeads % kMergeWaves == 0, "whole lanes and workgroups");
     static_assert(D == 4 * 32, "32 lanes of 4 dims cover a head");
@@ -642,6 +692,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeAr
     for (int r = 0; r < R; ++r)
         if (lane + 64 * r < n) M = fmaxf(M, mj[r]);
     M = wave_max(M);
+    MUSE_TL_HOLD("v"(ov[0]), "v"(ov[B - 1]), "v"(M));
+    MUSE_TL_STAMP(tm1);
     float wj[R], den = 0.0f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {                      // slots past n hold stale bytes: selected out, not weighted
@@ -683,6 +735,14 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeAr
 #pragma unroll
     for (int x = 0; x < 4; ++x) res[x] = sum_halves(acc[x]) * inv * sigmoid(gv[x]);
     store4(res);
+#ifdef MUSE_DECODE_TIMELINE
+    MUSE_TL_DRAIN();
+    MUSE_TL_STAMP(tm2);
+    if (threadIdx.x == 0 && blockIdx.x < MUSE_TL_MERGE_WORKGROUPS) {
+        unsigned long long* d = decode_tl_merge + (size_t)blockIdx.x * MUSE_TL_MERGE_SLOTS;
+        d[0] = tm0; d[1] = tm1; d[2] = tm2; d[3] = (unsigned long long)n;
+    }
+#endif
 }
 
 // The allocation-free decode's scratch: split partials in a file-scope
@@ -711,6 +771,31 @@ hipError_t decode_scratch(void** ptr) {
     return hipSuccess;
 }
 
+#ifdef MUSE_DECODE_TIMELINE
+static hipError_t decode_timeline_read(uint64_t* split, size_t split_count, uint64_t* merge, size_t merge_count,
+                                int32_t clear) {
+    const size_t ns = (size_t)MUSE_TL_SPLIT_WORKGROUPS * MUSE_TL_SPLIT_SLOTS;
+    const size_t nm = (size_t)MUSE_TL_MERGE_WORKGROUPS * MUSE_TL_MERGE_SLOTS;
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess && split)
+        e = hipMemcpyFromSymbol(split, HIP_SYMBOL(decode_tl_split), (split_count < ns ? split_count : ns) * 8, 0,
+                                hipMemcpyDeviceToHost);
+    if (e == hipSuccess && merge)
+        e = hipMemcpyFromSymbol(merge, HIP_SYMBOL(decode_tl_merge), (merge_count < nm ? merge_count : nm) * 8, 0,
+                                hipMemcpyDeviceToHost);
+    if (e == hipSuccess && clear) {
+        void* ps = nullptr;
+        void* pm = nullptr;
+        e = hipGetSymbolAddress(&ps, HIP_SYMBOL(decode_tl_split));
+        if (e == hipSuccess) e = hipGetSymbolAddress(&pm, HIP_SYMBOL(decode_tl_merge));
+        if (e == hipSuccess) e = hipMemset(ps, 0, ns * 8);
+        if (e == hipSuccess) e = hipMemset(pm, 0, nm * 8);
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+    }
+    return e;
+}
+#endif
+
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream) {
     const dim3 grid((unsigned)(a.n_seq * kKvHeads * a.nsplit)), block(64 * kDecodeWaves);
     if (dtype == 1)
@@ -730,3 +815,10 @@ hipError_t launch_decode_merge(const DecodeArgs& a, int dtype, hipStream_t strea
 }
 
 }  // namespace muse
+
+#ifdef MUSE_DECODE_TIMELINE
+extern "C" int muse_decode_timeline_read(uint64_t* split_host, size_t split_count, uint64_t* merge_host,
+                                         size_t merge_count, int32_t clear) {
+    return muse::decode_timeline_read(split_host, split_count, merge_host, merge_count, clear) == hipSuccess ? 0 : 7;
+}
+#endif

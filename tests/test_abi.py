@@ -40,6 +40,22 @@ def test_header_symbols_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_timeline_build_exports():
+    """The profiling build exports muse_attn.h's functions and its own
+    (include/muse_attn_timeline.h); the regular build does not export the
+    latter."""
+    tl_header = os.path.join(ROOT, "include", "muse_attn_timeline.h")
+    text = re.sub(r"/\*.*?\*/", "", open(tl_header).read(), flags=re.S)
+    tl_names = sorted(set(re.findall(r"\b(muse_[a-z_0-9]+)\s*\(", text)))
+    assert tl_names == sorted(fa.TIMELINE_EXPORTS)
+    tl = ctypes.CDLL(fa.TIMELINE_LIB_PATH)
+    for n in header_functions() + tl_names:
+        assert hasattr(tl, n), n
+    regular = ctypes.CDLL(fa.LIB_PATH)
+    for n in tl_names:
+        assert not hasattr(regular, n), n
+
+
 def test_status_strings(lib):
     for code in range(10):
         assert fa.status_str(code).startswith(fa.STATUS[code])
