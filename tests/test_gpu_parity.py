@@ -115,10 +115,11 @@ def test_decode_ragged(spec, dtype):
 @pytest.mark.parametrize("lens", [[40000, 9000, 7680], [60000]], ids=["3seq", "1seq"])
 def test_decode_long_context_many_splits(dtype, lens):
     """Long contexts make many splits per (sequence, KV head), merged by the
-    merge kernel in batches of 16 rows: three sequences of 40,000, 9,000 and
-    7,680 cached rows (42 splits, fewer live in the shorter ones), and one of
-    60,000 (126 splits: the (m, l) slots past 64 sit in a second register
-    per lane)."""
+    merge kernel 32 splits per round trip: three sequences of 40,000, 9,000
+    and 7,680 cached rows (42 splits in two batches, fewer live in the
+    shorter ones, whose last live split may be an even or an odd one), and
+    one of 60,000 (126 splits in four batches: the (m, l) slots past 64 sit
+    in a second register per lane)."""
     spec = synth.full()
     w = _custom("long_decode", dtype, len(lens), max(lens), 1, [spec])
     inp = _ragged_inputs(w, spec, lens, 1)
