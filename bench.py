@@ -213,6 +213,10 @@ def parse():
     ap.add_argument("--decode-timeline", nargs="?", const="", metavar="OUT_MD",
                     help="per-phase decode timelines from the profiling build (build it with "
                          "`python full_gqa_attention_amd/build.py --timeline`); optional markdown summary path")
+    ap.add_argument("--decode-leg", nargs=2, metavar=("WORKLOAD", "KIND"),
+                    help="replay one layer kind of a decode workload from a HIP graph (for a kernel trace)")
+    ap.add_argument("--summarize-leg-traces", nargs="+", metavar="ARG",
+                    help="OUT COMMAND LABEL CSV [LABEL CSV ...]: per-layer decode summary from --decode-leg traces")
     ap.add_argument("--summarize-mfma", nargs=4, metavar=("PMC1_CSV", "PMC2_CSV", "OUT", "COMMAND"),
                     help="write the prefill kernel's MFMA-utilisation summary from two --pmc runs and exit")
     return ap.parse_args()
@@ -954,6 +958,63 @@ def decode_timeline(fa, synth, torch, out_path=None, command=""):
     return cases
 
 
+def decode_leg_only(fa, synth, torch, name, kind, reps=20):
+    """One layer kind of a decode workload, replayed from a HIP graph of one
+    call per cache copy (as its leg times it), for a kernel trace of that
+    layer alone.  Prints one JSON object with the per-call time between events."""
+    wl = synth.WORKLOADS[name]
+    spec = next(s for s in wl.layers if _kind(s, synth) == kind)
+    per = kv_row_bytes(wl.dtype) * wl.n_seq * visible_rows(spec, wl.prefix)
+    copies = min(8, max(1, -(-(2 * MALL_BYTES) // max(per, 1)) + 1))
+    r = LayerRun(wl, spec, copies, True, fa, synth)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in range(copies):
+            r.call(fa, c)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / (reps * copies)
+    print(json.dumps({"decode_leg": name, "kind": kind, "calls": (reps + 3) * copies, "cache_copies": copies,
+                      "us_per_call": round(us, 2), "kv_bytes_per_call": per,
+                      "GBps": round(per / us / 1e3, 1)}), flush=True)
+
+
+def summarize_leg_traces(out: str, command: str, *pairs):
+    """Write per-layer decode summaries from kernel traces of `--decode-leg`
+    runs: pairs of (label, kernel_trace.csv)."""
+    import csv
+    lines = ["# Decode legs, one layer kind per run: kernel trace", "", "Commands (from /tmp, repository at $ROOT), one per row:",
+             "", "```", command, "```", "",
+             "Each run replays one layer kind of the workload from a HIP graph (one call per cache copy, enough "
+             "copies that the 256 MB Infinity Cache cannot serve a call from the previous one), 3 warm-up "
+             "and 20 timed replays; every traced call is averaged.", "",
+             "| workload, layer | split kernel avg us (min, max) | merge kernel avg us | call (sum) us | KV GB/s per call |",
+             "|---|---|---|---|---|"]
+    for i in range(0, len(pairs), 2):
+        label, path = pairs[i], pairs[i + 1]
+        rows = list(csv.DictReader(open(path)))
+        sp = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows
+              if "decode_kernel" in r["Kernel_Name"] and "merge" not in r["Kernel_Name"]]
+        mg = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows
+              if "decode_merge_kernel" in r["Kernel_Name"]]
+        name, kind = label.split(":")
+        wl_bytes = {"decode_64x8192_bf16": {"full": 64 * 8193 * 1024, "sliding": 64 * 2048 * 1024},
+                    "decode_16x131072_bf16": {"full": 16 * 131073 * 1024, "sliding": 16 * 2048 * 1024}}[name][kind]
+        a = sum(sp) / len(sp)
+        m = sum(mg) / len(mg) if mg else 0.0
+        lines.append(f"| {name}, {kind} | {a:.2f} ({min(sp):.2f}, {max(sp):.2f}) | {m:.2f} | {a + m:.2f} | "
+                     f"{wl_bytes / (a + m) / 1e3:.0f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def bench_verify(fa, synth, torch, steps=20, warmup=3, n_new=16):
     """Multi-token verify: 16 drafted tokens per sequence scored against the
     64 x 8,192 cached rows (the drafting-and-verifying section of "How Muse
@@ -1105,6 +1166,9 @@ def main():
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma)
         return
+    if args.summarize_leg_traces:
+        summarize_leg_traces(*args.summarize_leg_traces)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
               "multi-GPU path to measure.", file=sys.stderr)
@@ -1115,6 +1179,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.decode_leg:
+        fa.lib()
+        decode_leg_only(fa, synth, torch, *args.decode_leg)
+        return
     if args.decode_timeline is not None:
         decode_timeline(fa, synth, torch, out_path=args.decode_timeline or None,
                         command="python bench.py --decode-timeline " + (args.decode_timeline or ""))

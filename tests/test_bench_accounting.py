@@ -88,3 +88,28 @@ def test_timeline_summary_on_synthetic_records():
     assert t["merge"]["first_start_after_last_split_us"] == 1.2
     assert t["merge"]["loads_arrived_us_p50"] == 1.6
     assert t["merge"]["last_end_us"] == 9.1
+
+
+def test_leg_trace_summary(tmp_path):
+    """The per-leg trace summary averages the split and merge kernels of a
+    trace and prices the call at the leg's algorithmic bytes."""
+    import csv
+    path = tmp_path / "trace.csv"
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        wr.writeheader()
+        t = 0
+        for i in range(4):                              # split 20/22 us, merge 4 us (ns stamps)
+            wr.writerow({"Kernel_Name": "void muse::decode_kernel<__bf16, 3, 4>(muse::DecodeArgs)",
+                         "Start_Timestamp": t, "End_Timestamp": t + (20000 if i % 2 == 0 else 22000)})
+            t += 30000
+            wr.writerow({"Kernel_Name": "void muse::decode_merge_kernel<__bf16>(muse::DecodeArgs)",
+                         "Start_Timestamp": t, "End_Timestamp": t + 4000})
+            t += 10000
+        wr.writerow({"Kernel_Name": "other_kernel", "Start_Timestamp": t, "End_Timestamp": t + 999000})
+    out = tmp_path / "out.md"
+    bench.summarize_leg_traces(str(out), "cmd", "decode_64x8192_bf16:sliding", str(path))
+    row = [l for l in open(out).read().splitlines() if l.startswith("| decode_64x8192_bf16, sliding")][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[1] == "21.00 (20.00, 22.00)" and cells[2] == "4.00" and cells[3] == "25.00"
+    assert cells[4] == str(round(64 * 2048 * 1024 / 25.0 / 1e3))
