@@ -15,19 +15,21 @@ from full_gqa_attention_amd import synth
 pytestmark = pytest.mark.gpu
 
 
-def _decode_case(spec, n_seq, prefix, dev="cuda:0"):
-    w = synth.Workload("timeline", 41, synth.BF16, n_seq, prefix, 1, (spec,))
+def _decode_case(spec, n_seq, prefix, dtype=synth.BF16, dev="cuda:0"):
+    w = synth.Workload("timeline", 41, dtype, n_seq, prefix, 1, (spec,))
     inp = synth.layer_inputs(w, spec, device=dev, backend="torch", n_new=1, capacity=prefix + 1)
     lay = fa.make_layer(spec.kind, window=spec.window, rope_theta=spec.rope_theta, dtype=w.dtype)
     return lay, inp
 
 
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("kind", ["sliding", "full"])
-def test_timeline_build_matches_regular_build(kind):
+def test_timeline_build_matches_regular_build(kind, dtype):
     spec = synth.sliding(2048, 500000.0) if kind == "sliding" else synth.full()
     n_seq, prefix = 4, 6000
-    lay, inp = _decode_case(spec, n_seq, prefix)
-    print(f"timeline: {kind} decode S={n_seq} at position {prefix}, regular then profiling build", flush=True)
+    lay, inp = _decode_case(spec, n_seq, prefix, dtype)
+    print(f"timeline: {kind} decode S={n_seq} at position {prefix} (dtype {dtype}), regular then profiling build",
+          flush=True)
     ck0, cv0 = inp.cache_k.clone(), inp.cache_v.clone()
     out_a = fa.decode(lay, inp.q, inp.k, inp.v, inp.gate, inp.cache_k, inp.cache_v, inp.seq_len)
     torch.cuda.synchronize()
@@ -43,9 +45,10 @@ def test_timeline_build_matches_regular_build(kind):
         split, merge = fa.decode_timeline_read(clear=True)
     finally:
         fa._lib, fa.LIB_PATH = saved
-    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
-    assert torch.equal(ck_a.view(torch.int16), inp.cache_k.view(torch.int16))
-    assert torch.equal(cv_a.view(torch.int16), inp.cache_v.view(torch.int16))
+    bits = torch.int16 if dtype == synth.BF16 else torch.int32
+    assert torch.equal(out_a.view(bits), out_b.view(bits))
+    assert torch.equal(ck_a.view(bits), inp.cache_k.view(bits))
+    assert torch.equal(cv_a.view(bits), inp.cache_v.view(bits))
     d = split[split[:, 6] > 0]
     assert len(d) >= 2 * n_seq, len(d)                 # at least one split per (sequence, KV head)
     assert np.all(np.diff(d[:, :7], axis=1) >= 0)
